@@ -1,0 +1,398 @@
+"""Pins of the CPU oracle to facts that do not come from the oracle itself.
+
+Each test ties the oracle to one of: numbers printed on the pages (fixtures in
+tests/golden), closed forms, invariants the mathematics fixes, an evaluation
+in 50-digit decimal arithmetic, or a brute-force loop on tiny inputs that
+takes a different route (no max subtraction). The mutation tests re-run these
+functions against oracles with planted mistakes, so every test here must be
+self-contained (no fixtures).
+"""
+
+import math
+from decimal import Decimal, getcontext
+
+import numpy as np
+
+import oracle
+from tests._golden import load
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _row_attention(scores, values):
+    """Route a given score row through the full [B,H,N,d] oracle: one query
+    (q = [1]), keys k_j = s_j, scale 1, so S = scores exactly."""
+    scores = np.asarray(scores, dtype=np.float64)
+    values = np.asarray(values, dtype=np.float64).reshape(len(scores), -1)
+    q = np.ones((1, 1, 1, 1))
+    k = scores.reshape(1, 1, -1, 1)
+    v = values.reshape(1, 1, len(scores), -1)
+    o, lse = oracle.attention_forward(q, k, v, scale=1.0)
+    return o[0, 0, 0], lse[0, 0, 0]
+
+
+# ---------------------------------------------------------------- pages' numbers
+
+def test_worked_row_two_blocks():
+    g = load("worked_row_two_blocks.txt")
+    tol = g["tol"]
+    s, v = g["scores"], g["values"]
+    o, lse = _row_attention(s, v)
+    assert np.allclose(o, g["o"], atol=tol, rtol=0)
+    # the denominator: LSE = max + ln(l)
+    assert abs(math.exp(lse - s.max()) - g["l"]) < tol
+    # block 1 alone gives m1, l1 and its accumulator a1 = [1, e^-1]
+    o1, _, m1, l1 = oracle.online_softmax_blocked(s[:2], v[:2], int(g["block"]))
+    assert m1 == g["m1"] and abs(l1 - g["l1"]) < tol
+    assert np.allclose(o1 * l1, [1.0, math.exp(-1.0)], atol=1e-15)
+    # both blocks: the accumulator before the final division, and the result
+    ob, lseb, mb, lb = oracle.online_softmax_blocked(s, v, int(g["block"]))
+    assert np.allclose(ob * lb, g["a2"], atol=tol, rtol=0)
+    assert abs(lb - g["l"]) < tol and np.allclose(ob, g["o"], atol=tol, rtol=0)
+    assert abs(lseb - lse) < 1e-14
+
+
+def test_eight_scores_example():
+    g = load("eight_scores.txt")
+    tol = g["tol"]
+    s, v = g["scores"], g["values"]
+    o, lse = _row_attention(s, v)
+    assert abs(o[0] - g["o"]) < tol
+    p, m, l = oracle.masked_softmax(oracle.score_matrix(
+        np.ones((1, 1)), s.reshape(-1, 1), 1.0))
+    assert np.allclose(p[0], g["weights"], atol=g["weights_tol"], rtol=0)
+    blk = int(g["block"])
+    o1, _, m1, l1 = oracle.online_softmax_blocked(s[:blk], v[:blk], blk)
+    assert m1 == g["m1"] and abs(l1 - g["l1"]) < tol
+    assert abs(o1[0] * l1 - g["o_tilde1"]) < tol
+    # the second block on its own, relative to the new maximum 7
+    o2, _, m2, l2 = oracle.online_softmax_blocked(s[blk:], v[blk:], blk)
+    assert m2 == 7 and abs(l2 - g["block2_sum"]) < tol
+    assert abs(o2[0] * l2 - g["block2_times_v"]) < tol
+    assert abs(math.exp(m1 - m2) - g["alpha"]) < tol
+    ob, _, mb, lb = oracle.online_softmax_blocked(s, v, blk)
+    assert abs(lb - g["l"]) < tol
+    assert abs(ob[0] * lb - g["o_tilde"]) < g["o_tilde_tol"]
+    assert abs(ob[0] - o[0]) < 1e-12
+
+
+def test_lse_two_tiles():
+    g = load("lse_two_tiles.txt")
+    tol = g["tol"]
+    s = g["scores"]
+    v = np.eye(len(s))
+    _, lse = _row_attention(s, v)
+    assert abs(lse - g["lse"]) < g["lse_tol"]
+    o1, _, m1, l1 = oracle.online_softmax_blocked(s[:2], v[:2], 2)
+    assert m1 == g["m1"] and abs(l1 - g["l1"]) < tol
+    _, lseb, mb, lb = oracle.online_softmax_blocked(s, v, int(g["block"]))
+    assert abs(math.exp(m1 - mb) - g["correction"]) < tol
+    assert abs(lb - g["l"]) < tol
+    assert abs(mb + math.log(lb) - lse) < 1e-14
+
+
+def test_causal_pattern_3x3():
+    g = load("causal_3x3.txt")
+    allowed = g["allowed"].astype(bool)
+    r = _rng(1)
+    q = r.normal(size=(1, 1, 3, 4))
+    k = r.normal(size=(1, 1, 3, 4))
+    s = oracle.score_matrix(q[0, 0], k[0, 0], 0.5, causal=True)
+    assert np.array_equal(np.isfinite(s), allowed)
+    p, _, _ = oracle.masked_softmax(s)
+    assert np.all(p[~allowed] == 0.0)
+    assert np.all(p[allowed] > 0.0)
+    assert np.allclose(p.sum(axis=1), 1.0, atol=1e-15)
+
+
+def test_overflow_row():
+    # Understanding FlashAttention Pt 1, §2.2: x = [1000, 999] must not
+    # overflow; subtracting the maximum leaves [0, -1].
+    o, lse = _row_attention([1000.0, 999.0], np.eye(2))
+    e = math.exp(-1.0)
+    assert np.allclose(o, [1 / (1 + e), e / (1 + e)], atol=1e-15, rtol=0)
+    assert abs(lse - (1000.0 + math.log1p(e))) < 1e-12
+
+
+# ---------------------------------------------------------------- invariants
+
+def test_rows_sum_to_one_from_lse():
+    # flash-attention, Lab 3: exp(s - LSE) over a row sums to 1.
+    r = _rng(2)
+    q = r.normal(size=(2, 3, 40, 16))
+    k = r.normal(size=(2, 3, 56, 16))
+    v = r.normal(size=(2, 3, 56, 8))
+    bias = r.normal(size=(1, 3, 40, 56))
+    for causal in (False, True):
+        o, lse = oracle.attention_forward(q, k, v, scale=0.25, bias=bias,
+                                          causal=causal)
+        for b in range(2):
+            for h in range(3):
+                s = oracle.score_matrix(q[b, h], k[b, h], 0.25, bias[0, h],
+                                        causal=causal)
+                tot = np.exp(s - lse[b, h][:, None]).sum(axis=1)
+                assert np.all(np.abs(tot - 1.0) <= 1e-12)
+
+
+def test_row_shift_invariance():
+    # Adding a constant c_i to every score of row i leaves O unchanged and
+    # moves LSE_i by c_i (FlashAttention, Explained, §9).
+    r = _rng(3)
+    q = r.normal(size=(1, 2, 24, 8))
+    k = r.normal(size=(1, 2, 31, 8))
+    v = r.normal(size=(1, 2, 31, 5))
+    c = r.normal(size=(1, 2, 24, 1)) * 30.0
+    o0, l0 = oracle.attention_forward(q, k, v, scale=0.7)
+    o1, l1 = oracle.attention_forward(q, k, v, scale=0.7,
+                                      bias=np.broadcast_to(c, (1, 2, 24, 31)))
+    assert np.allclose(o1, o0, atol=1e-12, rtol=0)
+    assert np.allclose(l1, l0 + c[..., 0], atol=1e-11, rtol=0)
+
+
+def test_scalar_recurrence_matches_definition():
+    # Understanding FlashAttention Pt 1, §2.3: one key at a time.
+    r = _rng(4)
+    for n in (1, 2, 7, 100):
+        s = r.normal(size=n) * 3
+        v = r.normal(size=(n, 6))
+        o, lse = _row_attention(s, v)
+        o2, lse2, m2, l2 = oracle.online_softmax_scalar(s, v)
+        assert np.allclose(o2, o, atol=1e-12, rtol=0)
+        assert abs(lse2 - lse) <= 1e-12
+        assert m2 == s.max()
+
+
+def test_block_size_invariance():
+    # flash-attention, Lab 4: the blocked recurrence reproduces the direct
+    # result to ~1e-16 and does not depend on the block size.
+    r = _rng(0)
+    s = r.normal(size=64)
+    v = r.normal(size=(64, 8))
+    ref = np.exp(s - s.max())
+    ref /= ref.sum()
+    outs = []
+    for blk in (1, 3, 4, 64, 1000):
+        o, lse, _, _ = oracle.online_softmax_blocked(s, v, blk)
+        assert np.abs(o - ref @ v).max() < 1e-13
+        outs.append((o, lse))
+    for o, lse in outs[1:]:
+        assert np.abs(o - outs[0][0]).max() < 1e-13
+        assert abs(lse - outs[0][1]) < 1e-13
+    o, lse = _row_attention(s, v)
+    assert np.abs(o - outs[0][0]).max() < 1e-13
+
+
+def test_merge_identity():
+    # FlashAttention: Mathematical Foundations..., §7: partial (O, LSE) over
+    # disjoint key ranges merge into the full result.
+    r = _rng(5)
+    q = r.normal(size=(2, 2, 9, 8))
+    k = r.normal(size=(2, 2, 40, 8))
+    v = r.normal(size=(2, 2, 40, 3))
+    o, lse = oracle.attention_forward(q, k, v, scale=0.4)
+    for cut in (1, 17, 39):
+        pa = oracle.attention_forward(q, k[:, :, :cut], v[:, :, :cut], scale=0.4)
+        pb = oracle.attention_forward(q, k[:, :, cut:], v[:, :, cut:], scale=0.4)
+        om, lm = oracle.merge_partials([pa, pb])
+        assert np.allclose(om, o, atol=1e-13, rtol=0)
+        assert np.allclose(lm, lse, atol=1e-13, rtol=0)
+    # three parts, and a part that is empty (all keys masked)
+    parts = [oracle.attention_forward(q, k[:, :, a:b], v[:, :, a:b], scale=0.4)
+             for a, b in ((0, 10), (10, 25), (25, 40))]
+    empty = (np.zeros_like(o), np.full(lse.shape, -np.inf))
+    om, lm = oracle.merge_partials(parts + [empty])
+    assert np.allclose(om, o, atol=1e-13, rtol=0)
+    assert np.allclose(lm, lse, atol=1e-13, rtol=0)
+
+
+# ---------------------------------------------------------------- closed forms
+
+def test_single_key():
+    r = _rng(6)
+    q = r.normal(size=(1, 1, 5, 4))
+    k = r.normal(size=(1, 1, 1, 4))
+    v = r.normal(size=(1, 1, 1, 3))
+    o, lse = oracle.attention_forward(q, k, v, scale=0.3)
+    assert np.allclose(o[0, 0], np.broadcast_to(v[0, 0, 0], (5, 3)), atol=1e-15)
+    assert np.allclose(lse[0, 0], 0.3 * (q[0, 0] @ k[0, 0, 0]), atol=1e-14)
+
+
+def test_equal_scores_give_mean():
+    r = _rng(7)
+    nk = 13
+    q = np.zeros((1, 1, 3, 4))
+    k = r.normal(size=(1, 1, nk, 4))
+    v = r.normal(size=(1, 1, nk, 2))
+    o, lse = oracle.attention_forward(q, k, v, scale=1.0,
+                                      bias=np.full((1, 1, 3, nk), 2.5))
+    assert np.allclose(o[0, 0], v[0, 0].mean(axis=0), atol=1e-14)
+    assert np.allclose(lse, 2.5 + math.log(nk), atol=1e-14)
+
+
+def test_causal_first_row_and_last_row():
+    r = _rng(8)
+    q = r.normal(size=(1, 1, 6, 4))
+    k = r.normal(size=(1, 1, 6, 4))
+    v = r.normal(size=(1, 1, 6, 3))
+    o, lse = oracle.attention_forward(q, k, v, scale=0.5, causal=True)
+    assert np.allclose(o[0, 0, 0], v[0, 0, 0], atol=1e-15)
+    assert abs(lse[0, 0, 0] - 0.5 * q[0, 0, 0] @ k[0, 0, 0]) < 1e-14
+    on, ln_ = oracle.attention_forward(q, k, v, scale=0.5)
+    assert np.allclose(o[0, 0, -1], on[0, 0, -1], atol=1e-15)
+    assert abs(lse[0, 0, -1] - ln_[0, 0, -1]) < 1e-14
+
+
+def test_causal_bottom_right_alignment():
+    # flash-attention, Q10: with fewer queries than keys the last query sees
+    # every key; with more queries than keys the first rows see none.
+    r = _rng(9)
+    k = r.normal(size=(1, 1, 7, 4))
+    v = r.normal(size=(1, 1, 7, 2))
+    q = r.normal(size=(1, 1, 3, 4))
+    o, lse = oracle.attention_forward(q, k, v, scale=1.0, causal=True)
+    for i in range(3):
+        ref_o, ref_l = oracle.attention_forward(q[:, :, i:i + 1], k[:, :, :5 + i],
+                                                v[:, :, :5 + i], scale=1.0)
+        assert np.allclose(o[0, 0, i], ref_o[0, 0, 0], atol=1e-15)
+        assert abs(lse[0, 0, i] - ref_l[0, 0, 0]) < 1e-14
+    q2 = r.normal(size=(1, 1, 10, 4))
+    o2, l2 = oracle.attention_forward(q2, k, v, scale=1.0, causal=True)
+    assert np.all(o2[0, 0, :3] == 0.0) and np.all(l2[0, 0, :3] == -np.inf)
+    assert np.all(np.isfinite(l2[0, 0, 3:]))
+    assert np.allclose(o2[0, 0, 3], v[0, 0, 0], atol=1e-15)
+
+
+def test_one_dominant_key():
+    r = _rng(10)
+    q = r.normal(size=(1, 1, 4, 8))
+    k = r.normal(size=(1, 1, 9, 8))
+    v = r.normal(size=(1, 1, 9, 5))
+    bias = np.zeros((1, 1, 4, 9))
+    bias[0, 0, np.arange(4), [2, 5, 0, 8]] = 1e3
+    o, _ = oracle.attention_forward(q, k, v, scale=0.1, bias=bias)
+    assert np.allclose(o[0, 0], v[0, 0, [2, 5, 0, 8]], atol=1e-12)
+
+
+# ---------------------------------------------------------------- masks
+
+def test_kv_len_masks():
+    r = _rng(11)
+    q = r.normal(size=(3, 2, 5, 4))
+    k = r.normal(size=(3, 2, 12, 4))
+    v = r.normal(size=(3, 2, 12, 3))
+    lens = np.array([12, 7, 0])
+    o, lse = oracle.attention_forward(q, k, v, scale=0.5, kv_len=lens)
+    full_o, full_l = oracle.attention_forward(q, k, v, scale=0.5)
+    assert np.array_equal(o[0], full_o[0]) and np.array_equal(lse[0], full_l[0])
+    # key length 7 equals truncating the keys, and equals a -inf bias
+    t_o, t_l = oracle.attention_forward(q[1:2], k[1:2, :, :7], v[1:2, :, :7],
+                                        scale=0.5)
+    assert np.allclose(o[1], t_o[0], atol=1e-15)
+    assert np.allclose(lse[1], t_l[0], atol=1e-14)
+    bias = np.zeros((1, 1, 5, 12))
+    bias[..., 7:] = -np.inf
+    b_o, b_l = oracle.attention_forward(q[1:2], k[1:2], v[1:2], scale=0.5,
+                                        bias=bias)
+    assert np.array_equal(b_o[0], o[1]) and np.array_equal(b_l[0], lse[1])
+    s = oracle.score_matrix(q[1, 0], k[1, 0], 0.5, valid_keys=7)
+    p, _, _ = oracle.masked_softmax(s)
+    assert np.all(p[:, 7:] == 0.0)
+    # length 0: every key hidden -> zeros and -inf, never NaN
+    assert np.all(o[2] == 0.0) and np.all(lse[2] == -np.inf)
+    assert not np.isnan(o).any()
+
+
+def test_rows_subset_matches_full():
+    r = _rng(12)
+    q = r.normal(size=(2, 3, 20, 8))
+    k = r.normal(size=(2, 3, 26, 8))
+    v = r.normal(size=(2, 3, 26, 4))
+    bias = r.normal(size=(1, 3, 20, 26))
+    lens = np.array([26, 9])
+    o, lse = oracle.attention_forward(q, k, v, scale=0.3, bias=bias,
+                                      kv_len=lens, causal=True)
+    rows = [(0, 0, 0), (1, 2, 19), (0, 1, 7), (1, 0, 3), (1, 0, 4)]
+    ro, rl = oracle.attention_rows(q, k, v, rows, scale=0.3, bias=bias,
+                                   kv_len=lens, causal=True)
+    for n, (b, h, i) in enumerate(rows):
+        assert np.allclose(ro[n], o[b, h, i], atol=1e-15)
+        assert rl[n] == lse[b, h, i] or abs(rl[n] - lse[b, h, i]) < 1e-14
+
+
+# ---------------------------------------------------------------- independent evaluations
+
+def test_decimal_50_digits():
+    """The definition evaluated in 50-digit decimal arithmetic (no numpy, no
+    max subtraction); the oracle must agree to 1e-13."""
+    getcontext().prec = 50
+    r = _rng(13)
+    nq, nk, d, dv = 3, 5, 4, 3
+    q = r.normal(size=(nq, d))
+    k = r.normal(size=(nk, d))
+    v = r.normal(size=(nk, dv))
+    bias = r.normal(size=(nq, nk))
+    scale = 0.37
+    o, lse = oracle.attention_forward(q[None, None], k[None, None], v[None, None],
+                                      scale=scale, bias=bias[None, None])
+    D = Decimal
+    for i in range(nq):
+        sc = []
+        for j in range(nk):
+            dot = sum(D(float(q[i, t])) * D(float(k[j, t])) for t in range(d))
+            sc.append(D(scale) * dot + D(float(bias[i, j])))
+        ex = [x.exp() for x in sc]
+        tot = sum(ex)
+        for c in range(dv):
+            want = sum(ex[j] * D(float(v[j, c])) for j in range(nk)) / tot
+            assert abs(float(want) - o[0, 0, i, c]) < 1e-13
+        assert abs(float(tot.ln()) - lse[0, 0, i]) < 1e-13
+
+
+def test_brute_force_loops():
+    """Plain loops with exp(s) / sum exp(s) (no max subtraction) on tiny
+    inputs with a bias, causal masking and a key length."""
+    r = _rng(14)
+    B, H, nq, nk, d, dv = 2, 2, 4, 6, 3, 2
+    q = r.normal(size=(B, H, nq, d))
+    k = r.normal(size=(B, H, nk, d))
+    v = r.normal(size=(B, H, nk, dv))
+    bias = r.normal(size=(B, 1, nq, nk))
+    lens = [6, 4]
+    scale = 0.8
+    o, lse = oracle.attention_forward(q, k, v, scale=scale, bias=bias,
+                                      kv_len=lens, causal=True)
+    for b in range(B):
+        for h in range(H):
+            for i in range(nq):
+                w = []
+                for j in range(nk):
+                    ok = j < lens[b] and j <= i + (nk - nq)
+                    if ok:
+                        s = scale * sum(q[b, h, i, t] * k[b, h, j, t] for t in range(d))
+                        w.append(math.exp(s + bias[b, 0, i, j]))
+                    else:
+                        w.append(0.0)
+                tot = sum(w)
+                assert abs(math.log(tot) - lse[b, h, i]) < 1e-13
+                for c in range(dv):
+                    want = sum(w[j] * v[b, h, j, c] for j in range(nk)) / tot
+                    assert abs(want - o[b, h, i, c]) < 1e-14
+
+
+def test_layout_is_batch_head_seq_dim():
+    # A [B, H, N, d] input whose H and N are swapped must give a different
+    # answer: the oracle attends over axis 2.
+    r = _rng(15)
+    q = r.normal(size=(1, 3, 5, 4))
+    k = r.normal(size=(1, 3, 5, 4))
+    v = r.normal(size=(1, 3, 5, 4))
+    o, _ = oracle.attention_forward(q, k, v, scale=0.5)
+    for h in range(3):
+        oh, _ = oracle.attention_forward(q[:, h:h + 1], k[:, h:h + 1],
+                                         v[:, h:h + 1], scale=0.5)
+        assert np.allclose(o[:, h], oh[:, 0], atol=1e-15)
+    ot, _ = oracle.attention_forward(q.transpose(0, 2, 1, 3), k.transpose(0, 2, 1, 3),
+                                     v.transpose(0, 2, 1, 3), scale=0.5)
+    assert not np.allclose(ot.transpose(0, 2, 1, 3), o, atol=1e-3)
