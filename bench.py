@@ -1,0 +1,163 @@
+"""Benchmark of the fused attention forward on one MI355X.
+
+One step = one attn_fwd call over the whole workload (all of B x H x Nq x Nk),
+with inputs already resident in device memory. Prints ONE JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+The default workload is B=2, H=32, N=4096, d=128, bf16, non-causal.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3     # MI355X dense fp32 matrix
+KERNEL_SRC = {"bf16": "exact_io_aware_06_amd/csrc/fwd_bf16.hip",
+              "f32": "exact_io_aware_06_amd/csrc/fwd_f32.hip"}
+
+
+def _src_hash(rel):
+    with open(os.path.join(ROOT, rel), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def _traffic(workload, dtype):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    the kernel source has not changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.lstrip().startswith("#"):
+            a, b = line.split(":", 1)
+            kv[a.strip()] = b.strip()
+    if kv.get("source_sha256") != _src_hash(KERNEL_SRC[dtype]):
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:
+        return 1
+
+
+def cpu_baseline(inp, w, budget_s=15.0):
+    """Time the fp64 oracle, as it stands, on whole (b, h) heads of the same
+    inputs until the time budget is spent; report the rate in TFLOP/s."""
+    import oracle
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    done = 0
+    t0 = time.perf_counter()
+    for b, h in heads:
+        oracle.attention_forward(q[b:b + 1, h:h + 1].double().numpy(),
+                                 k[b:b + 1, h:h + 1].double().numpy(),
+                                 v[b:b + 1, h:h + 1].double().numpy(),
+                                 scale=inp["scale"], causal=w.causal)
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = w.flops() * done / len(heads)
+    return {
+        "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": _blas_threads(),
+        "kind": "oracle",
+        "sample": (f"{done} of {len(heads)} (b,h) heads of {w.name} at full "
+                   f"Nq=Nk={w.Nq}, fp64 materialising S and P, {dt:.1f} s"),
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the "
+              "forward has no multi-GPU path", file=sys.stderr)
+        return 2
+
+    import torch
+    import workloads
+    import exact_io_aware_06_amd as ea
+
+    name = args.workload or workloads.HEADLINE
+    w = workloads.CONFIGS[name]
+    inp = workloads.make_inputs(w)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, k, v = (inp[x].to(dev) for x in ("q", "k", "v"))
+    bias = inp["bias"].to(dev) if inp["bias"] is not None else None
+    kv_len = inp["kv_len"].to(dev) if inp["kv_len"] is not None else None
+    o = torch.empty_like(q)
+    lse = torch.empty(w.B, w.H, w.Nq, dtype=torch.float32, device=dev)
+
+    def step():
+        ea.attn_fwd(q, k, v, bias=bias, kv_len=kv_len, causal=w.causal,
+                    scale=inp["scale"], out=o, lse=lse)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+
+    flops = w.flops()
+    tflops = flops / (ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
+                "traffic": _traffic(name, w.dtype)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(inp, w, args.cpu_budget)
+        cpu["value"] = round(cpu["value"], 6)
+
+    out = {
+        "metric": "attention fwd TFLOP/s and % of bf16 MFMA peak at 1 MI355X (N=4096,d=128)",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {**w.describe(), "flops_per_step": flops, "parallelism": "single GPU"},
+        "roofline": roofline, "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

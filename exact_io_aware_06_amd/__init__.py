@@ -1,0 +1,161 @@
+"""Fused exact attention forward for AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding over ``libattn.so``, whose C ABI is declared in
+``include/attn.h``. The binding only marshals arguments: it allocates the
+outputs with PyTorch, passes device pointers, shapes, strides and the current
+HIP stream, and raises on a non-OK status. Every arithmetic step of the
+forward runs in the HIP kernels; there is no CPU fallback, and using this
+module without the built library or without a GPU raises.
+
+    from exact_io_aware_06_amd import attn_fwd
+    o, lse = attn_fwd(q, k, v, causal=True)    # q, k, v: [B, H, N, d] on cuda
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+__all__ = ["attn_fwd", "attn_fwd_raw", "AttnError", "load_library", "library_path",
+           "AttnTensor", "AttnMask", "ATTN_OK", "ATTN_ERR_INVALID",
+           "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_HIP", "ATTN_BF16", "ATTN_F32"]
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+ATTN_OK, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, 1, 2, 3
+ATTN_BF16, ATTN_F32 = 0, 1
+_STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_INVALID", 2: "ATTN_ERR_UNSUPPORTED", 3: "ATTN_ERR_HIP"}
+
+
+class AttnTensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32),
+                ("shape", ctypes.c_int64 * 4), ("stride", ctypes.c_int64 * 4)]
+
+
+class AttnMask(ctypes.Structure):
+    _fields_ = [("bias", ctypes.POINTER(AttnTensor)), ("kv_len", ctypes.c_void_p)]
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+def library_path() -> str:
+    return os.environ.get("ATTN_LIBRARY", os.path.join(HERE, "libattn.so"))
+
+
+_lib = None
+
+
+def load_library():
+    """Load ``libattn.so`` (built in-tree by ``exact_io_aware_06_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m exact_io_aware_06_amd.build` "
+            "(the forward has no CPU fallback)")
+    lib = ctypes.CDLL(path)
+    P = ctypes.POINTER(AttnTensor)
+    lib.attn_fwd.argtypes = [P, P, P, ctypes.POINTER(AttnMask), ctypes.c_int, ctypes.c_float,
+                             P, P, ctypes.c_void_p]
+    lib.attn_fwd.restype = ctypes.c_int
+    lib.attn_last_error.argtypes = []
+    lib.attn_last_error.restype = ctypes.c_char_p
+    lib.attn_abi_version.argtypes = []
+    lib.attn_abi_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def make_desc(data_ptr: int, dtype: int, shape, stride) -> AttnTensor:
+    t = AttnTensor()
+    t.data = data_ptr
+    t.dtype = dtype
+    for i in range(4):
+        t.shape[i] = int(shape[i])
+        t.stride[i] = int(stride[i])
+    return t
+
+
+def attn_fwd_raw(q: AttnTensor, k: AttnTensor, v: AttnTensor, mask: Optional[AttnMask],
+                 causal: bool, scale: float, o: AttnTensor, lse: AttnTensor,
+                 stream: int = 0) -> int:
+    """Call the C entry point with prepared descriptors; returns the status."""
+    lib = load_library()
+    return lib.attn_fwd(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v),
+                        ctypes.byref(mask) if mask is not None else None,
+                        1 if causal else 0, float(scale), ctypes.byref(o),
+                        ctypes.byref(lse), ctypes.c_void_p(stream))
+
+
+def last_error() -> str:
+    return load_library().attn_last_error().decode()
+
+
+def _torch_desc(t, name):
+    import torch
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be 4-D [B, H, N, d], got {tuple(t.shape)}")
+    if t.dtype == torch.bfloat16:
+        dt = ATTN_BF16
+    elif t.dtype == torch.float32:
+        dt = ATTN_F32
+    else:
+        raise TypeError(f"{name}: dtype {t.dtype} is not supported (bfloat16 or float32)")
+    return make_desc(t.data_ptr(), dt, t.shape, t.stride())
+
+
+def attn_fwd(q, k, v, bias=None, kv_len=None, causal: bool = False,
+             scale: Optional[float] = None, out=None, lse=None):
+    """O = softmax_row(scale * Q K^T + bias) V and the row log-sum-exp.
+
+    q: [B, H, Nq, d], k and v: [B, Hk, Nk, d] (Hk divides H), bfloat16 or
+    float32 CUDA/HIP tensors with a contiguous last dimension. bias: optional
+    float32 [B|1, H|1, Nq, Nk], added unscaled. kv_len: optional int32 [B] on
+    the same device; keys at or past kv_len[b] are masked. causal hides key j
+    from query i when j > i + (Nk - Nq). scale defaults to 1/sqrt(d).
+    Returns (o [B, H, Nq, d] in q's dtype, lse [B, H, Nq] float32).
+    """
+    import torch
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k and v must be GPU tensors (no CPU path exists)")
+    B, H, Nq, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, H, Nq, d), dtype=q.dtype, device=dev)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=dev)
+    if lse.dim() != 3 or lse.dtype != torch.float32:
+        raise ValueError("lse must be a float32 [B, H, Nq] tensor")
+    qd, kd, vd, od = (_torch_desc(t, n) for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out")))
+    ld = make_desc(lse.data_ptr(), ATTN_F32, (*lse.shape, 1), (*lse.stride(), 1))
+    mask = None
+    bias_desc = None
+    if bias is not None or kv_len is not None:
+        mask = AttnMask()
+        if bias is not None:
+            if bias.dtype != torch.float32 or not bias.is_cuda or bias.dim() != 4:
+                raise ValueError("bias must be a float32 4-D GPU tensor")
+            bias_desc = make_desc(bias.data_ptr(), ATTN_F32, bias.shape, bias.stride())
+            mask.bias = ctypes.pointer(bias_desc)
+        if kv_len is not None:
+            if kv_len.dtype != torch.int32 or not kv_len.is_cuda or kv_len.numel() != B:
+                raise ValueError("kv_len must be an int32 GPU tensor with B entries")
+            if not kv_len.is_contiguous():
+                raise ValueError("kv_len must be contiguous")
+            mask.kv_len = kv_len.data_ptr()
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        rc = attn_fwd_raw(qd, kd, vd, mask, causal, scale, od, ld, stream)
+    if rc != ATTN_OK:
+        raise AttnError(rc, last_error())
+    return out, lse

@@ -1,0 +1,195 @@
+// C ABI front end: argument validation, error reporting and dispatch.
+//
+// Every check runs on the host before any HIP call, so a rejected call never
+// touches the device (and can be exercised on a machine without a GPU). The
+// checks mirror the contract written in include/attn.h; the host-side checks
+// that a kernel needs before launch (head dimension, dtype, last-dimension
+// contiguity, output allocation) follow the C++ layer described in
+// "flash-attention" (stanleyjacob.dev), Part IV, stage 3, except that here the
+// caller allocates the outputs.
+
+#include "../../include/attn.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "fwd_params.h"
+
+namespace attn {
+const char* hip_error_text(int code);  // runtime.hip
+}
+
+namespace {
+
+thread_local std::string g_last_error;
+
+attn_status_t fail(attn_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+int64_t elem_bytes(int32_t dt) { return dt == ATTN_BF16 ? 2 : 4; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Common checks on a 4-D input/output view of dtype `dt`.
+attn_status_t check_view(const char* name, const attn_tensor_t* t, int32_t dt) {
+  if (t == nullptr) return fail(ATTN_ERR_INVALID, "%s: descriptor is NULL", name);
+  for (int i = 0; i < 4; ++i) {
+    if (t->shape[i] < 0) return fail(ATTN_ERR_INVALID, "%s: negative extent %lld in dim %d", name,
+                                     (long long)t->shape[i], i);
+    if (t->stride[i] < 0)
+      return fail(ATTN_ERR_UNSUPPORTED, "%s: negative stride in dim %d", name, i);
+  }
+  if (t->dtype != dt)
+    return fail(ATTN_ERR_INVALID, "%s: dtype %d, expected %d", name, (int)t->dtype, (int)dt);
+  return ATTN_OK;
+}
+
+attn_status_t check_rows(const char* name, const attn_tensor_t* t) {
+  // bf16 and f32 rows must start on 16-byte boundaries for vector loads
+  const int64_t eb = elem_bytes(t->dtype);
+  if (t->shape[3] > 1 && t->stride[3] != 1)
+    return fail(ATTN_ERR_UNSUPPORTED, "%s: last dimension must be contiguous (stride[3] == 1)", name);
+  for (int i = 0; i < 3; ++i)
+    if (t->shape[i] > 1 && (t->stride[i] * eb) % 16 != 0)
+      return fail(ATTN_ERR_UNSUPPORTED, "%s: stride[%d] = %lld elements is not a multiple of 16 bytes",
+                  name, i, (long long)t->stride[i]);
+  if (!aligned16(t->data))
+    return fail(ATTN_ERR_UNSUPPORTED, "%s: data pointer is not 16-byte aligned", name);
+  return ATTN_OK;
+}
+
+int64_t st(const attn_tensor_t* t, int i) { return t->shape[i] > 1 ? t->stride[i] : 0; }
+
+constexpr int64_t kMaxExtent = (int64_t)1 << 30;
+
+}  // namespace
+
+extern "C" {
+
+int attn_abi_version(void) { return ATTN_ABI_VERSION; }
+
+const char* attn_last_error(void) { return g_last_error.c_str(); }
+
+attn_status_t attn_fwd(const attn_tensor_t* q, const attn_tensor_t* k, const attn_tensor_t* v,
+                       const attn_mask_t* bias_or_mask, int causal, float scale,
+                       const attn_tensor_t* o, const attn_tensor_t* lse, void* stream) {
+  g_last_error.clear();
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || lse == nullptr)
+    return fail(ATTN_ERR_INVALID, "q, k, v, o and lse descriptors must be non-NULL");
+  const int32_t dt = q->dtype;
+  if (dt != ATTN_BF16 && dt != ATTN_F32)
+    return fail(ATTN_ERR_UNSUPPORTED, "q: dtype %d is neither ATTN_BF16 nor ATTN_F32", (int)dt);
+  attn_status_t s;
+  if ((s = check_view("q", q, dt)) != ATTN_OK) return s;
+  if ((s = check_view("k", k, dt)) != ATTN_OK) return s;
+  if ((s = check_view("v", v, dt)) != ATTN_OK) return s;
+  if ((s = check_view("o", o, dt)) != ATTN_OK) return s;
+  if ((s = check_view("lse", lse, ATTN_F32)) != ATTN_OK) return s;
+
+  const int64_t B = q->shape[0], H = q->shape[1], Nq = q->shape[2], d = q->shape[3];
+  const int64_t Hk = k->shape[1], Nk = k->shape[2];
+  if (k->shape[0] != B || v->shape[0] != B)
+    return fail(ATTN_ERR_INVALID, "batch mismatch: q %lld, k %lld, v %lld", (long long)B,
+                (long long)k->shape[0], (long long)v->shape[0]);
+  if (v->shape[1] != Hk || v->shape[2] != Nk)
+    return fail(ATTN_ERR_INVALID, "k and v must have the same [B, Hk, Nk] extents");
+  if (k->shape[3] != d || v->shape[3] != d)
+    return fail(ATTN_ERR_INVALID, "head dimension mismatch: q %lld, k %lld, v %lld", (long long)d,
+                (long long)k->shape[3], (long long)v->shape[3]);
+  if (o->shape[0] != B || o->shape[1] != H || o->shape[2] != Nq || o->shape[3] != d)
+    return fail(ATTN_ERR_INVALID, "o must be [B, H, Nq, d] like q");
+  if (lse->shape[0] != B || lse->shape[1] != H || lse->shape[2] != Nq || lse->shape[3] != 1)
+    return fail(ATTN_ERR_INVALID, "lse must be [B, H, Nq, 1]");
+  if (H > 0 && (Hk < 1 || H % Hk != 0))
+    return fail(ATTN_ERR_INVALID, "key/value heads (%lld) must divide query heads (%lld)",
+                (long long)Hk, (long long)H);
+  if (!(std::isfinite(scale) && scale > 0.f))
+    return fail(ATTN_ERR_INVALID, "scale must be finite and > 0 (got %g)", (double)scale);
+  if (B > kMaxExtent || H > kMaxExtent || Nq > kMaxExtent || Nk > kMaxExtent)
+    return fail(ATTN_ERR_UNSUPPORTED, "extents above 2^30 are not supported");
+  if (d != 64 && d != 128)
+    return fail(ATTN_ERR_UNSUPPORTED, "head dimension %lld is not supported (64 or 128)", (long long)d);
+
+  const attn_tensor_t* bias = bias_or_mask ? bias_or_mask->bias : nullptr;
+  const int32_t* kv_len = bias_or_mask ? bias_or_mask->kv_len : nullptr;
+  if (bias != nullptr) {
+    if ((s = check_view("bias", bias, ATTN_F32)) != ATTN_OK) return s;
+    if (!(bias->shape[0] == B || bias->shape[0] == 1) || !(bias->shape[1] == H || bias->shape[1] == 1) ||
+        bias->shape[2] != Nq || bias->shape[3] != Nk)
+      return fail(ATTN_ERR_INVALID, "bias must be [B|1, H|1, Nq, Nk]");
+  }
+
+  // empty work: nothing to write
+  if (B == 0 || H == 0 || Nq == 0) return ATTN_OK;
+
+  if ((s = check_rows("q", q)) != ATTN_OK) return s;
+  if ((s = check_rows("o", o)) != ATTN_OK) return s;
+  if (Nk > 0) {
+    if ((s = check_rows("k", k)) != ATTN_OK) return s;
+    if ((s = check_rows("v", v)) != ATTN_OK) return s;
+  }
+  if (lse->data == nullptr || (reinterpret_cast<uintptr_t>(lse->data) & 3u) != 0)
+    return fail(ATTN_ERR_UNSUPPORTED, "lse: data pointer is NULL or not 4-byte aligned");
+  if (Nq > 1 && lse->stride[2] != 1)
+    return fail(ATTN_ERR_UNSUPPORTED, "lse: rows must be contiguous (stride[2] == 1)");
+  bool bias_vec = false;
+  if (bias != nullptr && Nk > 0) {
+    if (Nk > 1 && bias->stride[3] != 1)
+      return fail(ATTN_ERR_UNSUPPORTED, "bias: last dimension must be contiguous (stride[3] == 1)");
+    if (bias->data == nullptr || (reinterpret_cast<uintptr_t>(bias->data) & 3u) != 0)
+      return fail(ATTN_ERR_UNSUPPORTED, "bias: data pointer is NULL or not 4-byte aligned");
+    // rows that all start on 16-byte boundaries are read with vector loads
+    bias_vec = aligned16(bias->data);
+    for (int i = 0; i < 3; ++i)
+      if (bias->shape[i] > 1 && bias->stride[i] % 4 != 0) bias_vec = false;
+  }
+
+  attn::FwdParams p{};
+  p.q = q->data;
+  p.k = k->data;
+  p.v = v->data;
+  p.o = o->data;
+  p.lse = static_cast<float*>(lse->data);
+  p.bias = bias ? static_cast<const float*>(bias->data) : nullptr;
+  p.kv_len = kv_len;
+  p.q_sb = st(q, 0); p.q_sh = st(q, 1); p.q_sn = st(q, 2);
+  p.k_sb = st(k, 0); p.k_sh = st(k, 1); p.k_sn = st(k, 2);
+  p.v_sb = st(v, 0); p.v_sh = st(v, 1); p.v_sn = st(v, 2);
+  p.o_sb = st(o, 0); p.o_sh = st(o, 1); p.o_sn = st(o, 2);
+  p.l_sb = st(lse, 0); p.l_sh = st(lse, 1);
+  if (bias) {
+    p.bias_sb = st(bias, 0);
+    p.bias_sh = st(bias, 1);
+    p.bias_sn = st(bias, 2);
+  }
+  p.B = (int32_t)B;
+  p.H = (int32_t)H;
+  p.Hk = (int32_t)Hk;
+  p.Nq = (int32_t)Nq;
+  p.Nk = (int32_t)Nk;
+  p.head_group = (int32_t)(H / Hk);
+  p.causal = causal ? 1 : 0;
+  p.bias_vec = bias_vec ? 1 : 0;
+  p.scale_log2 = scale * 1.44269504088896341f;
+
+  // grid size: 8 * ceil(B*H*ceil(Nq/16)/8) workgroups at most (f32 tiles are smallest)
+  const int64_t tiles = B * H * ((Nq + 15) / 16);
+  if (tiles > ((int64_t)1 << 31) - 64)
+    return fail(ATTN_ERR_UNSUPPORTED, "problem needs more than 2^31 workgroups");
+
+  const int rc = (dt == ATTN_BF16) ? attn::launch_fwd_bf16(p, (int)d, stream)
+                                   : attn::launch_fwd_f32(p, (int)d, stream);
+  if (rc != 0) return fail(ATTN_ERR_HIP, "kernel launch failed: %s", attn::hip_error_text(rc));
+  return ATTN_OK;
+}
+
+}  // extern "C"

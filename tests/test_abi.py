@@ -1,0 +1,187 @@
+"""The C ABI library without a GPU: it loads, exports every function that
+include/attn.h declares, its structs match the ctypes mirrors, and every
+malformed call is rejected on the host with the documented status before any
+HIP call is made."""
+
+import ctypes
+import math
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+import exact_io_aware_06_amd as ea
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+
+def _lib():
+    if not os.path.exists(ea.library_path()):
+        pytest.fail("libattn.so is not built; run `python -m exact_io_aware_06_amd.build`")
+    return ea.load_library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function():
+    lib = _lib()
+    names = _declared_functions()
+    assert names == ["attn_abi_version", "attn_fwd", "attn_last_error"]
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", ea.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (attn_\w+)", out))
+    assert set(names) <= exported
+
+
+def test_abi_version_matches_header():
+    m = re.search(r"#define ATTN_ABI_VERSION (\d+)", open(HEADER).read())
+    assert _lib().attn_abi_version() == int(m.group(1))
+
+
+def test_struct_layout_matches_header():
+    src = r"""
+    #include <stdio.h>
+    #include <stddef.h>
+    #include "attn.h"
+    int main(void) {
+      printf("%zu %zu %zu %zu %zu %zu %zu\n", sizeof(attn_tensor_t),
+             offsetof(attn_tensor_t, dtype), offsetof(attn_tensor_t, shape),
+             offsetof(attn_tensor_t, stride), sizeof(attn_mask_t),
+             offsetof(attn_mask_t, kv_len), sizeof(attn_status_t));
+      return 0;
+    }
+    """
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "layout.c")
+        exe = os.path.join(d, "layout")
+        open(c, "w").write(src)
+        subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), c, "-o", exe],
+                       check=True)
+        vals = [int(x) for x in subprocess.run([exe], capture_output=True, text=True,
+                                               check=True).stdout.split()]
+    T, M = ea.AttnTensor, ea.AttnMask
+    assert vals == [ctypes.sizeof(T), T.dtype.offset, T.shape.offset, T.stride.offset,
+                    ctypes.sizeof(M), M.kv_len.offset, 4]
+
+
+# ------------------------------------------------------------ host-side rejections
+
+def _desc(shape, dtype=ea.ATTN_BF16, data=0x10000, stride=None):
+    if stride is None:
+        stride = [shape[1] * shape[2] * shape[3], shape[2] * shape[3], shape[3], 1]
+    return ea.make_desc(data, dtype, shape, stride)
+
+
+def _call(q=None, k=None, v=None, o=None, lse=None, mask=None, causal=0, scale=0.125,
+          **over):
+    B, H, N, d = over.get("shape", (2, 4, 64, 64))
+    q = q or _desc((B, H, N, d))
+    k = k or _desc((B, H, N, d), data=0x20000)
+    v = v or _desc((B, H, N, d), data=0x30000)
+    o = o or _desc((B, H, N, d), data=0x40000)
+    lse = lse or _desc((B, H, N, 1), ea.ATTN_F32, data=0x50000, stride=[H * N, N, 1, 1])
+    _lib()
+    return ea.attn_fwd_raw(q, k, v, mask, causal, scale, o, lse, 0)
+
+
+def test_null_descriptor():
+    lib = _lib()
+    d = _desc((1, 1, 8, 64))
+    rc = lib.attn_fwd(None, ctypes.byref(d), ctypes.byref(d), None, 0, 0.125,
+                      ctypes.byref(d), ctypes.byref(d), None)
+    assert rc == ea.ATTN_ERR_INVALID
+    assert "non-NULL" in ea.last_error()
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.1, math.inf, math.nan])
+def test_bad_scale(scale):
+    assert _call(scale=scale) == ea.ATTN_ERR_INVALID
+    assert "scale" in ea.last_error()
+
+
+def test_unsupported_head_dim():
+    s = (1, 2, 16, 96)
+    assert _call(shape=s, q=_desc(s), k=_desc(s), v=_desc(s), o=_desc(s)) == ea.ATTN_ERR_UNSUPPORTED
+    assert "head dimension" in ea.last_error()
+
+
+def test_dtype_mismatch_and_unknown_dtype():
+    s = (2, 4, 64, 64)
+    assert _call(k=_desc(s, ea.ATTN_F32)) == ea.ATTN_ERR_INVALID
+    assert _call(q=_desc(s, 7), k=_desc(s, 7), v=_desc(s, 7), o=_desc(s, 7)) == ea.ATTN_ERR_UNSUPPORTED
+    bad_lse = _desc((2, 4, 64, 1), ea.ATTN_BF16, stride=[256, 64, 1, 1])
+    assert _call(lse=bad_lse) == ea.ATTN_ERR_INVALID
+
+
+def test_shape_mismatches():
+    assert _call(o=_desc((2, 4, 63, 64))) == ea.ATTN_ERR_INVALID
+    assert _call(k=_desc((2, 4, 64, 128))) == ea.ATTN_ERR_INVALID
+    assert _call(v=_desc((2, 4, 32, 64))) == ea.ATTN_ERR_INVALID
+    assert _call(k=_desc((1, 4, 64, 64)), v=_desc((1, 4, 64, 64))) == ea.ATTN_ERR_INVALID
+    # key/value heads must divide query heads
+    assert _call(k=_desc((2, 3, 64, 64)), v=_desc((2, 3, 64, 64))) == ea.ATTN_ERR_INVALID
+    assert "divide" in ea.last_error()
+    lse = _desc((2, 4, 64, 2), ea.ATTN_F32)
+    assert _call(lse=lse) == ea.ATTN_ERR_INVALID
+
+
+def test_negative_extent_and_stride():
+    assert _call(q=_desc((2, 4, -1, 64), stride=[1, 1, 1, 1])) == ea.ATTN_ERR_INVALID
+    assert _call(q=_desc((2, 4, 64, 64), stride=[-16384, 4096, 64, 1])) == ea.ATTN_ERR_UNSUPPORTED
+
+
+def test_layout_requirements():
+    s = (2, 4, 64, 64)
+    assert _call(q=_desc(s, stride=[16384, 4096, 64, 2])) == ea.ATTN_ERR_UNSUPPORTED
+    assert "contiguous" in ea.last_error()
+    assert _call(q=_desc(s, data=0x10002)) == ea.ATTN_ERR_UNSUPPORTED
+    assert "aligned" in ea.last_error()
+    assert _call(k=_desc(s, stride=[16384, 4096, 68, 1], data=0x20000)) == ea.ATTN_ERR_UNSUPPORTED
+    lse = _desc((2, 4, 64, 1), ea.ATTN_F32, data=0x50000, stride=[256, 64, 2, 1])
+    assert _call(lse=lse) == ea.ATTN_ERR_UNSUPPORTED
+
+
+def test_bias_checks():
+    m = ea.AttnMask()
+    b = _desc((1, 4, 64, 32), ea.ATTN_F32, data=0x60000)
+    m.bias = ctypes.pointer(b)
+    assert _call(mask=m) == ea.ATTN_ERR_INVALID          # Nk mismatch
+    b2 = _desc((1, 4, 64, 64), ea.ATTN_BF16, data=0x60000)
+    m.bias = ctypes.pointer(b2)
+    assert _call(mask=m) == ea.ATTN_ERR_INVALID          # dtype
+    b3 = _desc((3, 4, 64, 64), ea.ATTN_F32, data=0x60000)
+    m.bias = ctypes.pointer(b3)
+    assert _call(mask=m) == ea.ATTN_ERR_INVALID          # batch extent neither 1 nor B
+    b4 = _desc((1, 4, 64, 64), ea.ATTN_F32, data=0x60000, stride=[0, 4096, 64, 2])
+    m.bias = ctypes.pointer(b4)
+    assert _call(mask=m) == ea.ATTN_ERR_UNSUPPORTED      # last dimension not contiguous
+    b5 = _desc((1, 4, 64, 64), ea.ATTN_F32, data=0x60002)
+    m.bias = ctypes.pointer(b5)
+    assert _call(mask=m) == ea.ATTN_ERR_UNSUPPORTED      # not 4-byte aligned
+
+
+def test_empty_problem_is_a_no_op():
+    # B == 0: nothing to compute, nothing enqueued, OK (no GPU needed)
+    s = (0, 4, 64, 64)
+    lse = _desc((0, 4, 64, 1), ea.ATTN_F32, stride=[256, 64, 1, 1])
+    assert _call(q=_desc(s), k=_desc(s), v=_desc(s), o=_desc(s), lse=lse) == ea.ATTN_OK
+    assert ea.last_error() == ""
+    s = (2, 4, 0, 64)
+    lse = _desc((2, 4, 0, 1), ea.ATTN_F32, stride=[0, 0, 1, 1])
+    assert _call(q=_desc(s), o=_desc(s), lse=lse) == ea.ATTN_OK
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        ea.attn_fwd(q, q, q)

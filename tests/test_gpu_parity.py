@@ -1,0 +1,291 @@
+"""Parity of the HIP forward (through the C ABI) with the fp64 CPU oracle.
+
+Both sides read the same seeded bytes (bf16 or f32, widened exactly to fp64
+for the oracle). Bars, written here and nowhere else:
+  * max |O_gpu - O_oracle| <= 2e-2 for bf16 O, <= 1e-5 for f32 O;
+  * max |LSE_gpu - LSE_oracle| <= 1e-3;
+  * no NaN anywhere; a -inf LSE (fully masked row) must match exactly and
+    its O row must be exactly zero.
+Small cases are compared element by element; the five full-size workloads
+are run in the launch configuration the benchmark times and checked on
+sampled rows plus properties that hold at any size.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+import exact_io_aware_06_amd as ea
+
+pytestmark = pytest.mark.gpu
+
+TOL_O = {"bf16": 2e-2, "f32": 1e-5}
+TOL_LSE = 1e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("these tests need a GPU")
+    ea.load_library()
+    yield
+
+
+def _banner(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+
+
+def _to_gpu(x):
+    return None if x is None else x.cuda()
+
+
+def run_gpu(inp, **kw):
+    o, lse = ea.attn_fwd(_to_gpu(inp["q"]), _to_gpu(inp["k"]), _to_gpu(inp["v"]),
+                         bias=_to_gpu(inp["bias"]), kv_len=_to_gpu(inp["kv_len"]),
+                         causal=inp["causal"], scale=inp["scale"], **kw)
+    torch.cuda.synchronize()
+    return o.double().cpu().numpy(), lse.double().cpu().numpy()
+
+
+def run_oracle(inp):
+    f = lambda t: None if t is None else t.double().numpy()
+    kv = None if inp["kv_len"] is None else inp["kv_len"].numpy()
+    return oracle.attention_forward(f(inp["q"]), f(inp["k"]), f(inp["v"]),
+                                    scale=inp["scale"], bias=f(inp["bias"]),
+                                    kv_len=kv, causal=inp["causal"])
+
+
+def compare(o, lse, ro, rl, dtype, what=""):
+    assert not np.isnan(o).any(), f"{what}: NaN in O"
+    assert not np.isnan(lse).any(), f"{what}: NaN in LSE"
+    dead = np.isneginf(rl)
+    assert np.array_equal(np.isneginf(lse), dead), f"{what}: -inf LSE pattern differs"
+    if dead.any():
+        assert np.all(o[dead] == 0.0), f"{what}: fully masked rows must be zero"
+    err_o = np.abs(o - ro).max() if o.size else 0.0
+    live = ~dead
+    err_l = np.abs(lse[live] - rl[live]).max() if live.any() else 0.0
+    _banner(f"{what}: max|dO|={err_o:.3e} max|dLSE|={err_l:.3e}")
+    assert err_o <= TOL_O[dtype], f"{what}: O error {err_o}"
+    assert err_l <= TOL_LSE, f"{what}: LSE error {err_l}"
+
+
+def check(w: workloads.Workload, seed=None):
+    _banner(f"{w.name} B={w.B} H={w.H} Nq={w.Nq} Nk={w.Nk} d={w.d} {w.dtype} "
+            f"causal={w.causal} seed={seed}")
+    inp = workloads.make_inputs(w, seed=seed)
+    o, lse = run_gpu(inp)
+    ro, rl = run_oracle(inp)
+    compare(o, lse, ro, rl, w.dtype, w.name)
+    return inp, o, lse
+
+
+# --------------------------------------------------------------- reduced workloads
+
+def test_config1_full_size_f32():
+    w = workloads.CONFIGS["c1_f32_single_head"]
+    check(w)
+    check(w, seed=101)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("n", [333, 512])
+def test_config2_reduced(causal, n):
+    w = workloads.small("c2_bf16_d64", B=2, H=3, Nq=n, Nk=n, causal=causal)
+    check(w)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("n", [300, 640])
+def test_config3_reduced(causal, n):
+    w = workloads.small("c3_bf16_d128", B=2, H=2, Nq=n, Nk=n, causal=causal)
+    check(w)
+
+
+def test_config4_reduced():
+    w = workloads.small("c4_bf16_d128_long_causal", H=2, Nq=1000, Nk=1000)
+    check(w)
+    check(w, seed=104)
+
+
+@pytest.mark.parametrize("n", [300, 1024])
+def test_config5_reduced(n):
+    w = workloads.small("c5_bf16_d64_bias_padded", B=4, H=2, Nq=n, Nk=n,
+                        kv_len_range=(1, n))
+    check(w)
+
+
+# --------------------------------------------------------------- edge cases
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("nq,nk", [(1, 1), (1, 200), (70, 1), (129, 65), (65, 190), (200, 77)])
+def test_unequal_and_tiny_lengths(d, dtype, causal, nq, nk):
+    # causal with Nq > Nk leaves the first Nq - Nk rows fully masked
+    w = workloads.Workload("edge", 1, 2, nq, nk, d, dtype=dtype, causal=causal, seed=7)
+    check(w)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_bias_broadcast_and_key_lengths(dtype):
+    g = torch.Generator().manual_seed(11)
+    B, H, Nq, Nk, d = 3, 4, 150, 170, 64
+    st = torch.bfloat16 if dtype == "bf16" else torch.float32
+    q = torch.randn(B, H, Nq, d, generator=g).to(st)
+    k = torch.randn(B, H, Nk, d, generator=g).to(st)
+    v = torch.randn(B, H, Nk, d, generator=g).to(st)
+    kv_len = torch.tensor([170, 0, 64], dtype=torch.int32)
+    for bshape in [(B, 1, Nq, Nk), (1, H, Nq, Nk), (B, H, Nq, Nk), (1, 1, Nq, Nk)]:
+        bias = torch.randn(*bshape, generator=g) * 2.0
+        bias[..., 5] = -math.inf      # a masked key through the bias
+        for causal in (False, True):
+            inp = {"q": q, "k": k, "v": v, "bias": bias, "kv_len": kv_len,
+                   "causal": causal, "scale": 0.125}
+            o, lse = run_gpu(inp)
+            ro, rl = run_oracle(inp)
+            compare(o, lse, ro, rl, dtype, f"bias{bshape} causal={causal}")
+            assert np.all(o[1] == 0.0) and np.all(np.isneginf(lse[1]))
+
+
+def test_no_keys_at_all():
+    q = torch.randn(2, 2, 40, 64).to(torch.bfloat16)
+    k = torch.zeros(2, 2, 0, 64, dtype=torch.bfloat16)
+    o, lse = ea.attn_fwd(q.cuda(), k.cuda(), k.cuda())
+    torch.cuda.synchronize()
+    assert torch.all(o.cpu() == 0) and torch.all(torch.isneginf(lse.cpu()))
+
+
+@pytest.mark.parametrize("hk", [1, 2])
+def test_grouped_kv_heads(hk):
+    # query head h reads key/value head h // (H / Hk)
+    g = torch.Generator().manual_seed(12)
+    B, H, N, d = 2, 4, 190, 128
+    q = torch.randn(B, H, N, d, generator=g).to(torch.bfloat16)
+    k = torch.randn(B, hk, N, d, generator=g).to(torch.bfloat16)
+    v = torch.randn(B, hk, N, d, generator=g).to(torch.bfloat16)
+    o, lse = ea.attn_fwd(q.cuda(), k.cuda(), v.cuda(), causal=True)
+    torch.cuda.synchronize()
+    rep = H // hk
+    kx = k.repeat_interleave(rep, dim=1)
+    vx = v.repeat_interleave(rep, dim=1)
+    ro, rl = oracle.attention_forward(q.double().numpy(), kx.double().numpy(),
+                                      vx.double().numpy(), scale=1 / math.sqrt(d),
+                                      causal=True)
+    compare(o.double().cpu().numpy(), lse.double().cpu().numpy(), ro, rl, "bf16",
+            f"gqa Hk={hk}")
+
+
+def test_strided_views():
+    # [B, N, H, d] storage viewed as [B, H, N, d]; output written into a view
+    g = torch.Generator().manual_seed(13)
+    B, H, N, d = 2, 3, 211, 64
+    base = torch.randn(3, B, N, H, d, generator=g).to(torch.bfloat16).cuda()
+    q, k, v = (base[i].transpose(1, 2) for i in range(3))
+    out_store = torch.empty(B, N, H, d, dtype=torch.bfloat16, device="cuda")
+    out = out_store.transpose(1, 2)
+    lse_store = torch.empty(B, H, N + 8, dtype=torch.float32, device="cuda")
+    lse = lse_store[:, :, :N]
+    ea.attn_fwd(q, k, v, causal=True, out=out, lse=lse)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention_forward(q.double().cpu().numpy(), k.double().cpu().numpy(),
+                                      v.double().cpu().numpy(), scale=1 / 8, causal=True)
+    compare(out.double().cpu().numpy(), lse.double().cpu().numpy(), ro, rl, "bf16", "strided")
+
+
+def test_large_magnitude_scores():
+    # scores near +-1e3 would overflow exp() without the running maximum
+    g = torch.Generator().manual_seed(14)
+    q = (torch.randn(1, 2, 130, 64, generator=g) * 30).to(torch.bfloat16)
+    k = (torch.randn(1, 2, 130, 64, generator=g) * 30).to(torch.bfloat16)
+    v = torch.randn(1, 2, 130, 64, generator=g).to(torch.bfloat16)
+    inp = {"q": q, "k": k, "v": v, "bias": None, "kv_len": None, "causal": False,
+           "scale": 0.125}
+    o, lse = run_gpu(inp)
+    ro, rl = run_oracle(inp)
+    assert np.abs(rl).max() > 500
+    compare(o, lse, ro, rl, "bf16", "large scores")
+
+
+def test_deterministic_bitwise():
+    w = workloads.small("c3_bf16_d128_causal", B=1, H=4, Nq=777, Nk=777)
+    inp = workloads.make_inputs(w)
+    q, k, v = (inp[x].cuda() for x in ("q", "k", "v"))
+    o1, l1 = ea.attn_fwd(q, k, v, causal=True)
+    o2, l2 = ea.attn_fwd(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_merge_of_two_key_halves_gpu():
+    # FlashAttention: Mathematical Foundations..., section 7: two GPU calls on
+    # disjoint key ranges, merged by their LSEs, reproduce the full call.
+    g = torch.Generator().manual_seed(15)
+    q = torch.randn(2, 2, 260, 128, generator=g).to(torch.bfloat16).cuda()
+    k = torch.randn(2, 2, 500, 128, generator=g).to(torch.bfloat16).cuda()
+    v = torch.randn(2, 2, 500, 128, generator=g).to(torch.bfloat16).cuda()
+    o, lse = ea.attn_fwd(q, k, v)
+    oa, la = ea.attn_fwd(q, k[:, :, :192], v[:, :, :192])
+    ob, lb = ea.attn_fwd(q, k[:, :, 192:], v[:, :, 192:])
+    torch.cuda.synchronize()
+    f = lambda t: t.double().cpu().numpy()
+    om, lm = oracle.merge_partials([(f(oa), f(la)), (f(ob), f(lb))])
+    assert np.abs(om - f(o)).max() <= 2e-2
+    assert np.abs(lm - f(lse)).max() <= 1e-3
+
+
+def test_error_status_raises():
+    q = torch.randn(1, 1, 16, 96, device="cuda").to(torch.bfloat16)
+    with pytest.raises(ea.AttnError, match="UNSUPPORTED"):
+        ea.attn_fwd(q, q, q)
+    q = torch.randn(1, 1, 16, 64, device="cuda").to(torch.bfloat16)
+    with pytest.raises(ea.AttnError, match="INVALID"):
+        ea.attn_fwd(q, q, q, scale=-1.0)
+
+
+# --------------------------------------------------------------- full-size workloads
+
+def _sample_rows(w, n_rows, seed):
+    r = np.random.default_rng(seed)
+    rows = []
+    for _ in range(n_rows):
+        rows.append((int(r.integers(w.B)), int(r.integers(w.H)), int(r.integers(w.Nq))))
+    # first and last rows of the first and last heads, and tile edges
+    for b, h in ((0, 0), (w.B - 1, w.H - 1)):
+        for i in (0, 1, 127, 128, w.Nq - 129, w.Nq - 1):
+            rows.append((b, h, max(0, min(i, w.Nq - 1))))
+    return rows
+
+
+@pytest.mark.parametrize("name", sorted(workloads.CONFIGS))
+def test_full_size_sampled(name):
+    w = workloads.CONFIGS[name]
+    _banner(f"full {name}")
+    inp = workloads.make_inputs(w)
+    q, k, v = (inp[x].cuda() for x in ("q", "k", "v"))
+    bias = _to_gpu(inp["bias"])
+    kv_len = _to_gpu(inp["kv_len"])
+    o, lse = ea.attn_fwd(q, k, v, bias=bias, kv_len=kv_len, causal=w.causal,
+                         scale=inp["scale"])
+    torch.cuda.synchronize()
+    o_c = o.cpu()
+    lse_c = lse.cpu()
+    # properties at any size: finite, and each O row inside the range of V
+    assert not torch.isnan(o_c.float()).any() and torch.isfinite(lse_c).all()
+    vmin = inp["v"].float().amin(dim=2, keepdim=True)
+    vmax = inp["v"].float().amax(dim=2, keepdim=True)
+    slack = 1e-2 * (vmax - vmin) + 1e-6
+    assert bool(((o_c.float() >= vmin - slack) & (o_c.float() <= vmax + slack)).all())
+    rows = _sample_rows(w, 48, seed=w.seed)
+    f = lambda t: None if t is None else t.double().numpy()
+    kv = None if inp["kv_len"] is None else inp["kv_len"].numpy()
+    ro, rl = oracle.attention_rows(f(inp["q"]), f(inp["k"]), f(inp["v"]), rows,
+                                   scale=inp["scale"], bias=f(inp["bias"]), kv_len=kv,
+                                   causal=w.causal)
+    go = np.stack([o_c[b, h, i].double().numpy() for b, h, i in rows])
+    gl = np.array([float(lse_c[b, h, i]) for b, h, i in rows])
+    compare(go, gl, ro, rl, w.dtype, f"full {name} sampled")
