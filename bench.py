@@ -95,6 +95,9 @@ def main(argv=None):
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a device-to-device copy of MIB mebibytes (the "
+                         "reference kernel that scales the HBM byte counters)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -105,6 +108,17 @@ def main(argv=None):
     import torch
     import workloads
     import exact_io_aware_06_amd as ea
+
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(max(args.steps, 1)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4,
+                          "launches": max(args.steps, 1)}), flush=True)
+        return 0
 
     name = args.workload or workloads.HEADLINE
     w = workloads.CONFIGS[name]

@@ -16,22 +16,32 @@
 //   * Key/value tiles of 64 keys are staged global -> registers -> LDS, double
 //     buffered: the global loads of tile j+1 are issued before tile j is
 //     computed and land in the other LDS buffer afterwards; one barrier per
-//     tile.
+//     tile. K and V are copied to LDS unchanged (row-major), 16 bytes a lane.
 //   * Scores are computed transposed, S^T = K Q^T, with
 //     v_mfma_f32_32x32x16_bf16 (A = 32 keys from LDS, B = 32 queries held in
 //     VGPRs for the whole loop). In the 32x32 accumulator layout lane l holds
 //     query l%32 and 16 of the 32 keys; the other 16 sit in lane l^32. A row
-//     maximum is therefore 31 in-lane max operations and ONE cross-lane step
+//     maximum is therefore in-lane max operations plus ONE cross-lane step
 //     (v_permlane32_swap); the row sum needs no cross-lane step until the end.
 //   * The rows of the K operand are fed in a fixed permutation (bits 2 and 3
 //     of the row index swapped) so that the accumulator registers 8t..8t+7 of
 //     every lane hold 8 consecutive keys. They are converted to bf16 in place
 //     and used directly as the B operand of O^T += V^T P^T, with no shuffle.
-//   * V is written to LDS key-interleaved: the 16-byte unit (g, c) holds
-//     V[8g..8g+7][c], which is exactly one lane's A operand of the PV MFMA.
-//     The interleave is done in registers by the loader threads.
-//   * K rows are stored in LDS in the permuted order with a 16-byte row pad so
-//     the 32 rows read by one MFMA operand fall in distinct banks.
+//   * The A operand of that product (8 consecutive keys of one V column per
+//     lane) is read from the row-major V tile with two ds_read_b64_tr_b16:
+//     within a group of 16 lanes, lane i receives element i%4 of the 8-byte
+//     chunks addressed by lanes 4e + i/4 (e = 0..3), so 16 lanes that address
+//     4 key rows x 16 columns come back holding one column of 4 keys each.
+//   * LDS rows are padded (K by 16 bytes, V by 64 bytes plus an XOR of bit 2
+//     of the 8-byte chunk index with bit 1 of the row) so that the rows one
+//     MFMA operand reads fall in distinct banks.
+//   * The running maximum is a reference point, not necessarily the exact
+//     maximum: it moves only when a row's tile maximum exceeds it by more than
+//     kTau (base-2 units), so exponentials stay <= 2^kTau and the costly
+//     rescale of the output accumulator is rare. Any reference point gives the
+//     same result in exact arithmetic ("Understanding FlashAttention Pt 1",
+//     section 2.2: the maximum is only a change of reference; the conditional
+//     rescaling of "FlashAttention, Explained", section 22).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -43,10 +53,10 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
@@ -54,17 +64,19 @@ constexpr int kBr = 32 * kWaves;  // query rows per workgroup
 constexpr int kBc = 64;           // keys per tile
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kLog2e = 1.44269504088896341f;
+constexpr float kTau = 8.0f;      // reference-maximum slack, base-2 units
+constexpr int kPf = 4;            // MFMA operands read ahead from LDS
 
 template <int D>
 struct Geo {
-  static constexpr int kRowBytes = D * 2 + 16;        // padded K row in LDS
-  static constexpr int kKBytes = kBc * kRowBytes;
-  static constexpr int kVBytes = kBc * D * 2;
+  static constexpr int kKRow = D * 2 + 16;            // padded K row in LDS (bytes)
+  static constexpr int kVRow = D * 2 + 64;            // padded V row in LDS (bytes)
+  static constexpr int kKBytes = kBc * kKRow;
+  static constexpr int kVBytes = kBc * kVRow;
   static constexpr int kStage = kKBytes + kVBytes;
   static constexpr int kSmem = 2 * kStage;
   static constexpr int kChunks = D / 8;               // 16-byte chunks per row
-  static constexpr int kKLoads = kBc * kChunks / kThreads;
-  static constexpr int kVCols = D / 32;               // V columns per loader thread
+  static constexpr int kLoads = kBc * kChunks / kThreads;  // per thread, each of K and V
   static constexpr int kNkk = D / 16;                 // k-steps of QK^T
   static constexpr int kNcb = D / 32;                 // 32-wide output column blocks
 };
@@ -85,6 +97,16 @@ __device__ __forceinline__ float lane_pair_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
                                             false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Two LDS transpose reads (4 keys each) concatenated into one MFMA operand.
+__device__ __forceinline__ bf16x8 lds_read_tr_pair(const uint8_t* p0, const uint8_t* p1) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(const_cast<uint8_t*>(p0)));
+  const s16x4 c = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(const_cast<uint8_t*>(p1)));
+  const s16x8 v = __builtin_shufflevector(a, c, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
 }
 
 __device__ __forceinline__ bool decode_tile(const TileMap& tm, int B, int H,
@@ -109,20 +131,9 @@ __device__ __forceinline__ bool decode_tile(const TileMap& tm, int B, int H,
   return true;
 }
 
-template <int D>
-struct VLoad;
-template <>
-struct VLoad<128> { typedef u32x2 type; };   // 4 columns = 8 bytes
-template <>
-struct VLoad<64> { typedef uint32_t type; }; // 2 columns = 4 bytes
-
-__device__ __forceinline__ uint32_t word_of(const u32x2& v, int i) { return v[i]; }
-__device__ __forceinline__ uint32_t word_of(const uint32_t& v, int) { return v; }
-
 template <int D, bool CAUSAL, bool HAS_BIAS>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p, TileMap tm) {
   using G = Geo<D>;
-  using VRow = typename VLoad<D>::type;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
   int b, h, qt;
@@ -173,68 +184,67 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p, Tile
       qf[kk] = bf16x8{};
   }
 
-  // ---- loader roles
-  // K: chunk c = tid + kThreads*i -> key c / kChunks, 16-byte column chunk c % kChunks
-  // V: key group g = tid / 32 (8 keys), columns [vc0, vc0 + kVCols)
-  const int vg = tid >> 5;
-  const int vc0 = (tid & 31) * G::kVCols;
-  u32x4 kreg[G::kKLoads];
-  VRow vreg[8];
-
+  // ---- loader: chunk c = tid + kThreads*i of a tile -> key c / kChunks,
+  // 16-byte column chunk c % kChunks, the same for K and V.
+  // Rows past the last key are read from the last key row instead (always a
+  // valid address, finite data): their scores are masked to -inf, so their
+  // probabilities are exactly 0 and they contribute nothing.
+  u32x4 kreg[G::kLoads];
+  u32x4 vreg[G::kLoads];
+  const int last_key = Nk - 1;
+  constexpr int kRowsPerPass = kThreads / G::kChunks;  // key rows one pass of loads covers
+  const int lr0 = tid / G::kChunks;
+  const int lch = (tid % G::kChunks) * 8;
+  const __bf16* kld = kgp + (int64_t)lr0 * p.k_sn + lch;
+  const __bf16* vld = vgp + (int64_t)lr0 * p.v_sn + lch;
   auto load_tile = [&](int j) {
     const int kv0 = j * kBc;
-    const bool full = kv0 + kBc <= Nk;
+    if (kv0 + kBc <= Nk) {
+      const __bf16* kt = kld + (int64_t)kv0 * p.k_sn;
+      const __bf16* vt = vld + (int64_t)kv0 * p.v_sn;
 #pragma unroll
-    for (int i = 0; i < G::kKLoads; ++i) {
-      const int c = tid + kThreads * i;
-      const int key = kv0 + c / G::kChunks;
-      const int ch = c % G::kChunks;
-      if (full || key < Nk)
-        kreg[i] = *reinterpret_cast<const u32x4*>(kgp + (int64_t)key * p.k_sn + ch * 8);
-      else
-        kreg[i] = u32x4{0u, 0u, 0u, 0u};
-    }
+      for (int i = 0; i < G::kLoads; ++i) {
+        kreg[i] = *reinterpret_cast<const u32x4*>(kt + (int64_t)(i * kRowsPerPass) * p.k_sn);
+        vreg[i] = *reinterpret_cast<const u32x4*>(vt + (int64_t)(i * kRowsPerPass) * p.v_sn);
+      }
+    } else {
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int key = kv0 + vg * 8 + r;
-      if (full || key < Nk)
-        vreg[r] = *reinterpret_cast<const VRow*>(vgp + (int64_t)key * p.v_sn + vc0);
-      else
-        vreg[r] = VRow{};
+      for (int i = 0; i < G::kLoads; ++i) {
+        const int key = min(kv0 + lr0 + i * kRowsPerPass, last_key);
+        kreg[i] = *reinterpret_cast<const u32x4*>(kgp + (int64_t)key * p.k_sn + lch);
+        vreg[i] = *reinterpret_cast<const u32x4*>(vgp + (int64_t)key * p.v_sn + lch);
+      }
     }
   };
-
   auto store_tile = [&](int stage) {
     uint8_t* ks = smem + stage * G::kStage;
     uint8_t* vs = ks + G::kKBytes;
 #pragma unroll
-    for (int i = 0; i < G::kKLoads; ++i) {
+    for (int i = 0; i < G::kLoads; ++i) {
       const int c = tid + kThreads * i;
       const int key = c / G::kChunks;
       const int ch = c % G::kChunks;
       const int row = (key & ~31) | perm_row(key & 31);
-      *reinterpret_cast<u32x4*>(ks + row * G::kRowBytes + ch * 16) = kreg[i];
-    }
-    // key-interleave V: unit (vg, c) = V[8vg .. 8vg+7][c]
-#pragma unroll
-    for (int cc = 0; cc < G::kVCols; ++cc) {
-      u32x4 u;
-#pragma unroll
-      for (int pp = 0; pp < 4; ++pp) {
-        const uint32_t lo = word_of(vreg[2 * pp], cc >> 1);
-        const uint32_t up = word_of(vreg[2 * pp + 1], cc >> 1);
-        u[pp] = (cc & 1) ? ((lo >> 16) | (up & 0xffff0000u))
-                         : ((lo & 0xffffu) | (up << 16));
-      }
-      *reinterpret_cast<u32x4*>(vs + (vg * D + vc0 + cc) * 16) = u;
+      *reinterpret_cast<u32x4*>(ks + row * G::kKRow + ch * 16) = kreg[i];
+      const int vch = ch ^ (((key >> 1) & 1) << 1);
+      *reinterpret_cast<u32x4*>(vs + key * G::kVRow + vch * 16) = vreg[i];
     }
   };
+
+  // ---- V^T operand addressing (per lane, fixed): in its 16-lane group, lane
+  // i reads key row 4s + i/4 (+ 8hi + block/half offsets), 8-byte chunk
+  // 8cb + 4*(l32/16) + i%4, with the chunk's bit 2 flipped on rows whose bit 1
+  // is set (that bit is (i/8)%2 here).
+  const int gi = l32 & 15;
+  const int vx = ((gi >> 3) & 1) << 2;
+  const int vlane = ((gi >> 2) + 8 * hi) * G::kVRow +
+                    (((4 * (l32 >> 4) + (gi & 3)) ^ vx) * 8);
 
   // ---- running state of this lane's query row
   f32x16 oacc[G::kNcb];
 #pragma unroll
   for (int cb = 0; cb < G::kNcb; ++cb) oacc[cb] = f32x16{};
-  float m_run = -INFINITY;  // running maximum, base-2 units
+  float m_run = -INFINITY;  // reference maximum, base-2 units
   float l_run = 0.f;        // this lane's share of the running denominator
   const float c2 = p.scale_log2;
 
@@ -285,17 +295,27 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p, Tile
           }
       }
 
-      // ---- S^T = K Q^T for two 32-key blocks
+      // ---- S^T = K Q^T for two 32-key blocks. MFMA i uses k-step i/2 of
+      // block i%2; its A operand is read kPf MFMAs ahead so LDS latency
+      // overlaps the matrix pipe instead of stalling it.
       f32x16 sacc[2] = {f32x16{}, f32x16{}};
-      const uint8_t* kbase = ks + l32 * G::kRowBytes + hi * 16;
+      const uint8_t* kbase = ks + l32 * G::kKRow + hi * 16;
+      constexpr int kNq = 2 * G::kNkk;
+      auto kfrag = [&](int i) {
+        return *reinterpret_cast<const bf16x8*>(kbase + (i & 1) * 32 * G::kKRow + (i >> 1) * 32);
+      };
+      bf16x8 kf[kPf];
 #pragma unroll
-      for (int kk = 0; kk < G::kNkk; ++kk)
+      for (int i = 0; i < kPf; ++i) kf[i] = kfrag(i);
+      // the fences keep the compiler from sinking each read next to its use
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int bb = 0; bb < 2; ++bb) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-              kbase + bb * 32 * G::kRowBytes + kk * 32);
-          sacc[bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], sacc[bb], 0, 0, 0);
-        }
+      for (int i = 0; i < kNq; ++i) {
+        sacc[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % kPf], qf[i >> 1],
+                                                              sacc[i & 1], 0, 0, 0);
+        if (i + kPf < kNq) kf[i % kPf] = kfrag(i + kPf);
+        __builtin_amdgcn_sched_barrier(0);
+      }
 
       // register r of block bb holds key kv0 + 32bb + 16(r/8) + 8hi + (r%8)
       if (HAS_BIAS) {
@@ -318,17 +338,20 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p, Tile
           }
       }
 
-      // ---- online softmax update (base 2)
+      // ---- online softmax update (base 2) against a lagging reference
       float mx = sacc[0][0];
 #pragma unroll
       for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[0][r]);
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[1][r]);
       mx = lane_pair_max(mx);
-      const float m_new = HAS_BIAS ? fmaxf(m_run, mx) : fmaxf(m_run, mx * c2);
+      const float m_tile = HAS_BIAS ? mx : mx * c2;
+      // false while nothing is visible (m_tile = -inf); true on the first
+      // visible tile (m_run = -inf)
+      const bool move = m_tile > m_run + kTau;
+      const float m_new = move ? m_tile : m_run;
       // a row with nothing visible yet keeps 0 as its reference (no -inf - -inf)
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
 
       float rs = 0.f;
 #pragma unroll
@@ -341,15 +364,17 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p, Tile
           sacc[bb][r] = e;
           rs += e;
         }
-      l_run = __builtin_fmaf(l_run, alpha, rs);
-      m_run = m_new;
-      // rescale the accumulator only if some row of this wave moved its maximum
-      if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
+      if (__builtin_amdgcn_ballot_w64(move) != 0) {
+        // alpha = 1 exactly for rows whose reference did not move
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+        l_run *= alpha;
 #pragma unroll
         for (int cb = 0; cb < G::kNcb; ++cb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) oacc[cb][r] *= alpha;
       }
+      l_run += rs;
+      m_run = m_new;
 
       // ---- P^T operands: registers 8t..8t+7 of block bb = keys 32bb+16t+8hi+[0,8)
       bf16x8 pb[2][2];
@@ -360,18 +385,26 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p, Tile
 #pragma unroll
           for (int e = 0; e < 8; ++e) pb[bb][t][e] = (__bf16)sacc[bb][8 * t + e];
 
-      // ---- O^T += V^T P^T
-      const uint8_t* vbase = vs + (hi * D + l32) * 16;
+      // ---- O^T += V^T P^T; MFMA i: column block i/4, key block (i/2)%2,
+      // half i%2; A operand rows 32bb + 16t + 8hi + 4s + [0, 4), prefetched
+      // kPf MFMAs ahead.
+      const uint8_t* vbase = vs + vlane;
+      constexpr int kNv = 4 * G::kNcb;
+      auto vfrag = [&](int i) {
+        const uint8_t* p0 = vbase + (16 * (i & 3)) * G::kVRow + 64 * (i >> 2);
+        return lds_read_tr_pair(p0, p0 + 4 * G::kVRow);
+      };
+      bf16x8 vf[kPf];
 #pragma unroll
-      for (int cb = 0; cb < G::kNcb; ++cb)
+      for (int i = 0; i < kPf; ++i) vf[i] = vfrag(i);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int bb = 0; bb < 2; ++bb)
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                vbase + ((4 * bb + 2 * t) * D + 32 * cb) * 16);
-            oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[bb][t], oacc[cb], 0, 0, 0);
-          }
+      for (int i = 0; i < kNv; ++i) {
+        oacc[i >> 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            vf[i % kPf], pb[(i >> 1) & 1][i & 1], oacc[i >> 2], 0, 0, 0);
+        if (i + kPf < kNv) vf[i % kPf] = vfrag(i + kPf);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
 
     if (j + 1 < nt) store_tile(stage ^ 1);
