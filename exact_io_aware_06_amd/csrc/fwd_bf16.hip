@@ -11,7 +11,7 @@
 // ("flash-attention", stanleyjacob.dev, Part VI).
 //
 // Work decomposition on CDNA4
-//   * One workgroup = 4 wavefronts = 128 query rows of one (batch, head);
+//   * One workgroup = 8 wavefronts = 256 query rows of one (batch, head);
 //     each wavefront owns 32 rows, so no cross-wave reduction of O is needed.
 //   * Key/value tiles of 64 keys are staged global -> registers -> LDS, double
 //     buffered: the global loads of tile j+1 are issued before tile j is
@@ -46,6 +46,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "fwd_params.h"
 
 namespace attn {
@@ -53,12 +55,13 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBr = 32 * kWaves;  // query rows per workgroup
 constexpr int kBc = 64;           // keys per tile
@@ -73,8 +76,7 @@ struct Geo {
   static constexpr int kVRow = D * 2 + 64;            // padded V row in LDS (bytes)
   static constexpr int kKBytes = kBc * kKRow;
   static constexpr int kVBytes = kBc * kVRow;
-  static constexpr int kStage = kKBytes + kVBytes;
-  static constexpr int kSmem = 2 * kStage;
+  static constexpr int kSmem = 2 * (kKBytes + kVBytes);
   static constexpr int kChunks = D / 8;               // 16-byte chunks per row
   static constexpr int kLoads = kBc * kChunks / kThreads;  // per thread, each of K and V
   static constexpr int kNkk = D / 16;                 // k-steps of QK^T
@@ -163,12 +165,6 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p, Tile
   if (CAUSAL) wg_keys = min(kend, min(q0 + kBr, Nq) + off);
   wg_keys = max(wg_keys, 0);
   const int nt = (wg_keys + kBc - 1) / kBc;
-  int wave_keys = 0;
-  if (qw0 < Nq) {
-    wave_keys = kend;
-    if (CAUSAL) wave_keys = min(kend, min(qw0 + 32, Nq) + off);
-    wave_keys = max(wave_keys, 0);
-  }
 
   // ---- Q as the B operand, resident for the whole loop: lane holds query
   // my_q, elements [16kk + 8hi, 16kk + 8hi + 8).
@@ -195,50 +191,67 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p, Tile
   constexpr int kRowsPerPass = kThreads / G::kChunks;  // key rows one pass of loads covers
   const int lr0 = tid / G::kChunks;
   const int lch = (tid % G::kChunks) * 8;
-  const __bf16* kld = kgp + (int64_t)lr0 * p.k_sn + lch;
-  const __bf16* vld = vgp + (int64_t)lr0 * p.v_sn + lch;
-  auto load_tile = [&](int j) {
+  auto load_rows = [&](const __bf16* base, int64_t sn, int j, u32x4 (&dst)[G::kLoads]) {
     const int kv0 = j * kBc;
     if (kv0 + kBc <= Nk) {
-      const __bf16* kt = kld + (int64_t)kv0 * p.k_sn;
-      const __bf16* vt = vld + (int64_t)kv0 * p.v_sn;
+      const __bf16* t = base + (int64_t)(kv0 + lr0) * sn + lch;
 #pragma unroll
-      for (int i = 0; i < G::kLoads; ++i) {
-        kreg[i] = *reinterpret_cast<const u32x4*>(kt + (int64_t)(i * kRowsPerPass) * p.k_sn);
-        vreg[i] = *reinterpret_cast<const u32x4*>(vt + (int64_t)(i * kRowsPerPass) * p.v_sn);
-      }
+      for (int i = 0; i < G::kLoads; ++i)
+        dst[i] = *reinterpret_cast<const u32x4*>(t + (int64_t)(i * kRowsPerPass) * sn);
     } else {
 #pragma unroll
       for (int i = 0; i < G::kLoads; ++i) {
         const int key = min(kv0 + lr0 + i * kRowsPerPass, last_key);
-        kreg[i] = *reinterpret_cast<const u32x4*>(kgp + (int64_t)key * p.k_sn + lch);
-        vreg[i] = *reinterpret_cast<const u32x4*>(vgp + (int64_t)key * p.v_sn + lch);
+        dst[i] = *reinterpret_cast<const u32x4*>(base + (int64_t)key * sn + lch);
       }
     }
   };
-  auto store_tile = [&](int stage) {
-    uint8_t* ks = smem + stage * G::kStage;
-    uint8_t* vs = ks + G::kKBytes;
+  // LDS: two K tiles then two V tiles; tile t lives in buffer t % 2.
+  uint8_t* const kbuf = smem;
+  uint8_t* const vbuf = smem + 2 * G::kKBytes;
+  auto store_k = [&](int buf) {
+    uint8_t* ks = kbuf + buf * G::kKBytes;
 #pragma unroll
     for (int i = 0; i < G::kLoads; ++i) {
       const int c = tid + kThreads * i;
       const int key = c / G::kChunks;
-      const int ch = c % G::kChunks;
       const int row = (key & ~31) | perm_row(key & 31);
-      *reinterpret_cast<u32x4*>(ks + row * G::kKRow + ch * 16) = kreg[i];
-      const int vch = ch ^ (((key >> 1) & 1) << 1);
+      *reinterpret_cast<u32x4*>(ks + row * G::kKRow + (c % G::kChunks) * 16) = kreg[i];
+    }
+  };
+  auto store_v = [&](int buf) {
+    uint8_t* vs = vbuf + buf * G::kVBytes;
+#pragma unroll
+    for (int i = 0; i < G::kLoads; ++i) {
+      const int c = tid + kThreads * i;
+      const int key = c / G::kChunks;
+      const int vch = (c % G::kChunks) ^ (((key >> 1) & 1) << 1);
       *reinterpret_cast<u32x4*>(vs + key * G::kVRow + vch * 16) = vreg[i];
     }
   };
 
-  // ---- V^T operand addressing (per lane, fixed): in its 16-lane group, lane
-  // i reads key row 4s + i/4 (+ 8hi + block/half offsets), 8-byte chunk
-  // 8cb + 4*(l32/16) + i%4, with the chunk's bit 2 flipped on rows whose bit 1
-  // is set (that bit is (i/8)%2 here).
+  // ---- MFMA operand addressing (per lane, fixed).
+  // K: lane reads LDS row 32bb + l32 (key perm_row of it), 16-byte chunk
+  // 2kk + hi.
+  const uint8_t* const klane = kbuf + l32 * G::kKRow + hi * 16;
+  // V^T: in its 16-lane group, lane i reads key row 4s + i/4 (+ 8hi +
+  // block/half offsets), 8-byte chunk 8cb + 4*(l32/16) + i%4, with the
+  // chunk's bit 2 flipped on rows whose bit 1 is set (that bit is (i/8)%2).
   const int gi = l32 & 15;
   const int vx = ((gi >> 3) & 1) << 2;
-  const int vlane = ((gi >> 2) + 8 * hi) * G::kVRow +
-                    (((4 * (l32 >> 4) + (gi & 3)) ^ vx) * 8);
+  const uint8_t* const vlane = vbuf + ((gi >> 2) + 8 * hi) * G::kVRow +
+                               (((4 * (l32 >> 4) + (gi & 3)) ^ vx) * 8);
+  constexpr int kNq = 2 * G::kNkk;   // MFMAs of one S^T tile
+  constexpr int kNv = 4 * G::kNcb;   // MFMAs of one O^T update
+  // MFMA i of S^T: k-step i/2 of key block i%2
+  auto kfrag = [&](const uint8_t* kb, int i) {
+    return *reinterpret_cast<const bf16x8*>(kb + (i & 1) * 32 * G::kKRow + (i >> 1) * 32);
+  };
+  // MFMA i of O^T: column block i/4, key block (i/2)%2, half i%2
+  auto vfrag = [&](const uint8_t* vb, int i) {
+    const uint8_t* p0 = vb + (16 * (i & 3)) * G::kVRow + 64 * (i >> 2);
+    return lds_read_tr_pair(p0, p0 + 4 * G::kVRow);
+  };
 
   // ---- running state of this lane's query row
   f32x16 oacc[G::kNcb];
@@ -254,161 +267,233 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p, Tile
     brow = p.bias + b * p.bias_sb + h * p.bias_sh + (int64_t)qrow * p.bias_sn + 8 * hi;
   }
 
-  if (nt > 0) {
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
-  }
-
-  for (int j = 0; j < nt; ++j) {
-    const int stage = j & 1;
-    if (j + 1 < nt) load_tile(j + 1);
-
+  // Bias and masks of tile j. Register r of block bb holds key
+  // kv0 + 32bb + 16(r/8) + 8hi + (r%8).
+  auto mask_bias = [&](int j, f32x16 (&s)[2]) {
     const int kv0 = j * kBc;
-    if (kv0 < wave_keys) {
-      const uint8_t* ks = smem + stage * G::kStage;
-      const uint8_t* vs = ks + G::kKBytes;
-
+    if (HAS_BIAS) {
       f32x16 bia[2];
-      if (HAS_BIAS) {
-        // lane's keys in block bb: kv0 + 32bb + 16s + 8hi + [0, 8), s = 0, 1
-        const bool fullb = p.bias_vec && kv0 + kBc <= Nk;
+      const bool fullb = p.bias_vec && kv0 + kBc <= Nk;
 #pragma unroll
-        for (int bb = 0; bb < 2; ++bb)
+      for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
-          for (int s = 0; s < 2; ++s) {
-            const float* src = brow + kv0 + 32 * bb + 16 * s;
-            if (fullb) {
-              const f32x4 x0 = *reinterpret_cast<const f32x4*>(src);
-              const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + 4);
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const float* src = brow + kv0 + 32 * bb + 16 * s2;
+          if (fullb) {
+            const f32x4 x0 = *reinterpret_cast<const f32x4*>(src);
+            const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + 4);
 #pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                bia[bb][8 * s + e] = x0[e];
-                bia[bb][8 * s + 4 + e] = x1[e];
-              }
-            } else {
-              const int k0 = kv0 + 32 * bb + 16 * s + 8 * hi;
-#pragma unroll
-              for (int e = 0; e < 8; ++e)
-                bia[bb][8 * s + e] = (k0 + e < Nk) ? src[e] : 0.f;
+            for (int e = 0; e < 4; ++e) {
+              bia[bb][8 * s2 + e] = x0[e];
+              bia[bb][8 * s2 + 4 + e] = x1[e];
             }
+          } else {
+            const int k0 = kv0 + 32 * bb + 16 * s2 + 8 * hi;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) bia[bb][8 * s2 + e] = (k0 + e < Nk) ? src[e] : 0.f;
           }
-      }
-
-      // ---- S^T = K Q^T for two 32-key blocks. MFMA i uses k-step i/2 of
-      // block i%2; its A operand is read kPf MFMAs ahead so LDS latency
-      // overlaps the matrix pipe instead of stalling it.
-      f32x16 sacc[2] = {f32x16{}, f32x16{}};
-      const uint8_t* kbase = ks + l32 * G::kKRow + hi * 16;
-      constexpr int kNq = 2 * G::kNkk;
-      auto kfrag = [&](int i) {
-        return *reinterpret_cast<const bf16x8*>(kbase + (i & 1) * 32 * G::kKRow + (i >> 1) * 32);
-      };
-      bf16x8 kf[kPf];
+        }
 #pragma unroll
-      for (int i = 0; i < kPf; ++i) kf[i] = kfrag(i);
-      // the fences keep the compiler from sinking each read next to its use
-      __builtin_amdgcn_sched_barrier(0);
+      for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
-      for (int i = 0; i < kNq; ++i) {
-        sacc[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % kPf], qf[i >> 1],
-                                                              sacc[i & 1], 0, 0, 0);
-        if (i + kPf < kNq) kf[i % kPf] = kfrag(i + kPf);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-
-      // register r of block bb holds key kv0 + 32bb + 16(r/8) + 8hi + (r%8)
-      if (HAS_BIAS) {
-#pragma unroll
-        for (int bb = 0; bb < 2; ++bb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            sacc[bb][r] = __builtin_fmaf(sacc[bb][r], c2, bia[bb][r] * kLog2e);
-      }
-      const bool need_mask = (kv0 + kBc > kend) || (CAUSAL && kv0 + kBc - 1 > qw0 + off);
-      if (need_mask) {
-        const int lim_c = my_q + off;  // last key this query may see (causal)
-#pragma unroll
-        for (int bb = 0; bb < 2; ++bb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kv0 + 32 * bb + 16 * (r >> 3) + 8 * hi + (r & 7);
-            const bool hide = (key >= kend) || (CAUSAL && key > lim_c);
-            if (hide) sacc[bb][r] = -INFINITY;
-          }
-      }
-
-      // ---- online softmax update (base 2) against a lagging reference
-      float mx = sacc[0][0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[0][r]);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[1][r]);
-      mx = lane_pair_max(mx);
-      const float m_tile = HAS_BIAS ? mx : mx * c2;
-      // false while nothing is visible (m_tile = -inf); true on the first
-      // visible tile (m_run = -inf)
-      const bool move = m_tile > m_run + kTau;
-      const float m_new = move ? m_tile : m_run;
-      // a row with nothing visible yet keeps 0 as its reference (no -inf - -inf)
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-
-      float rs = 0.f;
+        for (int r = 0; r < 16; ++r) s[bb][r] = __builtin_fmaf(s[bb][r], c2, bia[bb][r] * kLog2e);
+    }
+    const bool need_mask = (kv0 + kBc > kend) || (CAUSAL && kv0 + kBc - 1 > qw0 + off);
+    if (need_mask) {
+      const int lim_c = my_q + off;  // last key this query may see (causal)
 #pragma unroll
       for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float t = HAS_BIAS ? (sacc[bb][r] - m_use)
-                                   : __builtin_fmaf(sacc[bb][r], c2, -m_use);
-          const float e = __builtin_amdgcn_exp2f(t);
-          sacc[bb][r] = e;
-          rs += e;
+          const int key = kv0 + 32 * bb + 16 * (r >> 3) + 8 * hi + (r & 7);
+          const bool hide = (key >= kend) || (CAUSAL && key > lim_c);
+          if (hide) s[bb][r] = -INFINITY;
         }
-      if (__builtin_amdgcn_ballot_w64(move) != 0) {
-        // alpha = 1 exactly for rows whose reference did not move
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-        l_run *= alpha;
-#pragma unroll
-        for (int cb = 0; cb < G::kNcb; ++cb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[cb][r] *= alpha;
-      }
-      l_run += rs;
-      m_run = m_new;
+    }
+  };
 
-      // ---- P^T operands: registers 8t..8t+7 of block bb = keys 32bb+16t+8hi+[0,8)
-      bf16x8 pb[2][2];
+  // The softmax of one tile is split into slices that are placed between
+  // MFMAs of the other product, so the vector ALUs and the matrix pipe work
+  // at the same time within one wavefront. Slices are straight-line VALU
+  // code; sched_barrier fences pin each slice after its MFMA.
+  //
+  // Row-maximum slices (4 of them, one per quarter of the tile) and the
+  // reference update that follows them.
+  struct Ref {
+    float m_new, m_use;
+    bool move;
+  };
+  auto max_slice = [&](const f32x16 (&s)[2], int q, float acc) {
+    const int bb = q >> 1, r0 = (q & 1) * 8;
+    float m = fmaxf(acc, s[bb][r0]);
 #pragma unroll
-      for (int bb = 0; bb < 2; ++bb)
+    for (int r = 1; r < 8; ++r) m = fmaxf(m, s[bb][r0 + r]);
+    return m;
+  };
+  auto ref_update = [&](float mx) {
+    Ref f;
+    mx = lane_pair_max(mx);
+    const float m_tile = HAS_BIAS ? mx : mx * c2;
+    // false while nothing is visible (m_tile = -inf); true on the first
+    // visible tile (m_run = -inf)
+    f.move = m_tile > m_run + kTau;
+    f.m_new = f.move ? m_tile : m_run;
+    // a row with nothing visible yet keeps 0 as its reference (no -inf - -inf)
+    f.m_use = (f.m_new == -INFINITY) ? 0.f : f.m_new;
+    return f;
+  };
+  // Exponential slice: scores 2i and 2i+1 of the tile (block i/8, registers
+  // 2(i%8), 2(i%8)+1) -> probabilities, their sum, and one packed bf16 pair
+  // of the P^T operand (registers 8t..8t+7 of block bb = keys
+  // 32bb + 16t + 8hi + [0, 8)).
+  auto exp_slice = [&](f32x16 (&s)[2], u32x4 (&pw)[2][2], float m_use, float& rs, int i) {
+    const int bb = i >> 3, r = 2 * (i & 7);
+    float x[2];
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) pb[bb][t][e] = (__bf16)sacc[bb][8 * t + e];
+    for (int e = 0; e < 2; ++e) {
+      const float t = HAS_BIAS ? (s[bb][r + e] - m_use) : __builtin_fmaf(s[bb][r + e], c2, -m_use);
+      x[e] = __builtin_amdgcn_exp2f(t);
+      rs += x[e];
+    }
+    const bf16x2 v = {(__bf16)x[0], (__bf16)x[1]};
+    uint32_t w = __builtin_bit_cast(uint32_t, v);
+    // keep the slice here: without a use in this block the compiler sinks
+    // the exponentials down to the PV MFMAs that consume them
+    asm volatile("" : "+v"(w), "+v"(rs));
+    pw[bb][r >> 3][(r & 7) >> 1] = w;
+  };
 
-      // ---- O^T += V^T P^T; MFMA i: column block i/4, key block (i/2)%2,
-      // half i%2; A operand rows 32bb + 16t + 8hi + 4s + [0, 4), prefetched
-      // kPf MFMAs ahead.
-      const uint8_t* vbase = vs + vlane;
-      constexpr int kNv = 4 * G::kNcb;
-      auto vfrag = [&](int i) {
-        const uint8_t* p0 = vbase + (16 * (i & 3)) * G::kVRow + 64 * (i >> 2);
-        return lds_read_tr_pair(p0, p0 + 4 * G::kVRow);
-      };
-      bf16x8 vf[kPf];
+  // ---- software pipeline over key tiles (per wavefront):
+  //   phase A of iteration j: S_{j+1} = K_{j+1} Q^T on the matrix pipe,
+  //       exponentials/sums/bf16 packing of tile j on the vector ALUs;
+  //   phase B: O += V_j P_j on the matrix pipe, masks and row maximum of
+  //       tile j+1 on the vector ALUs.
+  // The LDS holds K_{j+1} and V_j during iteration j; K_{j+2} and V_{j+1}
+  // are loaded meanwhile and written to the buffers of K_j and V_{j-1},
+  // which no wave reads any more (one barrier per iteration).
+  auto phase_a = [&](auto with_qk, const uint8_t* kb, f32x16 (&sc)[2], f32x16 (&sn)[2],
+                     u32x4 (&pb)[2][2], float m_use) {
+    float rs = 0.f;
+    if constexpr (decltype(with_qk)::value) {
+      sn[0] = f32x16{};
+      sn[1] = f32x16{};
+      bf16x8 kf[kPf];
 #pragma unroll
-      for (int i = 0; i < kPf; ++i) vf[i] = vfrag(i);
+      for (int i = 0; i < kPf; ++i) kf[i] = kfrag(kb, i);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < kNv; ++i) {
-        oacc[i >> 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            vf[i % kPf], pb[(i >> 1) & 1][i & 1], oacc[i >> 2], 0, 0, 0);
-        if (i + kPf < kNv) vf[i % kPf] = vfrag(i + kPf);
+      for (int i = 0; i < kNq; ++i) {
+        sn[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % kPf], qf[i >> 1], sn[i & 1], 0, 0, 0);
+        if (i + kPf < kNq) kf[i % kPf] = kfrag(kb, i + kPf);
+#pragma unroll
+        for (int k = (16 * i) / kNq; k < (16 * (i + 1)) / kNq; ++k) exp_slice(sc, pb, m_use, rs, k);
         __builtin_amdgcn_sched_barrier(0);
       }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) exp_slice(sc, pb, m_use, rs, k);
     }
+    return rs;
+  };
+  auto phase_b = [&](auto with_max, const uint8_t* vb, const u32x4 (&pb)[2][2],
+                     const f32x16 (&sn)[2]) {
+    float mx = -INFINITY;
+    bf16x8 vf[kPf];
+#pragma unroll
+    for (int i = 0; i < kPf; ++i) vf[i] = vfrag(vb, i);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < kNv; ++i) {
+      oacc[i >> 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          vf[i % kPf], __builtin_bit_cast(bf16x8, pb[(i >> 1) & 1][i & 1]), oacc[i >> 2], 0, 0, 0);
+      if (i + kPf < kNv) vf[i % kPf] = vfrag(vb, i + kPf);
+      if constexpr (decltype(with_max)::value)
+        if (i < 4) mx = max_slice(sn, i, mx);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return mx;
+  };
+  auto qk_plain = [&](const uint8_t* kb, f32x16 (&s)[2]) {
+    s[0] = f32x16{};
+    s[1] = f32x16{};
+    bf16x8 kf[kPf];
+#pragma unroll
+    for (int i = 0; i < kPf; ++i) kf[i] = kfrag(kb, i);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < kNq; ++i) {
+      s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % kPf], qf[i >> 1], s[i & 1], 0, 0, 0);
+      if (i + kPf < kNq) kf[i % kPf] = kfrag(kb, i + kPf);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
 
-    if (j + 1 < nt) store_tile(stage ^ 1);
+  Ref ref{};  // reference update of the tile whose exponentials come next
+  // has_next (compile time): tile j+1 exists. The last tile gets its own
+  // code so the compiler cannot merge its exponentials with the pipelined
+  // ones and pull them out of the MFMA slots.
+  auto iteration = [&](auto has_next, int j, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+    constexpr bool kNext = decltype(has_next)::value;
+    const int cur = j & 1;
+    // staging registers are held for one phase only: K_{j+2} across phase A,
+    // V_{j+1} across phase B
+    if (kNext && j + 2 < nt) load_rows(kgp, p.k_sn, j + 2, kreg);
+    u32x4 pb[2][2];
+    const float rs = phase_a(has_next, klane + (cur ^ 1) * G::kKBytes, sc, sn, pb, ref.m_use);
+    if (kNext && j + 2 < nt) store_k(cur);
+    if (__builtin_amdgcn_ballot_w64(ref.move) != 0) {
+      // alpha = 1 exactly for rows whose reference did not move
+      const float alpha = __builtin_amdgcn_exp2f(m_run - ref.m_use);
+      l_run *= alpha;
+#pragma unroll
+      for (int cb = 0; cb < G::kNcb; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[cb][r] *= alpha;
+    }
+    l_run += rs;
+    m_run = ref.m_new;
+    if constexpr (kNext) {
+      load_rows(vgp, p.v_sn, j + 1, vreg);
+      mask_bias(j + 1, sn);
+    }
+    const float mx = phase_b(has_next, vlane + cur * G::kVBytes, pb, sn);
+    if constexpr (kNext) {
+      ref = ref_update(mx);
+      store_v(cur ^ 1);
+      __syncthreads();
+    }
+  };
+  using Yes = std::integral_constant<bool, true>;
+  using No = std::integral_constant<bool, false>;
+
+  f32x16 sa[2], sb[2];
+  if (nt > 0) {
+    load_rows(kgp, p.k_sn, 0, kreg);
+    load_rows(vgp, p.v_sn, 0, vreg);
+    store_k(0);
+    store_v(0);
+    if (nt > 1) {
+      load_rows(kgp, p.k_sn, 1, kreg);
+      store_k(1);
+    }
     __syncthreads();
+    qk_plain(klane, sa);
+    mask_bias(0, sa);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) mx = max_slice(sa, q, mx);
+    ref = ref_update(mx);
+    int j = 0;
+    for (; j + 2 < nt; j += 2) {
+      iteration(Yes{}, j, sa, sb);
+      iteration(Yes{}, j + 1, sb, sa);
+    }
+    if (nt - j == 2) {
+      iteration(Yes{}, j, sa, sb);
+      iteration(No{}, j + 1, sb, sa);
+    } else {
+      iteration(No{}, j, sa, sb);
+    }
   }
 
   // ---- epilogue: one division per row, O and LSE written once
