@@ -247,9 +247,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p, Tile
   auto kfrag = [&](const uint8_t* kb, int i) {
     return *reinterpret_cast<const bf16x8*>(kb + (i & 1) * 32 * G::kKRow + (i >> 1) * 32);
   };
-  // MFMA i of O^T: column block i/4, key block (i/2)%2, half i%2
+  // MFMA i of O^T: column block i % kNcb, 16-key group u = i / kNcb (key
+  // block u/2, half u%2); consecutive MFMAs update different column blocks so
+  // no MFMA waits for the previous one's result
   auto vfrag = [&](const uint8_t* vb, int i) {
-    const uint8_t* p0 = vb + (16 * (i & 3)) * G::kVRow + 64 * (i >> 2);
+    const uint8_t* p0 = vb + (16 * (i / G::kNcb)) * G::kVRow + 64 * (i % G::kNcb);
     return lds_read_tr_pair(p0, p0 + 4 * G::kVRow);
   };
 
@@ -404,11 +406,16 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p, Tile
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < kNv; ++i) {
-      oacc[i >> 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-          vf[i % kPf], __builtin_bit_cast(bf16x8, pb[(i >> 1) & 1][i & 1]), oacc[i >> 2], 0, 0, 0);
+      const int u = i / G::kNcb;
+      oacc[i % G::kNcb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          vf[i % kPf], __builtin_bit_cast(bf16x8, pb[u >> 1][u & 1]), oacc[i % G::kNcb], 0, 0, 0);
       if (i + kPf < kNv) vf[i % kPf] = vfrag(vb, i + kPf);
-      if constexpr (decltype(with_max)::value)
-        if (i < 4) mx = max_slice(sn, i, mx);
+      if constexpr (decltype(with_max)::value) {
+        if (i < 4) {
+          mx = max_slice(sn, i, mx);
+          asm volatile("" : "+v"(mx));  // keep the slice in this MFMA slot
+        }
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
     return mx;
@@ -478,6 +485,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p, Tile
     }
     __syncthreads();
     qk_plain(klane, sa);
+    // iteration 0 overwrites K buffer 0 with K_2: every wave must be done
+    // reading K_0 first
+    if (nt > 2) __syncthreads();
     mask_bias(0, sa);
     float mx = -INFINITY;
 #pragma unroll
