@@ -13,10 +13,11 @@
 // Work decomposition on CDNA4
 //   * One workgroup = 8 wavefronts = 256 query rows of one (batch, head);
 //     each wavefront owns 32 rows, so no cross-wave reduction of O is needed.
-//   * Key/value tiles of 64 keys are staged global -> registers -> LDS, double
-//     buffered: the global loads of tile j+1 are issued before tile j is
-//     computed and land in the other LDS buffer afterwards; one barrier per
-//     tile. K and V are copied to LDS unchanged (row-major), 16 bytes a lane.
+//   * Key/value tiles of 64 keys are copied global -> LDS directly
+//     (global_load_lds_dwordx4, no staging registers), double buffered: the
+//     loads of the next tiles are issued at the start of an iteration into
+//     the buffers no wave reads any more and waited for just before the one
+//     barrier that ends it.
 //   * Scores are computed transposed, S^T = K Q^T, with
 //     v_mfma_f32_32x32x16_bf16 (A = 32 keys from LDS, B = 32 queries held in
 //     VGPRs for the whole loop). In the 32x32 accumulator layout lane l holds
@@ -32,9 +33,10 @@
 //     within a group of 16 lanes, lane i receives element i%4 of the 8-byte
 //     chunks addressed by lanes 4e + i/4 (e = 0..3), so 16 lanes that address
 //     4 key rows x 16 columns come back holding one column of 4 keys each.
-//   * LDS rows are padded (K by 16 bytes, V by 64 bytes plus an XOR of bit 2
-//     of the 8-byte chunk index with bit 1 of the row) so that the rows one
-//     MFMA operand reads fall in distinct banks.
+//   * In LDS, K rows are interleaved in blocks of 16 (16-byte chunk c of row
+//     r at slot 16c + r) and V rows in blocks of 4 (slot 4c + r), so the rows
+//     one MFMA operand reads fall in distinct banks while every read address
+//     is a per-lane base plus an immediate offset.
 //   * The running maximum is a reference point, not necessarily the exact
 //     maximum: it moves only when a row's tile maximum exceeds it by more than
 //     kTau (base-2 units), so exponentials stay <= 2^kTau and the costly
@@ -72,13 +74,14 @@ constexpr int kPf = 4;            // MFMA operands read ahead from LDS
 
 template <int D>
 struct Geo {
-  static constexpr int kKRow = D * 2 + 16;            // padded K row in LDS (bytes)
-  static constexpr int kVRow = D * 2 + 64;            // padded V row in LDS (bytes)
-  static constexpr int kKBytes = kBc * kKRow;
-  static constexpr int kVBytes = kBc * kVRow;
-  static constexpr int kSmem = 2 * (kKBytes + kVBytes);
   static constexpr int kChunks = D / 8;               // 16-byte chunks per row
-  static constexpr int kLoads = kBc * kChunks / kThreads;  // per thread, each of K and V
+  static constexpr int kKBlock = 16 * kChunks * 16;   // 16 K rows, chunk-interleaved
+  static constexpr int kVBlock = 4 * kChunks * 16;    // 4 V rows, chunk-interleaved
+  static constexpr int kKBytes = kBc * D * 2;
+  static constexpr int kVBytes = kBc * D * 2;
+  static constexpr int kSmem = 2 * (kKBytes + kVBytes);
+  static constexpr int kDma = kKBytes / 1024;         // 1 KB DMA instructions per tile (K or V)
+  static constexpr int kDmaPerWave = kDma / kWaves;
   static constexpr int kNkk = D / 16;                 // k-steps of QK^T
   static constexpr int kNcb = D / 32;                 // 32-wide output column blocks
 };
@@ -109,6 +112,13 @@ __device__ __forceinline__ bf16x8 lds_read_tr_pair(const uint8_t* p0, const uint
   const s16x4 c = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(const_cast<uint8_t*>(p1)));
   const s16x8 v = __builtin_shufflevector(a, c, 0, 1, 2, 3, 4, 5, 6, 7);
   return __builtin_bit_cast(bf16x8, v);
+}
+
+// 16 bytes from global memory straight into LDS at lds_base + 16 * lane
+// (lds_base must be the same for the whole wavefront).
+__device__ __forceinline__ void dma16(const void* src, uint8_t* lds_base) {
+  typedef __attribute__((address_space(3))) void lds_void;
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_base, 16, 0, 0);
 }
 
 __device__ __forceinline__ bool decode_tile(const TileMap& tm, int B, int H,
@@ -180,79 +190,68 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p, Tile
       qf[kk] = bf16x8{};
   }
 
-  // ---- loader: chunk c = tid + kThreads*i of a tile -> key c / kChunks,
-  // 16-byte column chunk c % kChunks, the same for K and V.
+  // ---- tile loads: global memory -> LDS directly (global_load_lds_dwordx4),
+  // no registers involved. One such instruction writes 1 KB of LDS, lane l
+  // at byte 16l; which global 16 bytes a lane fetches is free, so the LDS
+  // layouts below are produced by choosing each lane's source address.
+  //   K tile: blocks of 16 rows; inside a block, 16-byte slot
+  //     (chunk * 16 + row % 16). LDS row R holds key perm_row(R) (low 5 bits).
+  //   V tile: blocks of 4 rows; inside a block, slot (chunk * 4 + row % 4).
+  // DMA instruction n (0 <= n < kDma) of a tile is issued by wave n % kWaves.
   // Rows past the last key are read from the last key row instead (always a
   // valid address, finite data): their scores are masked to -inf, so their
   // probabilities are exactly 0 and they contribute nothing.
-  u32x4 kreg[G::kLoads];
-  u32x4 vreg[G::kLoads];
+  int kkey[G::kDmaPerWave], kcol[G::kDmaPerWave], vkey[G::kDmaPerWave], vcol[G::kDmaPerWave];
+#pragma unroll
+  for (int i = 0; i < G::kDmaPerWave; ++i) {
+    const int a = 1024 * (wave + kWaves * i) + 16 * lane;   // LDS byte offset in the tile
+    const int ks = (a % G::kKBlock) / 16;
+    kkey[i] = perm_row(16 * (a / G::kKBlock) + ks % 16);
+    kcol[i] = 8 * (ks / 16);
+    const int vs = (a % G::kVBlock) / 16;
+    vkey[i] = 4 * (a / G::kVBlock) + vs % 4;
+    vcol[i] = 8 * (vs / 4);
+  }
   const int last_key = Nk - 1;
-  constexpr int kRowsPerPass = kThreads / G::kChunks;  // key rows one pass of loads covers
-  const int lr0 = tid / G::kChunks;
-  const int lch = (tid % G::kChunks) * 8;
-  auto load_rows = [&](const __bf16* base, int64_t sn, int j, u32x4 (&dst)[G::kLoads]) {
+  uint8_t* const kbuf = smem;                  // K tile t in buffer t % 2
+  uint8_t* const vbuf = smem + 2 * G::kKBytes; // V tile t in buffer t % 2
+  auto dma_tile = [&](const __bf16* base, int64_t sn, const int (&key)[G::kDmaPerWave],
+                      const int (&col)[G::kDmaPerWave], int j, uint8_t* dst) {
     const int kv0 = j * kBc;
-    if (kv0 + kBc <= Nk) {
-      const __bf16* t = base + (int64_t)(kv0 + lr0) * sn + lch;
+    const bool full = kv0 + kBc <= Nk;
 #pragma unroll
-      for (int i = 0; i < G::kLoads; ++i)
-        dst[i] = *reinterpret_cast<const u32x4*>(t + (int64_t)(i * kRowsPerPass) * sn);
-    } else {
-#pragma unroll
-      for (int i = 0; i < G::kLoads; ++i) {
-        const int key = min(kv0 + lr0 + i * kRowsPerPass, last_key);
-        dst[i] = *reinterpret_cast<const u32x4*>(base + (int64_t)key * sn + lch);
-      }
+    for (int i = 0; i < G::kDmaPerWave; ++i) {
+      const int k = full ? kv0 + key[i] : min(kv0 + key[i], last_key);
+      dma16(base + (int64_t)k * sn + col[i], dst + 1024 * (wave + kWaves * i));
     }
   };
-  // LDS: two K tiles then two V tiles; tile t lives in buffer t % 2.
-  uint8_t* const kbuf = smem;
-  uint8_t* const vbuf = smem + 2 * G::kKBytes;
-  auto store_k = [&](int buf) {
-    uint8_t* ks = kbuf + buf * G::kKBytes;
-#pragma unroll
-    for (int i = 0; i < G::kLoads; ++i) {
-      const int c = tid + kThreads * i;
-      const int key = c / G::kChunks;
-      const int row = (key & ~31) | perm_row(key & 31);
-      *reinterpret_cast<u32x4*>(ks + row * G::kKRow + (c % G::kChunks) * 16) = kreg[i];
-    }
-  };
-  auto store_v = [&](int buf) {
-    uint8_t* vs = vbuf + buf * G::kVBytes;
-#pragma unroll
-    for (int i = 0; i < G::kLoads; ++i) {
-      const int c = tid + kThreads * i;
-      const int key = c / G::kChunks;
-      const int vch = (c % G::kChunks) ^ (((key >> 1) & 1) << 1);
-      *reinterpret_cast<u32x4*>(vs + key * G::kVRow + vch * 16) = vreg[i];
-    }
-  };
+  auto load_k = [&](int j) { dma_tile(kgp, p.k_sn, kkey, kcol, j, kbuf + (j & 1) * G::kKBytes); };
+  auto load_v = [&](int j) { dma_tile(vgp, p.v_sn, vkey, vcol, j, vbuf + (j & 1) * G::kVBytes); };
+  // the DMA writes count as outstanding vector-memory loads
+  auto wait_tiles = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
   // ---- MFMA operand addressing (per lane, fixed).
-  // K: lane reads LDS row 32bb + l32 (key perm_row of it), 16-byte chunk
-  // 2kk + hi.
-  const uint8_t* const klane = kbuf + l32 * G::kKRow + hi * 16;
+  // K: lane reads row 32bb + l32, 16-byte chunk 2kk + hi:
+  //   32bb*... + (l32/16) * kKBlock + (2kk + hi) * 256 + (l32 % 16) * 16.
+  const uint8_t* const klane = kbuf + (l32 >> 4) * G::kKBlock + hi * 256 + (l32 & 15) * 16;
   // V^T: in its 16-lane group, lane i reads key row 4s + i/4 (+ 8hi +
-  // block/half offsets), 8-byte chunk 8cb + 4*(l32/16) + i%4, with the
-  // chunk's bit 2 flipped on rows whose bit 1 is set (that bit is (i/8)%2).
+  // block/half offsets), 8-byte chunk 8cb + 4*(l32/16) + i%4, i.e. 16-byte
+  // chunk 4cb + 2*(l32/16) + (i/2)%2, half i%2, in 4-row block row/4.
   const int gi = l32 & 15;
-  const int vx = ((gi >> 3) & 1) << 2;
-  const uint8_t* const vlane = vbuf + ((gi >> 2) + 8 * hi) * G::kVRow +
-                               (((4 * (l32 >> 4) + (gi & 3)) ^ vx) * 8);
+  const uint8_t* const vlane = vbuf + 2 * hi * G::kVBlock + 128 * (l32 >> 4) +
+                               64 * ((gi >> 1) & 1) + 16 * (gi >> 2) + 8 * (gi & 1);
   constexpr int kNq = 2 * G::kNkk;   // MFMAs of one S^T tile
   constexpr int kNv = 4 * G::kNcb;   // MFMAs of one O^T update
   // MFMA i of S^T: k-step i/2 of key block i%2
   auto kfrag = [&](const uint8_t* kb, int i) {
-    return *reinterpret_cast<const bf16x8*>(kb + (i & 1) * 32 * G::kKRow + (i >> 1) * 32);
+    return *reinterpret_cast<const bf16x8*>(kb + (i & 1) * 2 * G::kKBlock + (i >> 1) * 512);
   };
   // MFMA i of O^T: column block i % kNcb, 16-key group u = i / kNcb (key
-  // block u/2, half u%2); consecutive MFMAs update different column blocks so
-  // no MFMA waits for the previous one's result
+  // block u/2, half u%2; rows 16u + 8hi + 4s + [0, 4)); consecutive MFMAs
+  // update different column blocks so no MFMA waits for the previous one
   auto vfrag = [&](const uint8_t* vb, int i) {
-    const uint8_t* p0 = vb + (16 * (i / G::kNcb)) * G::kVRow + 64 * (i % G::kNcb);
-    return lds_read_tr_pair(p0, p0 + 4 * G::kVRow);
+    const uint8_t* p0 = vb + 4 * (i / G::kNcb) * G::kVBlock + 256 * (i % G::kNcb);
+    return lds_read_tr_pair(p0, p0 + G::kVBlock);
   };
 
   // ---- running state of this lane's query row
@@ -442,12 +441,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p, Tile
   auto iteration = [&](auto has_next, int j, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
     constexpr bool kNext = decltype(has_next)::value;
     const int cur = j & 1;
-    // staging registers are held for one phase only: K_{j+2} across phase A,
-    // V_{j+1} across phase B
-    if (kNext && j + 2 < nt) load_rows(kgp, p.k_sn, j + 2, kreg);
+    // K_{j+2} and V_{j+1} go straight into the buffers of K_j and V_{j-1}
+    if (kNext && j + 2 < nt) load_k(j + 2);
+    if constexpr (kNext) load_v(j + 1);
     u32x4 pb[2][2];
     const float rs = phase_a(has_next, klane + (cur ^ 1) * G::kKBytes, sc, sn, pb, ref.m_use);
-    if (kNext && j + 2 < nt) store_k(cur);
     if (__builtin_amdgcn_ballot_w64(ref.move) != 0) {
       // alpha = 1 exactly for rows whose reference did not move
       const float alpha = __builtin_amdgcn_exp2f(m_run - ref.m_use);
@@ -459,14 +457,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p, Tile
     }
     l_run += rs;
     m_run = ref.m_new;
-    if constexpr (kNext) {
-      load_rows(vgp, p.v_sn, j + 1, vreg);
-      mask_bias(j + 1, sn);
-    }
+    if constexpr (kNext) mask_bias(j + 1, sn);
     const float mx = phase_b(has_next, vlane + cur * G::kVBytes, pb, sn);
     if constexpr (kNext) {
       ref = ref_update(mx);
-      store_v(cur ^ 1);
+      wait_tiles();
       __syncthreads();
     }
   };
@@ -475,14 +470,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p, Tile
 
   f32x16 sa[2], sb[2];
   if (nt > 0) {
-    load_rows(kgp, p.k_sn, 0, kreg);
-    load_rows(vgp, p.v_sn, 0, vreg);
-    store_k(0);
-    store_v(0);
-    if (nt > 1) {
-      load_rows(kgp, p.k_sn, 1, kreg);
-      store_k(1);
-    }
+    load_k(0);
+    load_v(0);
+    if (nt > 1) load_k(1);
+    wait_tiles();
     __syncthreads();
     qk_plain(klane, sa);
     // iteration 0 overwrites K buffer 0 with K_2: every wave must be done

@@ -185,3 +185,12 @@ def test_python_binding_refuses_cpu_tensors():
     q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU"):
         ea.attn_fwd(q, q, q)
+
+
+def test_no_undefined_kernel_symbols():
+    # hipcc can silently drop a kernel's host stub (leaving an undefined
+    # symbol that only fails when the library is loaded on the GPU machine)
+    out = subprocess.run(["nm", "-D", "--undefined-only", ea.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    missing = [ln for ln in out.splitlines() if "attn" in ln]
+    assert not missing, missing
