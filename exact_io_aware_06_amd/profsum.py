@@ -1,0 +1,122 @@
+"""Turn rocprofv3 CSV output into the short text summaries kept under profiles/.
+
+    python -m exact_io_aware_06_amd.profsum stats  <kernel_stats.csv> <out.txt> <command...>
+    python -m exact_io_aware_06_amd.profsum counters <workload> <out.txt> <pmc_dir>... -- <command...>
+    python -m exact_io_aware_06_amd.profsum traffic <workload> <fetch_dir> <write_dir> \
+        <copy_fetch_dir> <copy_write_dir> <copy_mib> <kernel_src> <out.txt> <command...>
+
+`stats` copies the per-kernel duration table. `counters` averages the SQ/GRBM
+counters of the attention kernel over its dispatches and derives MFMA busy
+fraction (per SIMD, from SQ_VALU_MFMA_BUSY_CYCLES over 1024 SIMDs and the
+per-XCD GRBM_GUI_ACTIVE), instruction mix per 256x64 wave tile and the LDS bank
+conflict rate. `traffic` turns FETCH_SIZE and
+WRITE_SIZE (KiB per dispatch, from two separate --pmc runs) into HBM bytes per
+launch, each scaled by what the same counter reads for a device-to-device copy
+of known size (bench.py --copy-calibration), and records the sha256 of the
+kernel source so that bench.py reports the figure only while the kernel is
+unchanged.
+"""
+
+import csv
+import hashlib
+import os
+import sys
+
+
+def _counter(d, name, kernel_substr):
+    path = os.path.join(d, "pmc_counter_collection.csv")
+    per = {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != name or kernel_substr not in r["Kernel_Name"]:
+            continue
+        key = int(r["Dispatch_Id"])
+        per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    if not per:
+        raise SystemExit(f"no {name} rows for {kernel_substr!r} in {path}")
+    vals = [per[k] for k in sorted(per)]
+    return sum(vals) / len(vals), len(vals)
+
+
+def stats(src, out, cmd):
+    rows = list(csv.DictReader(open(src)))
+    with open(out, "w") as f:
+        f.write(f"# rocprofv3 --kernel-trace --stats summary\n# command: {cmd}\n")
+        f.write("kernel | calls | avg_us | min_us | max_us | pct\n")
+        for r in rows:
+            f.write(f"{r['Name']} | {r['Calls']} | {float(r['AverageNs'])/1e3:.1f} | "
+                    f"{float(r['MinNs'])/1e3:.1f} | {float(r['MaxNs'])/1e3:.1f} | "
+                    f"{float(r['Percentage']):.2f}\n")
+
+
+def counters(workload, out, dirs, cmd):
+    acc = {}
+    for d in dirs:
+        path = os.path.join(d, "pmc_counter_collection.csv")
+        per = {}
+        for r in csv.DictReader(open(path)):
+            if "attn" not in r["Kernel_Name"]:
+                continue
+            key = (r["Counter_Name"], int(r["Dispatch_Id"]))
+            per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+        names = {}
+        for (n, _), v in per.items():
+            names.setdefault(n, []).append(v)
+        for n, vs in names.items():
+            acc.setdefault(n, []).append(sum(vs) / len(vs))
+    c = {n: sum(v) / len(v) for n, v in acc.items()}
+    lines = [f"# rocprofv3 --pmc counters of the attention kernel, workload {workload}",
+             f"# command (one run per counter group): {cmd}",
+             "counter | mean per dispatch"]
+    lines += [f"{n} | {c[n]:.1f}" for n in sorted(c)]
+    if "SQ_INSTS_MFMA" in c and "GRBM_GUI_ACTIVE" in c:
+        mf = c["SQ_INSTS_MFMA"]
+        gui = c["GRBM_GUI_ACTIVE"] / 8.0
+        lines.append("# derived")
+        lines.append(f"mfma_busy_fraction_per_simd | {c['SQ_VALU_MFMA_BUSY_CYCLES'] / 1024 / gui:.3f}")
+        lines.append(f"mfma_coexec_over_busy | {c['SQ_VALU_MFMA_COEXEC_CYCLES'] / c['SQ_VALU_MFMA_BUSY_CYCLES']:.3f}")
+        lines.append(f"lds_bank_conflict_over_idx_active | {c['SQ_LDS_BANK_CONFLICT'] / max(c['SQ_LDS_IDX_ACTIVE'], 1):.4f}")
+        if "SQ_INSTS_VALU" in c:
+            wt = mf / 32.0   # 32 MFMA instructions per wave per 64-key tile at d=128
+            lines.append(f"valu_non_mfma_per_wave_tile | {(c['SQ_INSTS_VALU'] - mf) / wt:.1f}")
+            lines.append(f"lds_insts_per_wave_tile | {c['SQ_INSTS_LDS'] / wt:.1f}")
+            lines.append(f"transcendental_per_wave_tile | {c['SQ_INSTS_VALU_TRANS_F32'] / wt:.1f}")
+    open(out, "w").write("\n".join(lines) + "\n")
+
+
+def traffic(workload, fdir, wdir, cfdir, cwdir, copy_mib, src, out, cmd):
+    fetch, nf = _counter(fdir, "FETCH_SIZE", "attn")
+    write, nw = _counter(wdir, "WRITE_SIZE", "attn")
+    cfetch, _ = _counter(cfdir, "FETCH_SIZE", "copyBuffer")
+    cwrite, _ = _counter(cwdir, "WRITE_SIZE", "copyBuffer")
+    copy_kib = float(copy_mib) * 1024.0
+    kf, kw = copy_kib / cfetch, copy_kib / cwrite
+    hbm = fetch * kf * 1024 + write * kw * 1024
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    with open(out, "w") as f:
+        f.write(f"# HBM traffic of the attention kernel, workload {workload}\n")
+        f.write(f"# command: {cmd}\n")
+        f.write(f"# counters: FETCH_SIZE and WRITE_SIZE in separate rocprofv3 --pmc runs "
+                f"({nf} and {nw} dispatches averaged)\n")
+        f.write(f"# calibration: a {copy_mib} MiB device-to-device copy reads FETCH_SIZE "
+                f"{cfetch:.0f} KiB and WRITE_SIZE {cwrite:.0f} KiB\n")
+        f.write(f"fetch_kib_per_dispatch: {fetch:.1f}\n")
+        f.write(f"write_kib_per_dispatch: {write:.1f}\n")
+        f.write(f"fetch_scale: {kf:.4f}\n")
+        f.write(f"write_scale: {kw:.4f}\n")
+        f.write(f"hbm_bytes_per_launch: {hbm:.0f}\n")
+        f.write(f"kernel_source: {os.path.relpath(src)}\n")
+        f.write(f"source_sha256: {sha}\n")
+
+
+if __name__ == "__main__":
+    mode = sys.argv[1]
+    if mode == "stats":
+        stats(sys.argv[2], sys.argv[3], " ".join(sys.argv[4:]))
+    elif mode == "counters":
+        rest = sys.argv[4:]
+        cut = rest.index("--")
+        counters(sys.argv[2], sys.argv[3], rest[:cut], " ".join(rest[cut + 1:]))
+    elif mode == "traffic":
+        traffic(*sys.argv[2:10], " ".join(sys.argv[10:]))
+    else:
+        raise SystemExit(__doc__)
