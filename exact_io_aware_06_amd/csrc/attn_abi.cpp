@@ -136,6 +136,12 @@ attn_status_t attn_fwd(const attn_tensor_t* q, const attn_tensor_t* k, const att
   if (Nk > 0) {
     if ((s = check_rows("k", k)) != ATTN_OK) return s;
     if ((s = check_rows("v", v)) != ATTN_OK) return s;
+    // the kernels address the rows of one 64-key tile with 32-bit byte offsets
+    const int64_t eb = dt == ATTN_BF16 ? 2 : 4;
+    for (const attn_tensor_t* t : {k, v})
+      if (Nk > 1 && 64 * t->stride[2] * eb >= (int64_t(1) << 31))
+        return fail(ATTN_ERR_UNSUPPORTED, "%s: row stride %lld elements is too large (64 rows must span < 2 GiB)",
+                    t == k ? "k" : "v", (long long)t->stride[2]);
   }
   if (lse->data == nullptr || (reinterpret_cast<uintptr_t>(lse->data) & 3u) != 0)
     return fail(ATTN_ERR_UNSUPPORTED, "lse: data pointer is NULL or not 4-byte aligned");

@@ -71,6 +71,10 @@ constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kLog2e = 1.44269504088896341f;
 constexpr float kTau = 8.0f;      // reference-maximum slack, base-2 units
 constexpr int kPf = 4;            // MFMA operands read ahead from LDS
+// Exponential slices (of 16 per tile) computed beside the O^T MFMAs instead
+// of the S^T ones, to balance vector work between the two halves of a tile.
+constexpr int kExpB = 8;
+static_assert(kExpB % 2 == 0 && kExpB <= 8, "slices of a 16-key group must precede its MFMA");
 
 template <int D>
 struct Geo {
@@ -114,11 +118,16 @@ __device__ __forceinline__ bf16x8 lds_read_tr_pair(const uint8_t* p0, const uint
   return __builtin_bit_cast(bf16x8, v);
 }
 
-// 16 bytes from global memory straight into LDS at lds_base + 16 * lane
-// (lds_base must be the same for the whole wavefront).
-__device__ __forceinline__ void dma16(const void* src, uint8_t* lds_base) {
-  typedef __attribute__((address_space(3))) void lds_void;
-  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_base, 16, 0, 0);
+// 16 bytes from global memory (tile + off) straight into LDS at
+// lds_base + 16 * lane. tile and lds_base are uniform. Written as inline asm
+// so that the compiler does not treat every later LDS read as a possible
+// alias of the copy and wait for it (vmcnt(0)), nor drain the LDS read queue
+// (lgkmcnt(0)) after issuing it: the kernel orders the copies itself with
+// s_waitcnt vmcnt and a barrier before any wave reads the buffer.
+__device__ __forceinline__ void dma16(const uint8_t* tile, uint32_t off, uint8_t* lds_base) {
+  typedef __attribute__((address_space(3))) uint8_t lds_u8;
+  const uint32_t lds = (uint32_t)(uintptr_t)(lds_u8*)lds_base;
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(tile), "{m0}"(lds));
 }
 
 __device__ __forceinline__ bool decode_tile(const TileMap& tm, int B, int H,
@@ -153,7 +162,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p, Tile
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: kept in SGPRs
   const int l32 = lane & 31;
   const int hi = lane >> 5;
   const int hk = h / p.head_group;
@@ -201,32 +210,58 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p, Tile
   // Rows past the last key are read from the last key row instead (always a
   // valid address, finite data): their scores are masked to -inf, so their
   // probabilities are exactly 0 and they contribute nothing.
+  // Each lane's source offset inside a full tile is fixed: a 32-bit byte
+  // offset added to the tile's base address, which is uniform (SGPRs).
   int kkey[G::kDmaPerWave], kcol[G::kDmaPerWave], vkey[G::kDmaPerWave], vcol[G::kDmaPerWave];
+  uint32_t koff[G::kDmaPerWave], voff[G::kDmaPerWave];
+  const int64_t ksn = p.k_sn * 2, vsn = p.v_sn * 2;   // row strides in bytes
 #pragma unroll
   for (int i = 0; i < G::kDmaPerWave; ++i) {
     const int a = 1024 * (wave + kWaves * i) + 16 * lane;   // LDS byte offset in the tile
     const int ks = (a % G::kKBlock) / 16;
     kkey[i] = perm_row(16 * (a / G::kKBlock) + ks % 16);
-    kcol[i] = 8 * (ks / 16);
+    kcol[i] = 16 * (ks / 16);
     const int vs = (a % G::kVBlock) / 16;
     vkey[i] = 4 * (a / G::kVBlock) + vs % 4;
-    vcol[i] = 8 * (vs / 4);
+    vcol[i] = 16 * (vs / 4);
+    koff[i] = (uint32_t)(kkey[i] * (int)ksn + kcol[i]);
+    voff[i] = (uint32_t)(vkey[i] * (int)vsn + vcol[i]);
   }
   const int last_key = Nk - 1;
   uint8_t* const kbuf = smem;                  // K tile t in buffer t % 2
   uint8_t* const vbuf = smem + 2 * G::kKBytes; // V tile t in buffer t % 2
-  auto dma_tile = [&](const __bf16* base, int64_t sn, const int (&key)[G::kDmaPerWave],
-                      const int (&col)[G::kDmaPerWave], int j, uint8_t* dst) {
+  const uint8_t* const kbase = reinterpret_cast<const uint8_t*>(kgp);
+  const uint8_t* const vbase = reinterpret_cast<const uint8_t*>(vgp);
+  // Base address of key tile j (uniform). A tile that runs past the last key
+  // is the last tile of its kind ever loaded, so its clamped offsets simply
+  // replace the fixed ones.
+  auto prep = [&](const uint8_t* base, int64_t sn, uint32_t (&off)[G::kDmaPerWave],
+                  const int (&key)[G::kDmaPerWave], const int (&col)[G::kDmaPerWave], int j) {
     const int kv0 = j * kBc;
-    const bool full = kv0 + kBc <= Nk;
+    if (kv0 + kBc > Nk) {
 #pragma unroll
-    for (int i = 0; i < G::kDmaPerWave; ++i) {
-      const int k = full ? kv0 + key[i] : min(kv0 + key[i], last_key);
-      dma16(base + (int64_t)k * sn + col[i], dst + 1024 * (wave + kWaves * i));
+      for (int i = 0; i < G::kDmaPerWave; ++i)
+        off[i] = (uint32_t)(min(key[i], last_key - kv0) * (int)sn + col[i]);
     }
+    return base + kv0 * sn;
   };
-  auto load_k = [&](int j) { dma_tile(kgp, p.k_sn, kkey, kcol, j, kbuf + (j & 1) * G::kKBytes); };
-  auto load_v = [&](int j) { dma_tile(vgp, p.v_sn, vkey, vcol, j, vbuf + (j & 1) * G::kVBytes); };
+  // DMA instruction i of this wave for a K (V) tile at `tile` into buffer `dst`
+  auto dma_k = [&](const uint8_t* tile, uint8_t* dst, int i) {
+    dma16(tile, koff[i], dst + 1024 * (wave + kWaves * i));
+  };
+  auto dma_v = [&](const uint8_t* tile, uint8_t* dst, int i) {
+    dma16(tile, voff[i], dst + 1024 * (wave + kWaves * i));
+  };
+  auto load_k = [&](int j) {
+    const uint8_t* t = prep(kbase, ksn, koff, kkey, kcol, j);
+#pragma unroll
+    for (int i = 0; i < G::kDmaPerWave; ++i) dma_k(t, kbuf + (j & 1) * G::kKBytes, i);
+  };
+  auto load_v = [&](int j) {
+    const uint8_t* t = prep(vbase, vsn, voff, vkey, vcol, j);
+#pragma unroll
+    for (int i = 0; i < G::kDmaPerWave; ++i) dma_v(t, vbuf + (j & 1) * G::kVBytes, i);
+  };
   // the DMA writes count as outstanding vector-memory loads
   auto wait_tiles = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
@@ -347,7 +382,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p, Tile
   // 2(i%8), 2(i%8)+1) -> probabilities, their sum, and one packed bf16 pair
   // of the P^T operand (registers 8t..8t+7 of block bb = keys
   // 32bb + 16t + 8hi + [0, 8)).
-  auto exp_slice = [&](f32x16 (&s)[2], u32x4 (&pw)[2][2], float m_use, float& rs, int i) {
+  auto exp_slice = [&](const f32x16 (&s)[2], u32x4 (&pw)[2][2], float m_use, float& rs, int i) {
     const int bb = i >> 3, r = 2 * (i & 7);
     float x[2];
 #pragma unroll
@@ -372,8 +407,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p, Tile
   // The LDS holds K_{j+1} and V_j during iteration j; K_{j+2} and V_{j+1}
   // are loaded meanwhile and written to the buffers of K_j and V_{j-1},
   // which no wave reads any more (one barrier per iteration).
-  auto phase_a = [&](auto with_qk, const uint8_t* kb, f32x16 (&sc)[2], f32x16 (&sn)[2],
-                     u32x4 (&pb)[2][2], float m_use) {
+  constexpr int kExpA = 16 - kExpB;
+  constexpr int kNdma = 2 * G::kDmaPerWave;  // K then V DMA instructions per wave and tile
+  auto phase_a = [&](auto with_qk, const uint8_t* kb, const f32x16 (&sc)[2], f32x16 (&sn)[2],
+                     u32x4 (&pb)[2][2], float m_use, auto&& dma) {
     float rs = 0.f;
     if constexpr (decltype(with_qk)::value) {
       sn[0] = f32x16{};
@@ -386,18 +423,22 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p, Tile
       for (int i = 0; i < kNq; ++i) {
         sn[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % kPf], qf[i >> 1], sn[i & 1], 0, 0, 0);
         if (i + kPf < kNq) kf[i % kPf] = kfrag(kb, i + kPf);
+        dma(i);
 #pragma unroll
-        for (int k = (16 * i) / kNq; k < (16 * (i + 1)) / kNq; ++k) exp_slice(sc, pb, m_use, rs, k);
+        for (int k = (kExpA * i) / kNq; k < (kExpA * (i + 1)) / kNq; ++k) exp_slice(sc, pb, m_use, rs, k);
         __builtin_amdgcn_sched_barrier(0);
       }
     } else {
 #pragma unroll
-      for (int k = 0; k < 16; ++k) exp_slice(sc, pb, m_use, rs, k);
+      for (int k = 0; k < kExpA; ++k) exp_slice(sc, pb, m_use, rs, k);
     }
     return rs;
   };
-  auto phase_b = [&](auto with_max, const uint8_t* vb, const u32x4 (&pb)[2][2],
-                     const f32x16 (&sn)[2]) {
+  // Exponential slice kExpA + n goes beside O^T MFMA (n * kNv) / (2 * kExpB),
+  // always before the first MFMA that reads its 16-key group; the row-maximum
+  // slices of the next tile take the second half of the MFMAs.
+  auto phase_b = [&](auto with_max, const uint8_t* vb, const f32x16 (&sc)[2], u32x4 (&pb)[2][2],
+                     const f32x16 (&sn)[2], float m_use, float& rs) {
     float mx = -INFINITY;
     bf16x8 vf[kPf];
 #pragma unroll
@@ -409,11 +450,16 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p, Tile
       oacc[i % G::kNcb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
           vf[i % kPf], __builtin_bit_cast(bf16x8, pb[u >> 1][u & 1]), oacc[i % G::kNcb], 0, 0, 0);
       if (i + kPf < kNv) vf[i % kPf] = vfrag(vb, i + kPf);
+#pragma unroll
+      for (int n = 0; n < kExpB; ++n)
+        if ((n * kNv) / (2 * kExpB) == i) exp_slice(sc, pb, m_use, rs, kExpA + n);
       if constexpr (decltype(with_max)::value) {
-        if (i < 4) {
-          mx = max_slice(sn, i, mx);
-          asm volatile("" : "+v"(mx));  // keep the slice in this MFMA slot
-        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (kNv / 2 + (q * kNv) / 8 == i) {
+            mx = max_slice(sn, q, mx);
+            asm volatile("" : "+v"(mx));  // keep the slice in this MFMA slot
+          }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -441,11 +487,31 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p, Tile
   auto iteration = [&](auto has_next, int j, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
     constexpr bool kNext = decltype(has_next)::value;
     const int cur = j & 1;
-    // K_{j+2} and V_{j+1} go straight into the buffers of K_j and V_{j-1}
-    if (kNext && j + 2 < nt) load_k(j + 2);
-    if constexpr (kNext) load_v(j + 1);
+    // K_{j+2} and V_{j+1} go straight into the buffers of K_j and V_{j-1},
+    // one DMA instruction beside every (kNq / kNdma)-th S^T MFMA so that the
+    // eight waves do not all queue their loads at once. Past the last tile
+    // the last K tile is fetched again into the free buffer (branch-free;
+    // nobody reads it).
+    const uint8_t* kt = nullptr;
+    const uint8_t* vt = nullptr;
+    if constexpr (kNext) {
+      kt = prep(kbase, ksn, koff, kkey, kcol, min(j + 2, nt - 1));
+      vt = prep(vbase, vsn, voff, vkey, vcol, j + 1);
+    }
+    uint8_t* const kd = kbuf + cur * G::kKBytes;
+    uint8_t* const vd = vbuf + (cur ^ 1) * G::kVBytes;
+    auto dma = [&](int slot) {
+      if constexpr (kNext) {
+#pragma unroll
+        for (int n = 0; n < kNdma; ++n) {
+          if ((n * kNq) / kNdma != slot) continue;
+          if (n < G::kDmaPerWave) dma_k(kt, kd, n);
+          else dma_v(vt, vd, n - G::kDmaPerWave);
+        }
+      }
+    };
     u32x4 pb[2][2];
-    const float rs = phase_a(has_next, klane + (cur ^ 1) * G::kKBytes, sc, sn, pb, ref.m_use);
+    const float rs = phase_a(has_next, klane + (cur ^ 1) * G::kKBytes, sc, sn, pb, ref.m_use, dma);
     if (__builtin_amdgcn_ballot_w64(ref.move) != 0) {
       // alpha = 1 exactly for rows whose reference did not move
       const float alpha = __builtin_amdgcn_exp2f(m_run - ref.m_use);
@@ -455,10 +521,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p, Tile
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[cb][r] *= alpha;
     }
-    l_run += rs;
     m_run = ref.m_new;
     if constexpr (kNext) mask_bias(j + 1, sn);
-    const float mx = phase_b(has_next, vlane + cur * G::kVBytes, pb, sn);
+    float rs_b = 0.f;
+    const float mx = phase_b(has_next, vlane + cur * G::kVBytes, sc, pb, sn, ref.m_use, rs_b);
+    l_run += rs + rs_b;
     if constexpr (kNext) {
       ref = ref_update(mx);
       wait_tiles();

@@ -105,8 +105,9 @@ typedef struct {
  *
  * Supported: d in {64, 128}; dtype bf16 or f32; stride[3] == 1 for q, k, v,
  * o; data pointers 16-byte aligned and strides of dimensions 0-2 multiples of
- * 16 bytes. Negative strides are not supported. o and lse must not overlap
- * the inputs or each other.
+ * 16 bytes. Negative strides are not supported. The row stride of k and v
+ * (stride[2]) times 64 rows must span less than 2 GiB. o and lse must not
+ * overlap the inputs or each other.
  *
  * A row whose keys are all masked gets O = 0 and LSE = -inf. B, H or Nq equal
  * to 0 is a no-op that returns ATTN_OK; Nk == 0 writes O = 0 and LSE = -inf.

@@ -148,6 +148,10 @@ def test_layout_requirements():
     assert _call(k=_desc(s, stride=[16384, 4096, 68, 1], data=0x20000)) == ea.ATTN_ERR_UNSUPPORTED
     lse = _desc((2, 4, 64, 1), ea.ATTN_F32, data=0x50000, stride=[256, 64, 2, 1])
     assert _call(lse=lse) == ea.ATTN_ERR_UNSUPPORTED
+    # 64 key rows must span < 2 GiB (32-bit tile offsets)
+    big = 1 << 24
+    assert _call(k=_desc(s, stride=[64 * big, 64 * big, big, 1], data=0x20000)) == ea.ATTN_ERR_UNSUPPORTED
+    assert "row stride" in ea.last_error()
 
 
 def test_bias_checks():
