@@ -11,8 +11,9 @@
 // ("flash-attention", stanleyjacob.dev, Part VI).
 //
 // Work decomposition on CDNA4
-//   * One workgroup = 8 wavefronts = 256 query rows of one (batch, head);
-//     each wavefront owns 32 rows, so no cross-wave reduction of O is needed.
+//   * One workgroup = 8 wavefronts = 256 query rows of one (batch, head)
+//     (4 wavefronts = 128 rows for d = 64 with a causal mask or a bias); each
+//     wavefront owns 32 rows, so no cross-wave reduction of O is needed.
 //   * Key/value tiles of 64 keys are copied global -> LDS directly
 //     (global_load_lds_dwordx4, no staging registers), double buffered: the
 //     loads of the next tiles are issued at the start of an iteration into
@@ -63,9 +64,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 8;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kBr = 32 * kWaves;  // query rows per workgroup
 constexpr int kBc = 64;           // keys per tile
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kLog2e = 1.44269504088896341f;
@@ -76,8 +74,13 @@ constexpr int kPf = 4;            // MFMA operands read ahead from LDS
 constexpr int kExpB = 8;
 static_assert(kExpB % 2 == 0 && kExpB <= 8, "slices of a 16-key group must precede its MFMA");
 
-template <int D>
+// W = wavefronts per workgroup (8, or 4 where finer workgroups balance
+// uneven work better); each wavefront owns 32 query rows.
+template <int D, int W>
 struct Geo {
+  static constexpr int kWaves = W;
+  static constexpr int kThreads = 64 * W;
+  static constexpr int kBr = 32 * W;                  // query rows per workgroup
   static constexpr int kChunks = D / 8;               // 16-byte chunks per row
   static constexpr int kKBlock = 16 * kChunks * 16;   // 16 K rows, chunk-interleaved
   static constexpr int kVBlock = 4 * kChunks * 16;    // 4 V rows, chunk-interleaved
@@ -85,7 +88,7 @@ struct Geo {
   static constexpr int kVBytes = kBc * D * 2;
   static constexpr int kSmem = 2 * (kKBytes + kVBytes);
   static constexpr int kDma = kKBytes / 1024;         // 1 KB DMA instructions per tile (K or V)
-  static constexpr int kDmaPerWave = kDma / kWaves;
+  static constexpr int kDmaPerWave = kDma / W;
   static constexpr int kNkk = D / 16;                 // k-steps of QK^T
   static constexpr int kNcb = D / 32;                 // 32-wide output column blocks
 };
@@ -152,9 +155,11 @@ __device__ __forceinline__ bool decode_tile(const TileMap& tm, int B, int H,
   return true;
 }
 
-template <int D, bool CAUSAL, bool HAS_BIAS>
-__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p, TileMap tm) {
-  using G = Geo<D>;
+template <int D, int W, bool CAUSAL, bool HAS_BIAS>
+__global__ __launch_bounds__(64 * W, 2) void fwd_bf16_kernel(FwdParams p, TileMap tm) {
+  using G = Geo<D, W>;
+  constexpr int kWaves = G::kWaves;
+  constexpr int kBr = G::kBr;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
   int b, h, qt;
@@ -586,11 +591,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p, Tile
   }
 }
 
-template <int D, bool CAUSAL, bool HAS_BIAS>
+template <int D, int W, bool CAUSAL, bool HAS_BIAS>
 hipError_t launch_one(const FwdParams& p, const TileMap& tm, hipStream_t stream) {
-  using G = Geo<D>;
+  using G = Geo<D, W>;
   static bool attr_set = false;  // benign race: every caller sets the same value
-  auto kern = fwd_bf16_kernel<D, CAUSAL, HAS_BIAS>;
+  auto kern = fwd_bf16_kernel<D, W, CAUSAL, HAS_BIAS>;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, G::kSmem);
@@ -598,30 +603,35 @@ hipError_t launch_one(const FwdParams& p, const TileMap& tm, hipStream_t stream)
     attr_set = true;
   }
   const int grid = 8 * tm.per_xcd;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), G::kSmem, stream, p, tm);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(G::kThreads), G::kSmem, stream, p, tm);
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, int W>
 hipError_t launch_d(const FwdParams& p, const TileMap& tm, hipStream_t s) {
   const bool bias = p.bias != nullptr;
-  if (p.causal) return bias ? launch_one<D, true, true>(p, tm, s) : launch_one<D, true, false>(p, tm, s);
-  return bias ? launch_one<D, false, true>(p, tm, s) : launch_one<D, false, false>(p, tm, s);
+  if (p.causal) return bias ? launch_one<D, W, true, true>(p, tm, s) : launch_one<D, W, true, false>(p, tm, s);
+  return bias ? launch_one<D, W, false, true>(p, tm, s) : launch_one<D, W, false, false>(p, tm, s);
 }
 
 }  // namespace
 
 int launch_fwd_bf16(const FwdParams& p, int d, void* stream) {
+  // d = 64 with a causal mask or a bias: 4-wave (128-row) workgroups, so
+  // that two run on a CU at once and the uneven per-workgroup work (diagonal
+  // tiles, per-batch key lengths) is spread more finely; otherwise 8 waves.
+  const int waves = (d == 64 && (p.causal || p.bias != nullptr)) ? 4 : 8;
+  const int br = 32 * waves;
   TileMap tm;
-  tm.n_qtiles = (p.Nq + kBr - 1) / kBr;
+  tm.n_qtiles = (p.Nq + br - 1) / br;
   const int64_t total = (int64_t)p.B * p.H * tm.n_qtiles;
   tm.total = (int)total;
   tm.per_xcd = (int)((total + 7) / 8);
   tm.batch_inner = (p.bias != nullptr && p.bias_sb == 0 && p.B > 1) ? 1 : 0;
   tm.reverse_q = p.causal ? 1 : 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (d == 128) return (int)launch_d<128>(p, tm, s);
-  if (d == 64) return (int)launch_d<64>(p, tm, s);
+  if (d == 128) return (int)launch_d<128, 8>(p, tm, s);
+  if (d == 64) return waves == 4 ? (int)launch_d<64, 4>(p, tm, s) : (int)launch_d<64, 8>(p, tm, s);
   return (int)hipErrorInvalidValue;
 }
 
