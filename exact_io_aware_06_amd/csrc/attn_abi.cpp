@@ -157,8 +157,6 @@ attn_status_t attn_fwd(const attn_tensor_t* q, const attn_tensor_t* k, const att
     bias_vec = aligned16(bias->data);
     for (int i = 0; i < 3; ++i)
       if (bias->shape[i] > 1 && bias->stride[i] % 4 != 0) bias_vec = false;
-    // the d = 64 kernel addresses 32 bias rows with 32-bit byte offsets
-    if (Nq > 1 && 32 * st(bias, 2) * 4 >= (int64_t(1) << 31)) bias_vec = false;
   }
 
   attn::FwdParams p{};
