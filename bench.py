@@ -150,6 +150,13 @@ def main(argv=None):
 
     flops = w.flops()
     tflops = flops / (ms * 1e-3) / 1e12
+    extra = {}
+    if inp["kv_len"] is not None and not w.causal:
+        # FLOPs of the keys inside each batch's valid length only
+        kl = inp["kv_len"].clamp(0, w.Nk).double()
+        useful = float(4.0 * w.H * w.Nq * w.d * kl.sum().item())
+        extra = {"useful_flops_per_step": useful,
+                 "useful_tflops": round(useful / (ms * 1e-3) / 1e12, 2)}
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
@@ -166,7 +173,7 @@ def main(argv=None):
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic",
-        "config": {**w.describe(), "flops_per_step": flops, "parallelism": "single GPU"},
+        "config": {**w.describe(), "flops_per_step": flops, **extra, "parallelism": "single GPU"},
         "roofline": roofline, "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -38,13 +38,19 @@
 //     r at slot 16c + r) and V rows in blocks of 4 (slot 4c + r), so the rows
 //     one MFMA operand reads fall in distinct banks while every read address
 //     is a per-lane base plus an immediate offset.
-//   * The running maximum is a reference point, not necessarily the exact
-//     maximum: it moves only when a row's tile maximum exceeds it by more than
-//     kTau (base-2 units), so exponentials stay <= 2^kTau and the costly
-//     rescale of the output accumulator is rare. Any reference point gives the
-//     same result in exact arithmetic ("Understanding FlashAttention Pt 1",
-//     section 2.2: the maximum is only a change of reference; the conditional
-//     rescaling of "FlashAttention, Explained", section 22).
+//   * The running maximum is replaced by a reference point R per row: any R
+//     gives the same result in exact arithmetic ("Understanding FlashAttention
+//     Pt 1", section 2.2: the maximum is only a change of reference), as long
+//     as no probability 2^(s - R) overflows. R starts at the exact maximum of
+//     the first tile. Each later tile is exponentiated against R directly,
+//     without computing its maximum; before the O^T product consumes the
+//     probabilities, the per-lane sum of the tile's probabilities (an upper
+//     bound of each of them) is checked against 2^32. Only if it is larger
+//     (or not finite, or the row has no reference yet) does the wave compute
+//     the tile's exact maximum, move R up to it, rescale O and the
+//     denominator by 2^(R_old - R_new) and exponentiate the tile again (the
+//     conditional rescaling of "FlashAttention, Explained", section 22, made
+//     rare). Probabilities therefore stay below 2^32 and far from overflow.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -67,12 +73,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kBc = 64;           // keys per tile
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kLog2e = 1.44269504088896341f;
-constexpr float kTau = 8.0f;      // reference-maximum slack, base-2 units
+constexpr float kBig = 4294967296.0f;  // 2^32: bound on a lane's probability sum per tile
 constexpr int kPf = 4;            // MFMA operands read ahead from LDS
-// Exponential slices (of 16 per tile) computed beside the O^T MFMAs instead
-// of the S^T ones, to balance vector work between the two halves of a tile.
-constexpr int kExpB = 8;
-static_assert(kExpB % 2 == 0 && kExpB <= 8, "slices of a 16-key group must precede its MFMA");
 
 // W = wavefronts per workgroup (8, or 4 where finer workgroups balance
 // uneven work better); each wavefront owns 32 query rows.
@@ -96,6 +98,35 @@ struct Geo {
 // Row permutation of the K operand: swap bits 2 and 3 (an involution).
 __device__ __forceinline__ int perm_row(int r) {
   return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
+}
+
+// Source of the 16 bytes that `lane` of wave `wave` fetches in DMA
+// instruction i of a tile (instruction n of a tile is issued by wave n % W
+// and fills LDS bytes [1024 n, 1024 n + 1024)): key row within the tile and
+// byte column within the row. K tiles are chunk-interleaved in blocks of 16
+// rows with the rows permuted (perm_row), V tiles in blocks of 4.
+template <int D, int W>
+__device__ __forceinline__ int k_dma_key(int wave, int lane, int i) {
+  const int a = 1024 * (wave + W * i) + 16 * lane;
+  constexpr int blk = 16 * (D / 8) * 16;
+  const int ks = (a % blk) / 16;
+  return perm_row(16 * (a / blk) + ks % 16);
+}
+template <int D, int W>
+__device__ __forceinline__ int k_dma_col(int wave, int lane, int i) {
+  const int a = 1024 * (wave + W * i) + 16 * lane;
+  return 16 * ((a % (16 * (D / 8) * 16)) / 256);
+}
+template <int D, int W>
+__device__ __forceinline__ int v_dma_key(int wave, int lane, int i) {
+  const int a = 1024 * (wave + W * i) + 16 * lane;
+  constexpr int blk = 4 * (D / 8) * 16;
+  return 4 * (a / blk) + ((a % blk) / 16) % 4;
+}
+template <int D, int W>
+__device__ __forceinline__ int v_dma_col(int wave, int lane, int i) {
+  const int a = 1024 * (wave + W * i) + 16 * lane;
+  return 16 * ((a % (4 * (D / 8) * 16)) / 64);
 }
 
 __device__ __forceinline__ float lane_pair_max(float x) {
@@ -217,20 +248,12 @@ __global__ __launch_bounds__(64 * W, 2) void fwd_bf16_kernel(FwdParams p, TileMa
   // probabilities are exactly 0 and they contribute nothing.
   // Each lane's source offset inside a full tile is fixed: a 32-bit byte
   // offset added to the tile's base address, which is uniform (SGPRs).
-  int kkey[G::kDmaPerWave], kcol[G::kDmaPerWave], vkey[G::kDmaPerWave], vcol[G::kDmaPerWave];
   uint32_t koff[G::kDmaPerWave], voff[G::kDmaPerWave];
   const int64_t ksn = p.k_sn * 2, vsn = p.v_sn * 2;   // row strides in bytes
 #pragma unroll
   for (int i = 0; i < G::kDmaPerWave; ++i) {
-    const int a = 1024 * (wave + kWaves * i) + 16 * lane;   // LDS byte offset in the tile
-    const int ks = (a % G::kKBlock) / 16;
-    kkey[i] = perm_row(16 * (a / G::kKBlock) + ks % 16);
-    kcol[i] = 16 * (ks / 16);
-    const int vs = (a % G::kVBlock) / 16;
-    vkey[i] = 4 * (a / G::kVBlock) + vs % 4;
-    vcol[i] = 16 * (vs / 4);
-    koff[i] = (uint32_t)(kkey[i] * (int)ksn + kcol[i]);
-    voff[i] = (uint32_t)(vkey[i] * (int)vsn + vcol[i]);
+    koff[i] = (uint32_t)(k_dma_key<D, W>(wave, lane, i) * (int)ksn + k_dma_col<D, W>(wave, lane, i));
+    voff[i] = (uint32_t)(v_dma_key<D, W>(wave, lane, i) * (int)vsn + v_dma_col<D, W>(wave, lane, i));
   }
   const int last_key = Nk - 1;
   uint8_t* const kbuf = smem;                  // K tile t in buffer t % 2
@@ -238,17 +261,27 @@ __global__ __launch_bounds__(64 * W, 2) void fwd_bf16_kernel(FwdParams p, TileMa
   const uint8_t* const kbase = reinterpret_cast<const uint8_t*>(kgp);
   const uint8_t* const vbase = reinterpret_cast<const uint8_t*>(vgp);
   // Base address of key tile j (uniform). A tile that runs past the last key
-  // is the last tile of its kind ever loaded, so its clamped offsets simply
-  // replace the fixed ones.
-  auto prep = [&](const uint8_t* base, int64_t sn, uint32_t (&off)[G::kDmaPerWave],
-                  const int (&key)[G::kDmaPerWave], const int (&col)[G::kDmaPerWave], int j) {
+  // is the last tile of its kind ever loaded (later loads only fetch it
+  // again), so its clamped offsets simply replace the fixed ones.
+  auto prep_k = [&](int j) {
     const int kv0 = j * kBc;
     if (kv0 + kBc > Nk) {
 #pragma unroll
       for (int i = 0; i < G::kDmaPerWave; ++i)
-        off[i] = (uint32_t)(min(key[i], last_key - kv0) * (int)sn + col[i]);
+        koff[i] = (uint32_t)(min(k_dma_key<D, W>(wave, lane, i), last_key - kv0) * (int)ksn +
+                             k_dma_col<D, W>(wave, lane, i));
     }
-    return base + kv0 * sn;
+    return kbase + kv0 * ksn;
+  };
+  auto prep_v = [&](int j) {
+    const int kv0 = j * kBc;
+    if (kv0 + kBc > Nk) {
+#pragma unroll
+      for (int i = 0; i < G::kDmaPerWave; ++i)
+        voff[i] = (uint32_t)(min(v_dma_key<D, W>(wave, lane, i), last_key - kv0) * (int)vsn +
+                             v_dma_col<D, W>(wave, lane, i));
+    }
+    return vbase + kv0 * vsn;
   };
   // DMA instruction i of this wave for a K (V) tile at `tile` into buffer `dst`
   auto dma_k = [&](const uint8_t* tile, uint8_t* dst, int i) {
@@ -258,12 +291,12 @@ __global__ __launch_bounds__(64 * W, 2) void fwd_bf16_kernel(FwdParams p, TileMa
     dma16(tile, voff[i], dst + 1024 * (wave + kWaves * i));
   };
   auto load_k = [&](int j) {
-    const uint8_t* t = prep(kbase, ksn, koff, kkey, kcol, j);
+    const uint8_t* t = prep_k(j);
 #pragma unroll
     for (int i = 0; i < G::kDmaPerWave; ++i) dma_k(t, kbuf + (j & 1) * G::kKBytes, i);
   };
   auto load_v = [&](int j) {
-    const uint8_t* t = prep(vbase, vsn, voff, vkey, vcol, j);
+    const uint8_t* t = prep_v(j);
 #pragma unroll
     for (int i = 0; i < G::kDmaPerWave; ++i) dma_v(t, vbuf + (j & 1) * G::kVBytes, i);
   };
@@ -298,7 +331,7 @@ __global__ __launch_bounds__(64 * W, 2) void fwd_bf16_kernel(FwdParams p, TileMa
   f32x16 oacc[G::kNcb];
 #pragma unroll
   for (int cb = 0; cb < G::kNcb; ++cb) oacc[cb] = f32x16{};
-  float m_run = -INFINITY;  // reference maximum, base-2 units
+  float m_run = -INFINITY;  // reference R of this lane's row, base-2 units (-inf: none yet)
   float l_run = 0.f;        // this lane's share of the running denominator
   const float c2 = p.scale_log2;
 
@@ -358,30 +391,17 @@ __global__ __launch_bounds__(64 * W, 2) void fwd_bf16_kernel(FwdParams p, TileMa
   // at the same time within one wavefront. Slices are straight-line VALU
   // code; sched_barrier fences pin each slice after its MFMA.
   //
-  // Row-maximum slices (4 of them, one per quarter of the tile) and the
-  // reference update that follows them.
-  struct Ref {
-    float m_new, m_use;
-    bool move;
-  };
-  auto max_slice = [&](const f32x16 (&s)[2], int q, float acc) {
-    const int bb = q >> 1, r0 = (q & 1) * 8;
-    float m = fmaxf(acc, s[bb][r0]);
+  // Exact maximum of a score tile for this lane's row, in base-2 units (the
+  // lane pair l, l^32 holds the row's 64 keys). Used for the first tile and
+  // on the rare path only.
+  auto tile_max = [&](const f32x16 (&s)[2]) {
+    float m = -INFINITY;
 #pragma unroll
-    for (int r = 1; r < 8; ++r) m = fmaxf(m, s[bb][r0 + r]);
-    return m;
-  };
-  auto ref_update = [&](float mx) {
-    Ref f;
-    mx = lane_pair_max(mx);
-    const float m_tile = HAS_BIAS ? mx : mx * c2;
-    // false while nothing is visible (m_tile = -inf); true on the first
-    // visible tile (m_run = -inf)
-    f.move = m_tile > m_run + kTau;
-    f.m_new = f.move ? m_tile : m_run;
-    // a row with nothing visible yet keeps 0 as its reference (no -inf - -inf)
-    f.m_use = (f.m_new == -INFINITY) ? 0.f : f.m_new;
-    return f;
+    for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) m = fmaxf(m, s[bb][r]);
+    m = lane_pair_max(m);
+    return HAS_BIAS ? m : m * c2;
   };
   // Exponential slice: scores 2i and 2i+1 of the tile (block i/8, registers
   // 2(i%8), 2(i%8)+1) -> probabilities, their sum, and one packed bf16 pair
@@ -407,12 +427,13 @@ __global__ __launch_bounds__(64 * W, 2) void fwd_bf16_kernel(FwdParams p, TileMa
   // ---- software pipeline over key tiles (per wavefront):
   //   phase A of iteration j: S_{j+1} = K_{j+1} Q^T on the matrix pipe,
   //       exponentials/sums/bf16 packing of tile j on the vector ALUs;
-  //   phase B: O += V_j P_j on the matrix pipe, masks and row maximum of
-  //       tile j+1 on the vector ALUs.
+  //   then the overflow check of tile j (rarely: its exact maximum, the move
+  //       of the reference and the exponentials again), masks of tile j+1;
+  //   phase B: O += V_j P_j on the matrix pipe.
   // The LDS holds K_{j+1} and V_j during iteration j; K_{j+2} and V_{j+1}
   // are loaded meanwhile and written to the buffers of K_j and V_{j-1},
   // which no wave reads any more (one barrier per iteration).
-  constexpr int kExpA = 16 - kExpB;
+  constexpr int kExpA = 16;  // exponential slices per tile
   constexpr int kNdma = 2 * G::kDmaPerWave;  // K then V DMA instructions per wave and tile
   auto phase_a = [&](auto with_qk, const uint8_t* kb, const f32x16 (&sc)[2], f32x16 (&sn)[2],
                      u32x4 (&pb)[2][2], float m_use, auto&& dma) {
@@ -439,12 +460,7 @@ __global__ __launch_bounds__(64 * W, 2) void fwd_bf16_kernel(FwdParams p, TileMa
     }
     return rs;
   };
-  // Exponential slice kExpA + n goes beside O^T MFMA (n * kNv) / (2 * kExpB),
-  // always before the first MFMA that reads its 16-key group; the row-maximum
-  // slices of the next tile take the second half of the MFMAs.
-  auto phase_b = [&](auto with_max, const uint8_t* vb, const f32x16 (&sc)[2], u32x4 (&pb)[2][2],
-                     const f32x16 (&sn)[2], float m_use, float& rs) {
-    float mx = -INFINITY;
+  auto phase_b = [&](const uint8_t* vb, const u32x4 (&pb)[2][2]) {
     bf16x8 vf[kPf];
 #pragma unroll
     for (int i = 0; i < kPf; ++i) vf[i] = vfrag(vb, i);
@@ -455,20 +471,8 @@ __global__ __launch_bounds__(64 * W, 2) void fwd_bf16_kernel(FwdParams p, TileMa
       oacc[i % G::kNcb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
           vf[i % kPf], __builtin_bit_cast(bf16x8, pb[u >> 1][u & 1]), oacc[i % G::kNcb], 0, 0, 0);
       if (i + kPf < kNv) vf[i % kPf] = vfrag(vb, i + kPf);
-#pragma unroll
-      for (int n = 0; n < kExpB; ++n)
-        if ((n * kNv) / (2 * kExpB) == i) exp_slice(sc, pb, m_use, rs, kExpA + n);
-      if constexpr (decltype(with_max)::value) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          if (kNv / 2 + (q * kNv) / 8 == i) {
-            mx = max_slice(sn, q, mx);
-            asm volatile("" : "+v"(mx));  // keep the slice in this MFMA slot
-          }
-      }
       __builtin_amdgcn_sched_barrier(0);
     }
-    return mx;
   };
   auto qk_plain = [&](const uint8_t* kb, f32x16 (&s)[2]) {
     s[0] = f32x16{};
@@ -485,7 +489,6 @@ __global__ __launch_bounds__(64 * W, 2) void fwd_bf16_kernel(FwdParams p, TileMa
     }
   };
 
-  Ref ref{};  // reference update of the tile whose exponentials come next
   // has_next (compile time): tile j+1 exists. The last tile gets its own
   // code so the compiler cannot merge its exponentials with the pipelined
   // ones and pull them out of the MFMA slots.
@@ -500,8 +503,8 @@ __global__ __launch_bounds__(64 * W, 2) void fwd_bf16_kernel(FwdParams p, TileMa
     const uint8_t* kt = nullptr;
     const uint8_t* vt = nullptr;
     if constexpr (kNext) {
-      kt = prep(kbase, ksn, koff, kkey, kcol, min(j + 2, nt - 1));
-      vt = prep(vbase, vsn, voff, vkey, vcol, j + 1);
+      kt = prep_k(min(j + 2, nt - 1));
+      vt = prep_v(j + 1);
     }
     uint8_t* const kd = kbuf + cur * G::kKBytes;
     uint8_t* const vd = vbuf + (cur ^ 1) * G::kVBytes;
@@ -516,23 +519,30 @@ __global__ __launch_bounds__(64 * W, 2) void fwd_bf16_kernel(FwdParams p, TileMa
       }
     };
     u32x4 pb[2][2];
-    const float rs = phase_a(has_next, klane + (cur ^ 1) * G::kKBytes, sc, sn, pb, ref.m_use, dma);
-    if (__builtin_amdgcn_ballot_w64(ref.move) != 0) {
-      // alpha = 1 exactly for rows whose reference did not move
-      const float alpha = __builtin_amdgcn_exp2f(m_run - ref.m_use);
+    // a row with no reference yet exponentiates against 0 and takes the
+    // rare path below
+    float rs = phase_a(has_next, klane + (cur ^ 1) * G::kKBytes, sc, sn, pb,
+                       m_run == -INFINITY ? 0.f : m_run, dma);
+    if (__builtin_amdgcn_ballot_w64(!(rs <= kBig) || m_run == -INFINITY) != 0) {
+      // rare: move the reference to the tile maximum (never down) and redo
+      // the tile; alpha = 0 for a row that had no reference (O, l are 0)
+      const float r_new = fmaxf(m_run, tile_max(sc));
+      const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - r_new);
       l_run *= alpha;
 #pragma unroll
       for (int cb = 0; cb < G::kNcb; ++cb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[cb][r] *= alpha;
+      m_run = r_new;
+      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+      rs = 0.f;
+#pragma unroll
+      for (int k = 0; k < kExpA; ++k) exp_slice(sc, pb, m_use, rs, k);
     }
-    m_run = ref.m_new;
+    l_run += rs;
     if constexpr (kNext) mask_bias(j + 1, sn);
-    float rs_b = 0.f;
-    const float mx = phase_b(has_next, vlane + cur * G::kVBytes, sc, pb, sn, ref.m_use, rs_b);
-    l_run += rs + rs_b;
+    phase_b(vlane + cur * G::kVBytes, pb);
     if constexpr (kNext) {
-      ref = ref_update(mx);
       wait_tiles();
       __syncthreads();
     }
@@ -552,10 +562,7 @@ __global__ __launch_bounds__(64 * W, 2) void fwd_bf16_kernel(FwdParams p, TileMa
     // reading K_0 first
     if (nt > 2) __syncthreads();
     mask_bias(0, sa);
-    float mx = -INFINITY;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) mx = max_slice(sa, q, mx);
-    ref = ref_update(mx);
+    m_run = tile_max(sa);
     int j = 0;
     for (; j + 2 < nt; j += 2) {
       iteration(Yes{}, j, sa, sb);

@@ -69,7 +69,13 @@ def compare(o, lse, ro, rl, dtype, what=""):
     err_o = np.abs(o - ro).max() if o.size else 0.0
     live = ~dead
     err_l = np.abs(lse[live] - rl[live]).max() if live.any() else 0.0
-    _banner(f"{what}: max|dO|={err_o:.3e} max|dLSE|={err_l:.3e}")
+    # reported, not asserted: the mean error, and the floor set by rounding
+    # the oracle's own O to the output dtype
+    mean_o = np.abs(o - ro).mean() if o.size else 0.0
+    rdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    floor_o = (np.abs(torch.from_numpy(ro).to(rdt).double().numpy() - ro).max() if o.size else 0.0)
+    _banner(f"{what}: max|dO|={err_o:.3e} mean|dO|={mean_o:.3e} (rounding floor {floor_o:.3e}) "
+            f"max|dLSE|={err_l:.3e}")
     assert err_o <= TOL_O[dtype], f"{what}: O error {err_o}"
     assert err_l <= TOL_LSE, f"{what}: LSE error {err_l}"
 
