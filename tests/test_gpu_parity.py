@@ -217,6 +217,47 @@ def test_large_magnitude_scores():
     compare(o, lse, ro, rl, "bf16", "large scores")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_reference_jumps_between_tiles(causal):
+    # Every key tile's scores lie about 40 base-2 units above the previous
+    # tile's, so each tile overflows the kernel's probability-sum guard (2^32)
+    # and takes the rare path that moves the reference; the result must not
+    # change (any reference gives the same softmax).
+    g = torch.Generator().manual_seed(16)
+    nq, nk, d, scale = 70, 330, 64, 0.125
+    q = torch.randn(1, 2, nq, d, generator=g) * 0.05
+    q[..., 0] = 8.0
+    k = torch.randn(1, 2, nk, d, generator=g) * 0.05
+    step = 40.0 / (8.0 * scale * math.log2(math.e))  # raw k[...,0] per tile
+    k[..., 0] = (torch.arange(nk) // 64).float() * step
+    v = torch.randn(1, 2, nk, d, generator=g)
+    inp = {"q": q.to(torch.bfloat16), "k": k.to(torch.bfloat16), "v": v.to(torch.bfloat16),
+           "bias": None, "kv_len": None, "causal": causal, "scale": scale}
+    o, lse = run_gpu(inp)
+    ro, rl = run_oracle(inp)
+    compare(o, lse, ro, rl, "bf16", f"reference jumps causal={causal}")
+
+
+def test_first_tile_masked_and_low_scores():
+    # Rows 0..9 see nothing in the first key tile (-inf bias) and every other
+    # key carries a bias of -300: a reference left at 0 would underflow all
+    # their probabilities, so the kernel must set the reference from the first
+    # tile that has a visible key.
+    g = torch.Generator().manual_seed(17)
+    nq, nk, d = 70, 200, 64
+    q = torch.randn(1, 2, nq, d, generator=g).to(torch.bfloat16)
+    k = torch.randn(1, 2, nk, d, generator=g).to(torch.bfloat16)
+    v = torch.randn(1, 2, nk, d, generator=g).to(torch.bfloat16)
+    bias = torch.full((1, 2, nq, nk), -300.0)
+    bias[:, :, :10, :64] = -math.inf
+    inp = {"q": q, "k": k, "v": v, "bias": bias, "kv_len": None, "causal": False,
+           "scale": 0.125}
+    o, lse = run_gpu(inp)
+    ro, rl = run_oracle(inp)
+    assert np.all(np.isfinite(rl)) and rl.max() < -200
+    compare(o, lse, ro, rl, "bf16", "first tile masked, low scores")
+
+
 def test_deterministic_bitwise():
     w = workloads.small("c3_bf16_d128_causal", B=1, H=4, Nq=777, Nk=777)
     inp = workloads.make_inputs(w)
