@@ -98,6 +98,9 @@ def main(argv=None):
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a device-to-device copy of MIB mebibytes (the "
                          "reference kernel that scales the HBM byte counters)")
+    ap.add_argument("--gemm-calibration", type=int, default=0, metavar="N",
+                    help="only time a plain bf16 N x N x N matrix product through torch "
+                         "(the matrix throughput this GPU sustains, for context)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -118,6 +121,24 @@ def main(argv=None):
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4,
                           "launches": max(args.steps, 1)}), flush=True)
+        return 0
+
+    if args.gemm_calibration:
+        n = args.gemm_calibration
+        a = torch.randn(n, n, dtype=torch.bfloat16, device="cuda")
+        b = torch.randn(n, n, dtype=torch.bfloat16, device="cuda")
+        for _ in range(max(args.warmup, 1)):
+            c = a @ b
+        torch.cuda.synchronize()
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(max(args.steps, 1)):
+            c = a @ b
+        stop.record()
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(stop) / max(args.steps, 1)
+        print(json.dumps({"gemm_bf16_n": n, "ms": round(ms, 4),
+                          "tflops": round(2.0 * n ** 3 / (ms * 1e-3) / 1e12, 1)}), flush=True)
         return 0
 
     name = args.workload or workloads.HEADLINE
