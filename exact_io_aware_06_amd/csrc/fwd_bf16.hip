@@ -438,6 +438,11 @@ __global__ __launch_bounds__(64 * W, 2) void fwd_bf16_kernel(FwdParams p, TileMa
   auto phase_a = [&](auto with_qk, const uint8_t* kb, const f32x16 (&sc)[2], f32x16 (&sn)[2],
                      u32x4 (&pb)[2][2], float m_use, auto&& dma) {
     float rs = 0.f;
+    // Wave priority: 1 in phase A, 0 in phase B. The two waves of a SIMD start
+    // a tile together; the one that reaches phase B first (MFMAs only) then
+    // yields issue slots to the other, still in its vector-heavy phase A, so
+    // both arrive at the barrier closer together.
+    __builtin_amdgcn_s_setprio(1);
     if constexpr (decltype(with_qk)::value) {
       sn[0] = f32x16{};
       sn[1] = f32x16{};
@@ -461,6 +466,7 @@ __global__ __launch_bounds__(64 * W, 2) void fwd_bf16_kernel(FwdParams p, TileMa
     return rs;
   };
   auto phase_b = [&](const uint8_t* vb, const u32x4 (&pb)[2][2]) {
+    __builtin_amdgcn_s_setprio(0);
     bf16x8 vf[kPf];
 #pragma unroll
     for (int i = 0; i < kPf; ++i) vf[i] = vfrag(vb, i);
