@@ -5,7 +5,11 @@ with inputs already resident in device memory. Prints ONE JSON line.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
-The default workload is B=2, H=32, N=4096, d=128, bf16, non-causal.
+The default workload is B=2, H=32, N=4096, d=128, bf16, non-causal. A
+decoding workload (one query row per head, names starting "decode_") runs
+the split-key forward instead: one step = one attn_fwd_splitkv call (split
+forward + merge), and its roofline is the HBM one: the bytes of Q, K and V
+read once and of O and LSE written once, over the step time.
 """
 
 from __future__ import annotations
@@ -24,6 +28,7 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3     # MI355X dense fp32 matrix
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 KERNEL_SRC = {"bf16": "exact_io_aware_06_amd/csrc/fwd_bf16.hip",
               "f32": "exact_io_aware_06_amd/csrc/fwd_f32.hip"}
 
@@ -67,12 +72,14 @@ def cpu_baseline(inp, w, budget_s=15.0):
     import oracle
     q, k, v = inp["q"], inp["k"], inp["v"]
     heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    rep = w.H // w.kv_heads   # query head h reads key/value head h // rep
     done = 0
     t0 = time.perf_counter()
     for b, h in heads:
+        hk = h // rep
         oracle.attention_forward(q[b:b + 1, h:h + 1].double().numpy(),
-                                 k[b:b + 1, h:h + 1].double().numpy(),
-                                 v[b:b + 1, h:h + 1].double().numpy(),
+                                 k[b:b + 1, hk:hk + 1].double().numpy(),
+                                 v[b:b + 1, hk:hk + 1].double().numpy(),
                                  scale=inp["scale"], causal=w.causal)
         done += 1
         if time.perf_counter() - t0 >= budget_s:
@@ -83,7 +90,7 @@ def cpu_baseline(inp, w, budget_s=15.0):
         "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": _blas_threads(),
         "kind": "oracle",
         "sample": (f"{done} of {len(heads)} (b,h) heads of {w.name} at full "
-                   f"Nq=Nk={w.Nq}, fp64 materialising S and P, {dt:.1f} s"),
+                   f"Nq={w.Nq}, Nk={w.Nk}, fp64 materialising S and P, {dt:.1f} s"),
     }
 
 
@@ -93,6 +100,8 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default=None)
+    ap.add_argument("--splits", type=int, default=None,
+                    help="split count for a decoding workload (default: the library's choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -142,7 +151,8 @@ def main(argv=None):
         return 0
 
     name = args.workload or workloads.HEADLINE
-    w = workloads.CONFIGS[name]
+    w = workloads.ALL[name]
+    split = name in workloads.DECODE
     inp = workloads.make_inputs(w)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -151,10 +161,14 @@ def main(argv=None):
     kv_len = inp["kv_len"].to(dev) if inp["kv_len"] is not None else None
     o = torch.empty_like(q)
     lse = torch.empty(w.B, w.H, w.Nq, dtype=torch.float32, device=dev)
-
-    def step():
-        ea.attn_fwd(q, k, v, bias=bias, kv_len=kv_len, causal=w.causal,
-                    scale=inp["scale"], out=o, lse=lse)
+    n_split = None
+    if split:
+        n_split = args.splits or ea.splitkv_num_splits(w.B, w.H, w.Nq, w.Nk, w.d, w.causal,
+                                                       bias is not None)
+    # arguments marshalled once: a step is the launch(es) alone
+    step, _, _ = ea.prepare_call(q, k, v, bias=bias, kv_len=kv_len, causal=w.causal,
+                                 scale=inp["scale"], out=o, lse=lse, split=split,
+                                 num_splits=n_split)
 
     for _ in range(args.warmup):
         step()
@@ -182,6 +196,15 @@ def main(argv=None):
     roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
                 "traffic": _traffic(name, w.dtype)}
+    if split:
+        eb = 2 if w.dtype == "bf16" else 4
+        algo = w.kv_bytes() + w.B * w.H * w.Nq * (2 * w.d * eb + 4)  # K, V; Q, O; LSE
+        gbps = algo / (ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS,
+                    "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4),
+                    "traffic": _traffic(name, w.dtype),
+                    "bytes_per_step": algo, "timed": "split forward + merge (whole step)"}
+        extra = {"num_splits": n_split}
 
     cpu = None
     if not args.no_cpu_baseline:

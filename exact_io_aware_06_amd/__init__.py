@@ -9,6 +9,10 @@ module without the built library or without a GPU raises.
 
     from exact_io_aware_06_amd import attn_fwd
     o, lse = attn_fwd(q, k, v, causal=True)    # q, k, v: [B, H, N, d] on cuda
+
+For few query rows against many keys (decoding), ``attn_fwd_splitkv``
+computes the same function with the keys split across workgroups and the
+partial results merged by their log-sum-exps.
 """
 
 from __future__ import annotations
@@ -18,7 +22,8 @@ import math
 import os
 from typing import Optional
 
-__all__ = ["attn_fwd", "attn_fwd_raw", "AttnError", "load_library", "library_path",
+__all__ = ["attn_fwd", "attn_fwd_raw", "attn_fwd_splitkv", "attn_fwd_splitkv_raw",
+           "splitkv_num_splits", "splitkv_workspace_size", "prepare_call", "AttnError", "load_library", "library_path",
            "AttnTensor", "AttnMask", "ATTN_OK", "ATTN_ERR_INVALID",
            "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_HIP", "ATTN_BF16", "ATTN_F32"]
 
@@ -66,6 +71,14 @@ def load_library():
     lib.attn_fwd.argtypes = [P, P, P, ctypes.POINTER(AttnMask), ctypes.c_int, ctypes.c_float,
                              P, P, ctypes.c_void_p]
     lib.attn_fwd.restype = ctypes.c_int
+    lib.attn_fwd_splitkv.argtypes = [P, P, P, ctypes.POINTER(AttnMask), ctypes.c_int,
+                                     ctypes.c_float, ctypes.c_int32, ctypes.c_void_p,
+                                     ctypes.c_int64, P, P, ctypes.c_void_p]
+    lib.attn_fwd_splitkv.restype = ctypes.c_int
+    lib.attn_fwd_splitkv_workspace_size.argtypes = [ctypes.c_int64] * 4 + [ctypes.c_int32]
+    lib.attn_fwd_splitkv_workspace_size.restype = ctypes.c_int64
+    lib.attn_fwd_splitkv_num_splits.argtypes = [ctypes.c_int64] * 5 + [ctypes.c_int] * 2
+    lib.attn_fwd_splitkv_num_splits.restype = ctypes.c_int32
     lib.attn_last_error.argtypes = []
     lib.attn_last_error.restype = ctypes.c_char_p
     lib.attn_abi_version.argtypes = []
@@ -95,6 +108,31 @@ def attn_fwd_raw(q: AttnTensor, k: AttnTensor, v: AttnTensor, mask: Optional[Att
                         ctypes.byref(lse), ctypes.c_void_p(stream))
 
 
+def attn_fwd_splitkv_raw(q: AttnTensor, k: AttnTensor, v: AttnTensor, mask: Optional[AttnMask],
+                         causal: bool, scale: float, num_splits: int, workspace: int,
+                         workspace_bytes: int, o: AttnTensor, lse: AttnTensor,
+                         stream: int = 0) -> int:
+    """Call the split-key C entry point with prepared descriptors; returns the status."""
+    lib = load_library()
+    return lib.attn_fwd_splitkv(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v),
+                                ctypes.byref(mask) if mask is not None else None,
+                                1 if causal else 0, float(scale), int(num_splits),
+                                ctypes.c_void_p(workspace), int(workspace_bytes),
+                                ctypes.byref(o), ctypes.byref(lse), ctypes.c_void_p(stream))
+
+
+def splitkv_workspace_size(B: int, H: int, Nq: int, d: int, num_splits: int) -> int:
+    """Workspace bytes ``attn_fwd_splitkv`` needs (-1 for invalid arguments)."""
+    return int(load_library().attn_fwd_splitkv_workspace_size(B, H, Nq, d, num_splits))
+
+
+def splitkv_num_splits(B: int, H: int, Nq: int, Nk: int, d: int, causal: bool = False,
+                       has_bias: bool = False) -> int:
+    """The library's split count for this shape (1: no split)."""
+    return int(load_library().attn_fwd_splitkv_num_splits(
+        B, H, Nq, Nk, d, 1 if causal else 0, 1 if has_bias else 0))
+
+
 def last_error() -> str:
     return load_library().attn_last_error().decode()
 
@@ -112,17 +150,7 @@ def _torch_desc(t, name):
     return make_desc(t.data_ptr(), dt, t.shape, t.stride())
 
 
-def attn_fwd(q, k, v, bias=None, kv_len=None, causal: bool = False,
-             scale: Optional[float] = None, out=None, lse=None):
-    """O = softmax_row(scale * Q K^T + bias) V and the row log-sum-exp.
-
-    q: [B, H, Nq, d], k and v: [B, Hk, Nk, d] (Hk divides H), bfloat16 or
-    float32 CUDA/HIP tensors with a contiguous last dimension. bias: optional
-    float32 [B|1, H|1, Nq, Nk], added unscaled. kv_len: optional int32 [B] on
-    the same device; keys at or past kv_len[b] are masked. causal hides key j
-    from query i when j > i + (Nk - Nq). scale defaults to 1/sqrt(d).
-    Returns (o [B, H, Nq, d] in q's dtype, lse [B, H, Nq] float32).
-    """
+def _prepare(q, k, v, bias, kv_len, scale, out, lse):
     import torch
     if not (q.is_cuda and k.is_cuda and v.is_cuda):
         raise ValueError("q, k and v must be GPU tensors (no CPU path exists)")
@@ -139,13 +167,14 @@ def attn_fwd(q, k, v, bias=None, kv_len=None, causal: bool = False,
     qd, kd, vd, od = (_torch_desc(t, n) for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out")))
     ld = make_desc(lse.data_ptr(), ATTN_F32, (*lse.shape, 1), (*lse.stride(), 1))
     mask = None
-    bias_desc = None
+    keep = []
     if bias is not None or kv_len is not None:
         mask = AttnMask()
         if bias is not None:
             if bias.dtype != torch.float32 or not bias.is_cuda or bias.dim() != 4:
                 raise ValueError("bias must be a float32 4-D GPU tensor")
             bias_desc = make_desc(bias.data_ptr(), ATTN_F32, bias.shape, bias.stride())
+            keep.append(bias_desc)
             mask.bias = ctypes.pointer(bias_desc)
         if kv_len is not None:
             if kv_len.dtype != torch.int32 or not kv_len.is_cuda or kv_len.numel() != B:
@@ -153,8 +182,102 @@ def attn_fwd(q, k, v, bias=None, kv_len=None, causal: bool = False,
             if not kv_len.is_contiguous():
                 raise ValueError("kv_len must be contiguous")
             mask.kv_len = kv_len.data_ptr()
-    with torch.cuda.device(dev):
-        stream = torch.cuda.current_stream(dev).cuda_stream
+    return scale, out, lse, (qd, kd, vd, od, ld, mask, keep)
+
+
+def attn_fwd_splitkv(q, k, v, bias=None, kv_len=None, causal: bool = False,
+                     scale: Optional[float] = None, num_splits: Optional[int] = None,
+                     workspace=None, out=None, lse=None):
+    """``attn_fwd`` with the keys split across workgroups (flash-decoding).
+
+    Same arguments and result as ``attn_fwd`` (bfloat16 only). num_splits
+    defaults to the library's choice for the shape. workspace: optional
+    uint8 GPU tensor of at least ``splitkv_workspace_size(B, H, Nq, d,
+    num_splits)`` bytes; allocated here when not given.
+    """
+    import torch
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if num_splits is None:
+        num_splits = splitkv_num_splits(B, H, Nq, Nk, d, causal, bias is not None)
+    scale, out, lse, (qd, kd, vd, od, ld, mask, _keep) = _prepare(q, k, v, bias, kv_len, scale,
+                                                                    out, lse)
+    need = splitkv_workspace_size(B, H, Nq, d, num_splits)
+    if need < 0:
+        raise AttnError(ATTN_ERR_INVALID, f"invalid split count {num_splits} for this shape")
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        rc = attn_fwd_splitkv_raw(qd, kd, vd, mask, causal, scale, num_splits,
+                                  workspace.data_ptr(), ws_bytes, od, ld, stream)
+    if rc != ATTN_OK:
+        raise AttnError(rc, last_error())
+    return out, lse
+
+
+def prepare_call(q, k, v, bias=None, kv_len=None, causal: bool = False,
+                 scale: Optional[float] = None, out=None, lse=None, split: bool = False,
+                 num_splits: Optional[int] = None, workspace=None):
+    """Marshal the arguments once; return ``(enqueue, out, lse)``.
+
+    ``enqueue()`` launches the forward (``split``: the split-key forward) on
+    the stream that was current when this was called, with no per-call
+    argument marshalling, and raises AttnError on a non-OK status. The
+    tensors must stay alive and in place while ``enqueue`` is used.
+    """
+    import torch
+    B, H, Nq, d = q.shape
+    scale, out, lse, (qd, kd, vd, od, ld, mask, keep) = _prepare(q, k, v, bias, kv_len, scale,
+                                                                   out, lse)
+    lib = load_library()
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    refs = (qd, kd, vd, od, ld, mask, keep)
+    mp = ctypes.byref(mask) if mask is not None else None
+    args = [ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(vd), mp, 1 if causal else 0,
+            float(scale)]
+    if split:
+        if num_splits is None:
+            num_splits = splitkv_num_splits(B, H, Nq, k.shape[2], d, causal, bias is not None)
+        need = splitkv_workspace_size(B, H, Nq, d, num_splits)
+        if need < 0:
+            raise AttnError(ATTN_ERR_INVALID, f"invalid split count {num_splits} for this shape")
+        if workspace is None:
+            workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        args += [int(num_splits), ctypes.c_void_p(workspace.data_ptr()),
+                 workspace.numel() * workspace.element_size()]
+        fn = lib.attn_fwd_splitkv
+    else:
+        fn = lib.attn_fwd
+    args += [ctypes.byref(od), ctypes.byref(ld), ctypes.c_void_p(stream)]
+
+    def enqueue(_refs=refs, _ws=workspace):
+        rc = fn(*args)
+        if rc != ATTN_OK:
+            raise AttnError(rc, last_error())
+
+    return enqueue, out, lse
+
+
+def attn_fwd(q, k, v, bias=None, kv_len=None, causal: bool = False,
+             scale: Optional[float] = None, out=None, lse=None):
+    """O = softmax_row(scale * Q K^T + bias) V and the row log-sum-exp.
+
+    q: [B, H, Nq, d], k and v: [B, Hk, Nk, d] (Hk divides H), bfloat16 or
+    float32 CUDA/HIP tensors with a contiguous last dimension. bias: optional
+    float32 [B|1, H|1, Nq, Nk], added unscaled. kv_len: optional int32 [B] on
+    the same device; keys at or past kv_len[b] are masked. causal hides key j
+    from query i when j > i + (Nk - Nq). scale defaults to 1/sqrt(d).
+    Returns (o [B, H, Nq, d] in q's dtype, lse [B, H, Nq] float32).
+    """
+    import torch
+    scale, out, lse, (qd, kd, vd, od, ld, mask, _keep) = _prepare(q, k, v, bias, kv_len, scale,
+                                                                    out, lse)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
         rc = attn_fwd_raw(qd, kd, vd, mask, causal, scale, od, ld, stream)
     if rc != ATTN_OK:
         raise AttnError(rc, last_error())

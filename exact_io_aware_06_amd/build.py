@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libattn.so")
 
-SOURCES = ["attn_abi.cpp", "runtime.hip", "fwd_bf16.hip", "fwd_f32.hip"]
+SOURCES = ["attn_abi.cpp", "runtime.hip", "fwd_bf16.hip", "fwd_f32.hip", "combine.hip"]
 
 # -packed-fp32-ops: keep the compiler from emitting v_pk_{add,mul,fma}_f32.
 HIPCC_FLAGS = [
@@ -35,15 +35,36 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    """Compile every source to an object in parallel, then link the library."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    common = [hipcc(), *[f for f in HIPCC_FLAGS if f != "-shared"], "-I", INCLUDE, "-I", CSRC]
+
+    def compile_one(src):
+        obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
+        cmd = [*common, "-c", "-o", obj, os.path.join(CSRC, src)]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        return obj, res
+
+    with ThreadPoolExecutor(max_workers=min(len(SOURCES), 8)) as ex:
+        results = list(ex.map(compile_one, SOURCES))
+    for obj, res in results:
+        if res.returncode != 0:
+            sys.stderr.write(res.stdout + res.stderr)
+            raise RuntimeError(f"hipcc failed on {obj} with exit code {res.returncode}")
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-o", tmp, *srcs]
+    cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp,
+           *[obj for obj, _ in results]]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
+        raise RuntimeError(f"link failed with exit code {res.returncode}")
     os.replace(tmp, LIB)
     return LIB
 

@@ -10,6 +10,7 @@
 
 #include "../../include/attn.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -71,18 +72,13 @@ int64_t st(const attn_tensor_t* t, int i) { return t->shape[i] > 1 ? t->stride[i
 
 constexpr int64_t kMaxExtent = (int64_t)1 << 30;
 
-}  // namespace
-
-extern "C" {
-
-int attn_abi_version(void) { return ATTN_ABI_VERSION; }
-
-const char* attn_last_error(void) { return g_last_error.c_str(); }
-
-attn_status_t attn_fwd(const attn_tensor_t* q, const attn_tensor_t* k, const attn_tensor_t* v,
-                       const attn_mask_t* bias_or_mask, int causal, float scale,
-                       const attn_tensor_t* o, const attn_tensor_t* lse, void* stream) {
-  g_last_error.clear();
+// Validates the arguments shared by every forward entry point and fills `p`.
+// `empty` is set when there is nothing to write (B, H or Nq is 0).
+attn_status_t prepare(const attn_tensor_t* q, const attn_tensor_t* k, const attn_tensor_t* v,
+                      const attn_mask_t* bias_or_mask, int causal, float scale,
+                      const attn_tensor_t* o, const attn_tensor_t* lse, attn::FwdParams& p,
+                      bool& empty) {
+  empty = false;
   if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || lse == nullptr)
     return fail(ATTN_ERR_INVALID, "q, k, v, o and lse descriptors must be non-NULL");
   const int32_t dt = q->dtype;
@@ -129,7 +125,10 @@ attn_status_t attn_fwd(const attn_tensor_t* q, const attn_tensor_t* k, const att
   }
 
   // empty work: nothing to write
-  if (B == 0 || H == 0 || Nq == 0) return ATTN_OK;
+  if (B == 0 || H == 0 || Nq == 0) {
+    empty = true;
+    return ATTN_OK;
+  }
 
   if ((s = check_rows("q", q)) != ATTN_OK) return s;
   if ((s = check_rows("o", o)) != ATTN_OK) return s;
@@ -159,7 +158,7 @@ attn_status_t attn_fwd(const attn_tensor_t* q, const attn_tensor_t* k, const att
       if (bias->shape[i] > 1 && bias->stride[i] % 4 != 0) bias_vec = false;
   }
 
-  attn::FwdParams p{};
+  p = attn::FwdParams{};
   p.q = q->data;
   p.k = k->data;
   p.v = v->data;
@@ -186,14 +185,113 @@ attn_status_t attn_fwd(const attn_tensor_t* q, const attn_tensor_t* k, const att
   p.causal = causal ? 1 : 0;
   p.bias_vec = bias_vec ? 1 : 0;
   p.scale_log2 = scale * 1.44269504088896341f;
+  p.n_split = 1;
 
   // grid size: 8 * ceil(B*H*ceil(Nq/16)/8) workgroups at most (f32 tiles are smallest)
   const int64_t tiles = B * H * ((Nq + 15) / 16);
   if (tiles > ((int64_t)1 << 31) - 64)
     return fail(ATTN_ERR_UNSUPPORTED, "problem needs more than 2^31 workgroups");
+  return ATTN_OK;
+}
 
-  const int rc = (dt == ATTN_BF16) ? attn::launch_fwd_bf16(p, (int)d, stream)
-                                   : attn::launch_fwd_f32(p, (int)d, stream);
+attn_status_t launch(const attn::FwdParams& p, int32_t dt, int d, void* stream) {
+  const int rc = (dt == ATTN_BF16) ? attn::launch_fwd_bf16(p, d, stream)
+                                   : attn::launch_fwd_f32(p, d, stream);
+  if (rc != 0) return fail(ATTN_ERR_HIP, "kernel launch failed: %s", attn::hip_error_text(rc));
+  return ATTN_OK;
+}
+
+// Keys per split for a requested split count: a whole number of 64-key tiles.
+int64_t split_keys(int64_t Nk, int64_t num_splits) {
+  const int64_t per = (Nk + num_splits - 1) / num_splits;
+  return (per + 63) / 64 * 64;
+}
+
+constexpr int kMaxSplits = 1024;
+
+}  // namespace
+
+extern "C" {
+
+int attn_abi_version(void) { return ATTN_ABI_VERSION; }
+
+const char* attn_last_error(void) { return g_last_error.c_str(); }
+
+attn_status_t attn_fwd(const attn_tensor_t* q, const attn_tensor_t* k, const attn_tensor_t* v,
+                       const attn_mask_t* bias_or_mask, int causal, float scale,
+                       const attn_tensor_t* o, const attn_tensor_t* lse, void* stream) {
+  g_last_error.clear();
+  attn::FwdParams p;
+  bool empty;
+  attn_status_t s = prepare(q, k, v, bias_or_mask, causal, scale, o, lse, p, empty);
+  if (s != ATTN_OK || empty) return s;
+  return launch(p, q->dtype, (int)q->shape[3], stream);
+}
+
+int64_t attn_fwd_splitkv_workspace_size(int64_t B, int64_t H, int64_t Nq, int64_t d,
+                                        int32_t num_splits) {
+  if (B < 0 || H < 0 || Nq < 0 || d < 0 || num_splits < 1) return -1;
+  if (B > kMaxExtent || H > kMaxExtent || Nq > kMaxExtent || d > 1024 || num_splits > kMaxSplits)
+    return -1;
+  // partial outputs [num_splits, B, H, Nq, d] then log-sum-exps [num_splits, B, H, Nq], fp32
+  const double bytes = (double)num_splits * B * H * Nq * (d + 1) * 4.0;
+  if (bytes > 9.0e18) return -1;
+  return (int64_t)num_splits * B * H * Nq * (d + 1) * 4;
+}
+
+int32_t attn_fwd_splitkv_num_splits(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                                    int causal, int has_bias) {
+  if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || (d != 64 && d != 128)) return 1;
+  // Workgroups without a split, against the 512 that MI355X runs at once
+  // (256 CUs, two workgroups each); aim for two full waves of workgroups,
+  // with at least 256 keys (four tiles) per split.
+  const int64_t rows = attn::fwd_bf16_rows((int)d, Nq, causal != 0, has_bias != 0, true);
+  const int64_t wgs = B * H * ((Nq + rows - 1) / rows);
+  constexpr int64_t kTarget = 1024;
+  int64_t n = (kTarget + wgs - 1) / wgs;
+  n = std::min<int64_t>(n, std::max<int64_t>(1, Nk / 256));
+  n = std::min<int64_t>(n, kMaxSplits);
+  return (int32_t)std::max<int64_t>(n, 1);
+}
+
+attn_status_t attn_fwd_splitkv(const attn_tensor_t* q, const attn_tensor_t* k,
+                               const attn_tensor_t* v, const attn_mask_t* bias_or_mask,
+                               int causal, float scale, int32_t num_splits, void* workspace,
+                               int64_t workspace_bytes, const attn_tensor_t* o,
+                               const attn_tensor_t* lse, void* stream) {
+  g_last_error.clear();
+  if (num_splits < 1 || num_splits > kMaxSplits)
+    return fail(ATTN_ERR_INVALID, "num_splits must be in [1, %d] (got %d)", kMaxSplits, (int)num_splits);
+  attn::FwdParams p;
+  bool empty;
+  attn_status_t s = prepare(q, k, v, bias_or_mask, causal, scale, o, lse, p, empty);
+  if (s != ATTN_OK || empty) return s;
+  if (q->dtype != ATTN_BF16)
+    return fail(ATTN_ERR_UNSUPPORTED, "the split-key forward supports bf16 only");
+  const int d = (int)q->shape[3];
+  const int64_t kv_split = p.Nk > 0 ? split_keys(p.Nk, num_splits) : 64;
+  const int64_t n_split = p.Nk > 0 ? (p.Nk + kv_split - 1) / kv_split : 1;
+  // a single split is the plain forward: no workspace is used
+  if (n_split <= 1) return launch(p, ATTN_BF16, d, stream);
+
+  const int64_t need = attn_fwd_splitkv_workspace_size(p.B, p.H, p.Nq, d, (int32_t)n_split);
+  if (need < 0) return fail(ATTN_ERR_UNSUPPORTED, "workspace size overflows");
+  if (workspace == nullptr || !aligned16(workspace))
+    return fail(ATTN_ERR_INVALID, "workspace is NULL or not 16-byte aligned");
+  if (workspace_bytes < need)
+    return fail(ATTN_ERR_INVALID, "workspace of %lld bytes is too small (%lld needed for %lld splits)",
+                (long long)workspace_bytes, (long long)need, (long long)n_split);
+  const int rows = attn::fwd_bf16_rows(d, p.Nq, p.causal != 0, p.bias != nullptr, true);
+  const int64_t wgs = (int64_t)p.B * p.H * ((p.Nq + rows - 1) / rows) * n_split;
+  if (wgs > ((int64_t)1 << 31) - 64 || (int64_t)p.B * p.H * p.Nq > ((int64_t)1 << 32))
+    return fail(ATTN_ERR_UNSUPPORTED, "problem needs more than 2^31 workgroups");
+
+  p.kv_split = (int32_t)kv_split;
+  p.n_split = (int32_t)n_split;
+  p.part_o = static_cast<float*>(workspace);
+  p.part_lse = p.part_o + n_split * (int64_t)p.B * p.H * p.Nq * d;
+  int rc = attn::launch_fwd_bf16(p, d, stream);
+  if (rc == 0) rc = attn::launch_combine_bf16(p, d, stream);
   if (rc != 0) return fail(ATTN_ERR_HIP, "kernel launch failed: %s", attn::hip_error_text(rc));
   return ATTN_OK;
 }

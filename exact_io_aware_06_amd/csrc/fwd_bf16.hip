@@ -164,14 +164,24 @@ __device__ __forceinline__ void dma16(const uint8_t* tile, uint32_t off, uint8_t
   asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(tile), "{m0}"(lds));
 }
 
+template <bool SPLIT>
 __device__ __forceinline__ bool decode_tile(const TileMap& tm, int B, int H,
-                                            int& b, int& h, int& qt) {
+                                            int& b, int& h, int& qt, int& split) {
   const int w = blockIdx.x;
   const int logical = (w & 7) * tm.per_xcd + (w >> 3);
   if (logical >= tm.total) return false;
   int rest;
   int qi;
-  if (tm.batch_inner) {
+  split = 0;
+  if (SPLIT) {
+    // query tile fastest (they read the same key range), then the split
+    qi = logical % tm.n_qtiles;
+    rest = logical / tm.n_qtiles;
+    split = rest % tm.n_split;
+    rest /= tm.n_split;
+    h = rest % H;
+    b = rest / H;
+  } else if (tm.batch_inner) {
     b = logical % B;
     rest = logical / B;
     qi = rest % tm.n_qtiles;
@@ -186,15 +196,17 @@ __device__ __forceinline__ bool decode_tile(const TileMap& tm, int B, int H,
   return true;
 }
 
-template <int D, int W, bool CAUSAL, bool HAS_BIAS>
+// SPLIT: one split of the keys per workgroup, partial results to the
+// workspace (p.n_split > 1); otherwise all keys, results to o / lse.
+template <int D, int W, bool CAUSAL, bool HAS_BIAS, bool SPLIT>
 __global__ __launch_bounds__(64 * W, 2) void fwd_bf16_kernel(FwdParams p, TileMap tm) {
   using G = Geo<D, W>;
   constexpr int kWaves = G::kWaves;
   constexpr int kBr = G::kBr;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
-  int b, h, qt;
-  if (!decode_tile(tm, p.B, p.H, b, h, qt)) return;
+  int b, h, qt, split;
+  if (!decode_tile<SPLIT>(tm, p.B, p.H, b, h, qt, split)) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -203,19 +215,24 @@ __global__ __launch_bounds__(64 * W, 2) void fwd_bf16_kernel(FwdParams p, TileMa
   const int hi = lane >> 5;
   const int hk = h / p.head_group;
 
+  // Split over keys: this workgroup covers keys [kbeg, kbeg + kv_split) of
+  // its rows. Key indices below are relative to kbeg (the K/V and bias base
+  // addresses, the key count and the causal offset are shifted by it).
+  const int kbeg = SPLIT ? split * p.kv_split : 0;
   const __bf16* qg = static_cast<const __bf16*>(p.q) + b * p.q_sb + h * p.q_sh;
-  const __bf16* kgp = static_cast<const __bf16*>(p.k) + b * p.k_sb + hk * p.k_sh;
-  const __bf16* vgp = static_cast<const __bf16*>(p.v) + b * p.v_sb + hk * p.v_sh;
+  const __bf16* kgp = static_cast<const __bf16*>(p.k) + b * p.k_sb + hk * p.k_sh + (int64_t)kbeg * p.k_sn;
+  const __bf16* vgp = static_cast<const __bf16*>(p.v) + b * p.v_sb + hk * p.v_sh + (int64_t)kbeg * p.v_sn;
 
   const int Nq = p.Nq;
-  const int Nk = p.Nk;
+  const int Nk = p.Nk - kbeg;  // keys from kbeg on
   const int q0 = qt * kBr;
   const int qw0 = q0 + wave * 32;
   const int my_q = qw0 + l32;
-  const int off = Nk - Nq;  // causal alignment: key j hidden when j > i + off
+  const int off = p.Nk - Nq - kbeg;  // causal alignment: key j hidden when j > i + off
 
   int kend = Nk;
-  if (p.kv_len != nullptr) kend = min(max(p.kv_len[b], 0), Nk);
+  if (p.kv_len != nullptr) kend = min(max(p.kv_len[b] - kbeg, 0), Nk);
+  if (SPLIT) kend = min(kend, p.kv_split);
   int wg_keys = kend;
   if (CAUSAL) wg_keys = min(kend, min(q0 + kBr, Nq) + off);
   wg_keys = max(wg_keys, 0);
@@ -338,7 +355,7 @@ __global__ __launch_bounds__(64 * W, 2) void fwd_bf16_kernel(FwdParams p, TileMa
   const float* brow = nullptr;
   if (HAS_BIAS) {
     const int qrow = min(my_q, Nq - 1);
-    brow = p.bias + b * p.bias_sb + h * p.bias_sh + (int64_t)qrow * p.bias_sn + 8 * hi;
+    brow = p.bias + b * p.bias_sb + h * p.bias_sh + (int64_t)qrow * p.bias_sn + kbeg + 8 * hi;
   }
 
   // Bias and masks of tile j. Register r of block bb holds key
@@ -584,7 +601,24 @@ __global__ __launch_bounds__(64 * W, 2) void fwd_bf16_kernel(FwdParams p, TileMa
 
   // ---- epilogue: one division per row, O and LSE written once
   const float l_tot = lane_pair_sum(l_run);
-  if (my_q < Nq) {
+  if (SPLIT && my_q < Nq) {
+    // one split of the keys: its normalised output and log-sum-exp in fp32,
+    // merged with the other splits by the combine kernel
+    const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+    const int64_t row = (((int64_t)split * p.B + b) * p.H + h) * Nq + my_q;
+    float* orow = p.part_o + row * D;
+#pragma unroll
+    for (int cb = 0; cb < G::kNcb; ++cb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = oacc[cb][4 * g + e] * inv;
+        *reinterpret_cast<f32x4*>(orow + 32 * cb + 8 * g + 4 * hi) = w;
+      }
+    if (hi == 0)
+      p.part_lse[row] = (l_tot > 0.f) ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
+  } else if (my_q < Nq) {
     const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
     __bf16* orow = static_cast<__bf16*>(p.o) + b * p.o_sb + h * p.o_sh + (int64_t)my_q * p.o_sn;
     // register r of block cb holds column 32cb + 8(r/4) + 4hi + (r%4)
@@ -604,11 +638,11 @@ __global__ __launch_bounds__(64 * W, 2) void fwd_bf16_kernel(FwdParams p, TileMa
   }
 }
 
-template <int D, int W, bool CAUSAL, bool HAS_BIAS>
+template <int D, int W, bool CAUSAL, bool HAS_BIAS, bool SPLIT>
 hipError_t launch_one(const FwdParams& p, const TileMap& tm, hipStream_t stream) {
   using G = Geo<D, W>;
   static bool attr_set = false;  // benign race: every caller sets the same value
-  auto kern = fwd_bf16_kernel<D, W, CAUSAL, HAS_BIAS>;
+  auto kern = fwd_bf16_kernel<D, W, CAUSAL, HAS_BIAS, SPLIT>;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, G::kSmem);
@@ -620,21 +654,43 @@ hipError_t launch_one(const FwdParams& p, const TileMap& tm, hipStream_t stream)
   return hipGetLastError();
 }
 
-template <int D, int W>
+template <int D, int W, bool SPLIT>
 hipError_t launch_d(const FwdParams& p, const TileMap& tm, hipStream_t s) {
   const bool bias = p.bias != nullptr;
-  if (p.causal) return bias ? launch_one<D, W, true, true>(p, tm, s) : launch_one<D, W, true, false>(p, tm, s);
-  return bias ? launch_one<D, W, false, true>(p, tm, s) : launch_one<D, W, false, false>(p, tm, s);
+  if (p.causal)
+    return bias ? launch_one<D, W, true, true, SPLIT>(p, tm, s) : launch_one<D, W, true, false, SPLIT>(p, tm, s);
+  return bias ? launch_one<D, W, false, true, SPLIT>(p, tm, s) : launch_one<D, W, false, false, SPLIT>(p, tm, s);
+}
+
+template <bool SPLIT>
+hipError_t launch_dw(const FwdParams& p, const TileMap& tm, int d, int waves, hipStream_t s) {
+  if (d == 128) {
+    // 4-wave workgroups for d = 128 are only chosen for split launches
+    if constexpr (SPLIT)
+      if (waves == 4) return launch_d<128, 4, true>(p, tm, s);
+    return launch_d<128, 8, SPLIT>(p, tm, s);
+  }
+  if (d == 64) return waves == 4 ? launch_d<64, 4, SPLIT>(p, tm, s) : launch_d<64, 8, SPLIT>(p, tm, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-int launch_fwd_bf16(const FwdParams& p, int d, void* stream) {
+int fwd_bf16_rows(int d, int64_t nq, bool causal, bool bias, bool split) {
   // d = 64 with a causal mask or a bias: 4-wave (128-row) workgroups, so
   // that two run on a CU at once and the uneven per-workgroup work (diagonal
-  // tiles, per-batch key lengths) is spread more finely; otherwise 8 waves.
-  const int waves = (d == 64 && (p.causal || p.bias != nullptr)) ? 4 : 8;
-  const int br = 32 * waves;
+  // tiles, per-batch key lengths) is spread more finely. A split launch with
+  // at most 128 query rows (decoding) also takes 4 waves: the rows past Nq
+  // are wasted matrix work, and 4-wave workgroups put half as much of it on
+  // each SIMD. Otherwise 8 waves.
+  if (d == 64 && (causal || bias)) return 128;
+  if (split && nq <= 128) return 128;
+  return 256;
+}
+
+int launch_fwd_bf16(const FwdParams& p, int d, void* stream) {
+  const int br = fwd_bf16_rows(d, p.Nq, p.causal != 0, p.bias != nullptr, p.n_split > 1);
+  const int waves = br / 32;
   TileMap tm;
   tm.n_qtiles = (p.Nq + br - 1) / br;
   const int64_t total = (int64_t)p.B * p.H * tm.n_qtiles;
@@ -642,10 +698,16 @@ int launch_fwd_bf16(const FwdParams& p, int d, void* stream) {
   tm.per_xcd = (int)((total + 7) / 8);
   tm.batch_inner = (p.bias != nullptr && p.bias_sb == 0 && p.B > 1) ? 1 : 0;
   tm.reverse_q = p.causal ? 1 : 0;
+  tm.n_split = 1;
+  if (p.n_split > 1) {
+    tm.n_split = p.n_split;
+    const int64_t all = total * p.n_split;
+    tm.total = (int)all;
+    tm.per_xcd = (int)((all + 7) / 8);
+    tm.batch_inner = 0;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (d == 128) return (int)launch_d<128, 8>(p, tm, s);
-  if (d == 64) return waves == 4 ? (int)launch_d<64, 4>(p, tm, s) : (int)launch_d<64, 8>(p, tm, s);
-  return (int)hipErrorInvalidValue;
+  return p.n_split > 1 ? (int)launch_dw<true>(p, tm, d, waves, s) : (int)launch_dw<false>(p, tm, d, waves, s);
 }
 
 }  // namespace attn

@@ -233,7 +233,7 @@ hipError_t launch_d(const FwdParams& p, const TileMap& tm, hipStream_t s) {
 }  // namespace
 
 int launch_fwd_f32(const FwdParams& p, int d, void* stream) {
-  TileMap tm;
+  TileMap tm{};
   tm.n_qtiles = (p.Nq + kBr - 1) / kBr;
   const int64_t total = (int64_t)p.B * p.H * tm.n_qtiles;
   tm.total = (int)total;

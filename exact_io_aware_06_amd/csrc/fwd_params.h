@@ -28,6 +28,17 @@ struct FwdParams {
   int32_t causal;
   int32_t bias_vec;          // 1: every bias row start is 16-byte aligned
   float scale_log2;          // scale * log2(e): scores go to base-2 units
+
+  // Split over keys (flash-decoding). n_split == 1: each workgroup covers all
+  // keys of its query tile and writes o / lse. n_split > 1: a workgroup
+  // covers keys [s * kv_split, (s + 1) * kv_split) of one split s and writes
+  // its normalised partial output and log-sum-exp (natural log) to
+  // part_o[s][b][h][i][:] and part_lse[s][b][h][i] (fp32, contiguous);
+  // the combine kernel then merges the splits into o / lse.
+  int32_t kv_split;          // keys per split, a multiple of 64
+  int32_t n_split;
+  float* part_o;             // [n_split, B, H, Nq, d]
+  float* part_lse;           // [n_split, B, H, Nq]
 };
 
 // How the flat workgroup index maps onto (batch, head, query tile).
@@ -37,10 +48,15 @@ struct TileMap {
   int32_t per_xcd;       // ceil(total / 8)
   int32_t batch_inner;   // 1: batch index varies fastest (shared bias reuse)
   int32_t reverse_q;     // 1: longest query tiles first (causal)
+  int32_t n_split;       // key splits per query tile (1: no split)
 };
 
 // Host-side launchers (one per kernel family). Return a hipError_t value.
 int launch_fwd_bf16(const FwdParams& p, int d, void* stream);
 int launch_fwd_f32(const FwdParams& p, int d, void* stream);
+// Merge of the n_split partial results of a split launch into o / lse (bf16 o).
+int launch_combine_bf16(const FwdParams& p, int d, void* stream);
+// Query rows per workgroup of the bf16 forward (split: a split-key launch).
+int fwd_bf16_rows(int d, int64_t nq, bool causal, bool bias, bool split);
 
 }  // namespace attn

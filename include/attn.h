@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 1
+#define ATTN_ABI_VERSION 2
 
 typedef enum {
   ATTN_OK = 0,
@@ -116,6 +116,70 @@ attn_status_t attn_fwd(const attn_tensor_t* q, const attn_tensor_t* k,
                        const attn_tensor_t* v, const attn_mask_t* bias_or_mask,
                        int causal, float scale, const attn_tensor_t* o,
                        const attn_tensor_t* lse, void* stream);
+
+/*
+ * Split-key forward (flash-decoding).
+ *
+ * Same function and outputs as attn_fwd, for shapes with few query rows per
+ * (batch, head) - decoding, Nq = 1 - where one workgroup per query tile
+ * leaves most compute units idle. The keys are cut into splits of whole
+ * 64-key tiles; each workgroup computes one query tile against one split and
+ * writes that split's normalised output O_s and log-sum-exp LSE_s (fp32) to
+ * the workspace; a second kernel merges the splits with the log-sum-exp
+ * identity of the blockwise softmax:
+ *
+ *     M = max_s LSE_s,  w_s = exp(LSE_s - M),
+ *     O = sum_s w_s O_s / sum_s w_s,  LSE = M + log(sum_s w_s).
+ *
+ * Definitions followed: "Understanding FlashAttention Pt 1: Personal Notes",
+ * section 2.4 (merging two softmax blocks); "FlashAttention: Mathematical
+ * Foundations, Online Softmax Tiling, IO-Awareness, and Exact Attention
+ * Scaling", section 7 (flash-decoding: split the keys, reduce with the LSE);
+ * "FlashAttention, Explained", section 25.
+ */
+
+/* Bytes of workspace attn_fwd_splitkv needs for num_splits splits of a
+   [B, H, Nq, d] problem: num_splits * B * H * Nq * (d + 1) * 4. Returns -1
+   for a negative extent, num_splits outside [1, 1024] or d above 1024. */
+int64_t attn_fwd_splitkv_workspace_size(int64_t B, int64_t H, int64_t Nq, int64_t d,
+                                        int32_t num_splits);
+
+/* A split count for this shape on MI355X: enough splits for about two rounds
+   of workgroups on its 256 compute units, with at least 256 keys per split,
+   at most 1024. Returns 1 (no split) when splitting does not help or the
+   shape is empty or unsupported. A host-only computation. */
+int32_t attn_fwd_splitkv_num_splits(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                                    int causal, int has_bias);
+
+/*
+ * attn_fwd_splitkv - enqueue the split-key forward on `stream`.
+ *
+ * Arguments q, k, v, bias_or_mask, causal, scale, o, lse and stream are as
+ * for attn_fwd, with the same checks, except that only bf16 is supported.
+ *
+ *   num_splits       requested number of splits, in [1, 1024]. The keys are
+ *                    cut into ceil(Nk / S) splits of S keys, S =
+ *                    ceil(Nk / num_splits) rounded up to a multiple of 64, so
+ *                    fewer splits may be used. With one split the call is
+ *                    exactly attn_fwd and the workspace is not touched.
+ *   workspace        DEVICE pointer, 16-byte aligned, owned by the caller,
+ *                    used as scratch by the two kernels of this call: its
+ *                    contents on entry are ignored and on return undefined.
+ *                    It must not overlap any tensor of the call, and calls
+ *                    that run concurrently need distinct workspaces.
+ *   workspace_bytes  at least attn_fwd_splitkv_workspace_size(B, H, Nq, d,
+ *                    num_splits) (checked against the split count used).
+ *
+ * Enqueues two kernels (the split forward, then the merge) and returns; the
+ * error behaviour is that of attn_fwd. Results agree with attn_fwd up to
+ * rounding: the splits' outputs are kept in fp32 and rounded to bf16 once,
+ * after the merge.
+ */
+attn_status_t attn_fwd_splitkv(const attn_tensor_t* q, const attn_tensor_t* k,
+                               const attn_tensor_t* v, const attn_mask_t* bias_or_mask,
+                               int causal, float scale, int32_t num_splits, void* workspace,
+                               int64_t workspace_bytes, const attn_tensor_t* o,
+                               const attn_tensor_t* lse, void* stream);
 
 /* Text describing the last non-OK status returned on the calling thread
    ("" if none). The pointer stays valid until the next call on this thread. */

@@ -33,7 +33,9 @@ def _declared_functions():
 def test_exports_every_declared_function():
     lib = _lib()
     names = _declared_functions()
-    assert names == ["attn_abi_version", "attn_fwd", "attn_last_error"]
+    assert names == ["attn_abi_version", "attn_fwd", "attn_fwd_splitkv",
+                     "attn_fwd_splitkv_num_splits", "attn_fwd_splitkv_workspace_size",
+                     "attn_last_error"]
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", ea.library_path()],
@@ -198,3 +200,67 @@ def test_no_undefined_kernel_symbols():
                          capture_output=True, text=True, check=True).stdout
     missing = [ln for ln in out.splitlines() if "attn" in ln]
     assert not missing, missing
+
+
+# ------------------------------------------------------------ split-key entry points
+
+def test_splitkv_workspace_size():
+    ws = ea.splitkv_workspace_size
+    # [num_splits, B, H, Nq, d] partial outputs + [num_splits, B, H, Nq] LSEs, fp32
+    assert ws(2, 3, 5, 128, 4) == 4 * 2 * 3 * 5 * 129 * 4
+    assert ws(8, 32, 1, 64, 1) == 8 * 32 * 65 * 4
+    assert ws(0, 3, 5, 128, 4) == 0
+    for bad in [(2, 3, 5, 128, 0), (2, 3, 5, 128, 1025), (-1, 3, 5, 128, 2), (2, 3, 5, 2048, 2)]:
+        assert ws(*bad) == -1, bad
+
+
+def test_splitkv_num_splits_choice():
+    n = ea.splitkv_num_splits
+    # decoding: 8 x 32 single-row tiles -> 4 splits make 1024 workgroups
+    assert n(8, 32, 1, 16384, 128) == 4
+    # one sequence, 32 heads, 64K keys: 32 splits of 2048 keys
+    assert n(1, 32, 1, 65536, 128) == 32
+    # every split keeps at least 256 keys
+    assert n(1, 1, 1, 1000, 128) == 3
+    assert n(1, 1, 1, 200, 64) == 1
+    # enough query tiles already: no split
+    assert n(2, 32, 4096, 4096, 128) == 1
+    # empty or unsupported shapes: no split
+    assert n(0, 32, 1, 4096, 128) == 1 and n(1, 1, 1, 4096, 96) == 1
+    assert 1 <= n(1, 1, 1, 1 << 30, 128) <= 1024
+
+
+def _split_call(num_splits=4, workspace=0x70000, ws_bytes=1 << 30, dtype=ea.ATTN_BF16,
+                shape=(2, 4, 1, 64), nk=1024):
+    B, H, Nq, d = shape
+    q = _desc((B, H, Nq, d), dtype)
+    k = _desc((B, H, nk, d), dtype, data=0x20000)
+    v = _desc((B, H, nk, d), dtype, data=0x30000)
+    o = _desc((B, H, Nq, d), dtype, data=0x40000)
+    lse = _desc((B, H, Nq, 1), ea.ATTN_F32, data=0x50000, stride=[H * Nq, Nq, 1, 1])
+    _lib()
+    return ea.attn_fwd_splitkv_raw(q, k, v, None, 0, 0.125, num_splits, workspace, ws_bytes,
+                                   o, lse, 0)
+
+
+def test_splitkv_rejections():
+    # every call below needs more than one split, so it is refused before
+    # any kernel could be enqueued
+    assert _split_call(num_splits=0) == ea.ATTN_ERR_INVALID
+    assert "num_splits" in ea.last_error()
+    assert _split_call(num_splits=1025) == ea.ATTN_ERR_INVALID
+    assert _split_call(dtype=ea.ATTN_F32) == ea.ATTN_ERR_UNSUPPORTED
+    assert "bf16" in ea.last_error()
+    assert _split_call(workspace=0) == ea.ATTN_ERR_INVALID
+    assert "workspace" in ea.last_error()
+    assert _split_call(workspace=0x70008) == ea.ATTN_ERR_INVALID
+    need = ea.splitkv_workspace_size(2, 4, 1, 64, 4)
+    assert _split_call(ws_bytes=need - 1) == ea.ATTN_ERR_INVALID
+    assert "too small" in ea.last_error()
+    # the check is against the split count actually used: 1024 keys in
+    # requested 7 splits -> splits of 192 keys -> 6 splits
+    need6 = ea.splitkv_workspace_size(2, 4, 1, 64, 6)
+    assert _split_call(num_splits=7, ws_bytes=need6 - 4) == ea.ATTN_ERR_INVALID
+    assert "6 splits" in ea.last_error()
+    # the common argument checks still apply
+    assert _split_call(shape=(2, 4, 1, 96)) == ea.ATTN_ERR_UNSUPPORTED

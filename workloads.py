@@ -14,6 +14,11 @@ Recipe (fixed here, stated again in the design notes):
 * The bias, when present, is float32 with standard deviation ``bias_std``,
   shaped [1, H, Nq, Nk] so that it is shared by every batch entry.
 * Key lengths are integers drawn uniformly from [kv_len_lo, kv_len_hi].
+* Grouped key/value heads (``Hk`` set): K and V are drawn with Hk heads.
+* Decoding workloads: one query row per (batch, head) against a long key
+  sequence (the pages give no decode shape; these are typical serving ones:
+  batch 8 at 16K keys, and one sequence at 64K keys, the length up to which
+  the pages report near-constant decode latency).
 """
 
 from __future__ import annotations
@@ -41,6 +46,11 @@ class Workload:
     bias_std: Optional[float] = None        # dense bias [1, H, Nq, Nk] if set
     kv_len_range: Optional[tuple] = None    # (lo, hi) inclusive integer range
     seed: int = 0
+    Hk: Optional[int] = None                # key/value heads (None: H)
+
+    @property
+    def kv_heads(self) -> int:
+        return self.H if self.Hk is None else self.Hk
 
     @property
     def softmax_scale(self) -> float:
@@ -59,8 +69,13 @@ class Workload:
             "workload": self.name, "B": self.B, "H": self.H, "Nq": self.Nq,
             "Nk": self.Nk, "d": self.d, "dtype": self.dtype,
             "causal": self.causal, "scale": self.softmax_scale,
-            "seed": self.seed,
+            "seed": self.seed, **({} if self.Hk is None else {"Hk": self.Hk}),
         }
+
+    def kv_bytes(self) -> int:
+        """Bytes of K and V (each read once by a split-key forward)."""
+        eb = 4 if self.dtype == "f32" else 2
+        return 2 * self.B * self.kv_heads * self.Nk * self.d * eb
 
 
 # The five workloads the method is measured on (seeds follow the config index).
@@ -85,6 +100,18 @@ CONFIGS = {
 
 HEADLINE = "c3_bf16_d128"
 
+# Decoding (one query row per head) for the split-key forward.
+DECODE = {
+    "decode_b8_h32_k16k_d128": Workload("decode_b8_h32_k16k_d128", 8, 32, 1, 16384, 128,
+                                        seed=6),
+    "decode_gqa_b8_h32_hk8_k16k_d128": Workload("decode_gqa_b8_h32_hk8_k16k_d128", 8, 32, 1,
+                                                16384, 128, Hk=8, seed=6),
+    "decode_b1_h32_k64k_d128": Workload("decode_b1_h32_k64k_d128", 1, 32, 1, 65536, 128,
+                                        seed=7),
+}
+
+ALL = {**CONFIGS, **DECODE}
+
 
 def _storage(dtype: str):
     if dtype == "bf16":
@@ -104,8 +131,8 @@ def make_inputs(w: Workload, seed: Optional[int] = None) -> dict:
     g = torch.Generator().manual_seed(w.seed if seed is None else int(seed))
     st = _storage(w.dtype)
     q = torch.randn((w.B, w.H, w.Nq, w.d), generator=g, dtype=torch.float32)
-    k = torch.randn((w.B, w.H, w.Nk, w.d), generator=g, dtype=torch.float32)
-    v = torch.randn((w.B, w.H, w.Nk, w.d), generator=g, dtype=torch.float32)
+    k = torch.randn((w.B, w.kv_heads, w.Nk, w.d), generator=g, dtype=torch.float32)
+    v = torch.randn((w.B, w.kv_heads, w.Nk, w.d), generator=g, dtype=torch.float32)
     if w.value_scale != 1.0:
         q.mul_(w.value_scale)
         k.mul_(w.value_scale)
@@ -134,4 +161,4 @@ def make_inputs(w: Workload, seed: Optional[int] = None) -> dict:
 def small(name: str, **overrides) -> Workload:
     """A reduced copy of a named workload (same dtype, masks and value
     distribution) for checks the oracle can evaluate in full."""
-    return CONFIGS[name].with_(**overrides)
+    return ALL[name].with_(**overrides)
