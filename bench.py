@@ -125,11 +125,19 @@ def main(argv=None):
         n = args.copy_calibration * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
         for _ in range(max(args.steps, 1)):
             dst.copy_(src)
+        stop.record()
         torch.cuda.synchronize()
+        ms = start.elapsed_time(stop) / max(args.steps, 1)
+        # the HBM rate a plain device-to-device copy sustains (read + write)
         print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4,
-                          "launches": max(args.steps, 1)}), flush=True)
+                          "launches": max(args.steps, 1) + 1, "ms": round(ms, 4),
+                          "gbps": round(2 * n * 4 / (ms * 1e-3) / 1e9, 1)}), flush=True)
         return 0
 
     if args.gemm_calibration:
@@ -164,7 +172,7 @@ def main(argv=None):
     n_split = None
     if split:
         n_split = args.splits or ea.splitkv_num_splits(w.B, w.H, w.Nq, w.Nk, w.d, w.causal,
-                                                       bias is not None)
+                                                       bias is not None, w.kv_heads)
     # arguments marshalled once: a step is the launch(es) alone
     step, _, _ = ea.prepare_call(q, k, v, bias=bias, kv_len=kv_len, causal=w.causal,
                                  scale=inp["scale"], out=o, lse=lse, split=split,

@@ -77,7 +77,7 @@ def load_library():
     lib.attn_fwd_splitkv.restype = ctypes.c_int
     lib.attn_fwd_splitkv_workspace_size.argtypes = [ctypes.c_int64] * 4 + [ctypes.c_int32]
     lib.attn_fwd_splitkv_workspace_size.restype = ctypes.c_int64
-    lib.attn_fwd_splitkv_num_splits.argtypes = [ctypes.c_int64] * 5 + [ctypes.c_int] * 2
+    lib.attn_fwd_splitkv_num_splits.argtypes = [ctypes.c_int64] * 6 + [ctypes.c_int] * 2
     lib.attn_fwd_splitkv_num_splits.restype = ctypes.c_int32
     lib.attn_last_error.argtypes = []
     lib.attn_last_error.restype = ctypes.c_char_p
@@ -127,10 +127,11 @@ def splitkv_workspace_size(B: int, H: int, Nq: int, d: int, num_splits: int) -> 
 
 
 def splitkv_num_splits(B: int, H: int, Nq: int, Nk: int, d: int, causal: bool = False,
-                       has_bias: bool = False) -> int:
-    """The library's split count for this shape (1: no split)."""
+                       has_bias: bool = False, Hk: Optional[int] = None) -> int:
+    """The library's split count for this shape (1: no split); Hk: key/value
+    heads (default H)."""
     return int(load_library().attn_fwd_splitkv_num_splits(
-        B, H, Nq, Nk, d, 1 if causal else 0, 1 if has_bias else 0))
+        B, H, H if Hk is None else Hk, Nq, Nk, d, 1 if causal else 0, 1 if has_bias else 0))
 
 
 def last_error() -> str:
@@ -199,7 +200,7 @@ def attn_fwd_splitkv(q, k, v, bias=None, kv_len=None, causal: bool = False,
     B, H, Nq, d = q.shape
     Nk = k.shape[2]
     if num_splits is None:
-        num_splits = splitkv_num_splits(B, H, Nq, Nk, d, causal, bias is not None)
+        num_splits = splitkv_num_splits(B, H, Nq, Nk, d, causal, bias is not None, k.shape[1])
     scale, out, lse, (qd, kd, vd, od, ld, mask, _keep) = _prepare(q, k, v, bias, kv_len, scale,
                                                                     out, lse)
     need = splitkv_workspace_size(B, H, Nq, d, num_splits)
@@ -241,7 +242,8 @@ def prepare_call(q, k, v, bias=None, kv_len=None, causal: bool = False,
             float(scale)]
     if split:
         if num_splits is None:
-            num_splits = splitkv_num_splits(B, H, Nq, k.shape[2], d, causal, bias is not None)
+            num_splits = splitkv_num_splits(B, H, Nq, k.shape[2], d, causal, bias is not None,
+                                            k.shape[1])
         need = splitkv_workspace_size(B, H, Nq, d, num_splits)
         if need < 0:
             raise AttnError(ATTN_ERR_INVALID, f"invalid split count {num_splits} for this shape")

@@ -186,6 +186,7 @@ attn_status_t prepare(const attn_tensor_t* q, const attn_tensor_t* k, const attn
   p.bias_vec = bias_vec ? 1 : 0;
   p.scale_log2 = scale * 1.44269504088896341f;
   p.n_split = 1;
+  p.pack = 1;
 
   // grid size: 8 * ceil(B*H*ceil(Nq/16)/8) workgroups at most (f32 tiles are smallest)
   const int64_t tiles = B * H * ((Nq + 15) / 16);
@@ -239,15 +240,19 @@ int64_t attn_fwd_splitkv_workspace_size(int64_t B, int64_t H, int64_t Nq, int64_
   return (int64_t)num_splits * B * H * Nq * (d + 1) * 4;
 }
 
-int32_t attn_fwd_splitkv_num_splits(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
-                                    int causal, int has_bias) {
-  if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || (d != 64 && d != 128)) return 1;
+int32_t attn_fwd_splitkv_num_splits(int64_t B, int64_t H, int64_t Hk, int64_t Nq, int64_t Nk,
+                                    int64_t d, int causal, int has_bias) {
+  if (B <= 0 || H <= 0 || Hk <= 0 || H % Hk != 0 || Nq <= 0 || Nk <= 0 || (d != 64 && d != 128))
+    return 1;
   // Workgroups without a split, against the 512 that MI355X runs at once
-  // (256 CUs, two workgroups each); aim for two full waves of workgroups,
-  // with at least 256 keys (four tiles) per split.
-  const int64_t rows = attn::fwd_bf16_rows((int)d, Nq, causal != 0, has_bias != 0, true);
-  const int64_t wgs = B * H * ((Nq + rows - 1) / rows);
-  constexpr int64_t kTarget = 1024;
+  // (256 CUs, two workgroups each): aim for one full round of workgroups,
+  // with at least 256 keys (four tiles) per split. (Measured on the decoding
+  // workloads: one round beats two; fewer splits leave CUs idle.)
+  const int pack = attn::fwd_bf16_pack(H / Hk, Nq);
+  const int64_t nrows = pack * Nq;
+  const int64_t rows = attn::fwd_bf16_rows((int)d, nrows, causal != 0, has_bias != 0, true);
+  const int64_t wgs = B * (H / pack) * ((nrows + rows - 1) / rows);
+  constexpr int64_t kTarget = 512;
   int64_t n = (kTarget + wgs - 1) / wgs;
   n = std::min<int64_t>(n, std::max<int64_t>(1, Nk / 256));
   n = std::min<int64_t>(n, kMaxSplits);
@@ -281,13 +286,16 @@ attn_status_t attn_fwd_splitkv(const attn_tensor_t* q, const attn_tensor_t* k,
   if (workspace_bytes < need)
     return fail(ATTN_ERR_INVALID, "workspace of %lld bytes is too small (%lld needed for %lld splits)",
                 (long long)workspace_bytes, (long long)need, (long long)n_split);
-  const int rows = attn::fwd_bf16_rows(d, p.Nq, p.causal != 0, p.bias != nullptr, true);
-  const int64_t wgs = (int64_t)p.B * p.H * ((p.Nq + rows - 1) / rows) * n_split;
+  const int pack = attn::fwd_bf16_pack(p.head_group, p.Nq);
+  const int64_t nrows = (int64_t)pack * p.Nq;
+  const int rows = attn::fwd_bf16_rows(d, nrows, p.causal != 0, p.bias != nullptr, true);
+  const int64_t wgs = (int64_t)p.B * (p.H / pack) * ((nrows + rows - 1) / rows) * n_split;
   if (wgs > ((int64_t)1 << 31) - 64 || (int64_t)p.B * p.H * p.Nq > ((int64_t)1 << 32))
     return fail(ATTN_ERR_UNSUPPORTED, "problem needs more than 2^31 workgroups");
 
   p.kv_split = (int32_t)kv_split;
   p.n_split = (int32_t)n_split;
+  p.pack = pack;
   p.part_o = static_cast<float*>(workspace);
   p.part_lse = p.part_o + n_split * (int64_t)p.B * p.H * p.Nq * d;
   int rc = attn::launch_fwd_bf16(p, d, stream);

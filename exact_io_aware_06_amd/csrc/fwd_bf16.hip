@@ -205,21 +205,22 @@ __global__ __launch_bounds__(64 * W, 2) void fwd_bf16_kernel(FwdParams p, TileMa
   constexpr int kBr = G::kBr;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
+  // packed: the query heads of one key/value head share the workgroup's rows
+  const bool packed = SPLIT && p.pack > 1;
   int b, h, qt, split;
-  if (!decode_tile<SPLIT>(tm, p.B, p.H, b, h, qt, split)) return;
+  if (!decode_tile<SPLIT>(tm, p.B, packed ? p.Hk : p.H, b, h, qt, split)) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: kept in SGPRs
   const int l32 = lane & 31;
   const int hi = lane >> 5;
-  const int hk = h / p.head_group;
+  const int hk = packed ? h : h / p.head_group;
 
   // Split over keys: this workgroup covers keys [kbeg, kbeg + kv_split) of
   // its rows. Key indices below are relative to kbeg (the K/V and bias base
   // addresses, the key count and the causal offset are shifted by it).
   const int kbeg = SPLIT ? split * p.kv_split : 0;
-  const __bf16* qg = static_cast<const __bf16*>(p.q) + b * p.q_sb + h * p.q_sh;
   const __bf16* kgp = static_cast<const __bf16*>(p.k) + b * p.k_sb + hk * p.k_sh + (int64_t)kbeg * p.k_sn;
   const __bf16* vgp = static_cast<const __bf16*>(p.v) + b * p.v_sb + hk * p.v_sh + (int64_t)kbeg * p.v_sn;
 
@@ -227,22 +228,39 @@ __global__ __launch_bounds__(64 * W, 2) void fwd_bf16_kernel(FwdParams p, TileMa
   const int Nk = p.Nk - kbeg;  // keys from kbeg on
   const int q0 = qt * kBr;
   const int qw0 = q0 + wave * 32;
-  const int my_q = qw0 + l32;
+  const int my_q = qw0 + l32;   // this lane's row of the workgroup's row space
   const int off = p.Nk - Nq - kbeg;  // causal alignment: key j hidden when j > i + off
+
+  // Row r of the row space is query r of head h, or, packed, query r % Nq
+  // of query head h * pack + r / Nq. row_i: this lane's query index;
+  // qmin_w: the smallest query index of the wave's rows; qend: one past the
+  // largest of the workgroup's rows (both bound the causal mask).
+  int row_h = h, row_i = my_q, nrows = Nq, qmin_w = qw0, qend = min(q0 + kBr, Nq);
+  if (packed) {
+    nrows = p.pack * Nq;
+    const int rr = min(my_q, nrows - 1);
+    row_h = h * p.pack + rr / Nq;
+    row_i = rr % Nq;
+    const int wl = min(qw0 + 31, nrows - 1), gl = min(q0 + kBr - 1, nrows - 1);
+    qmin_w = (qw0 / Nq == wl / Nq) ? qw0 % Nq : 0;
+    qend = (q0 / Nq == gl / Nq) ? gl % Nq + 1 : Nq;
+  }
+  const bool row_live = my_q < nrows;
+  const __bf16* qg = static_cast<const __bf16*>(p.q) + b * p.q_sb + row_h * p.q_sh;
 
   int kend = Nk;
   if (p.kv_len != nullptr) kend = min(max(p.kv_len[b] - kbeg, 0), Nk);
   if (SPLIT) kend = min(kend, p.kv_split);
   int wg_keys = kend;
-  if (CAUSAL) wg_keys = min(kend, min(q0 + kBr, Nq) + off);
+  if (CAUSAL) wg_keys = min(kend, qend + off);
   wg_keys = max(wg_keys, 0);
   const int nt = (wg_keys + kBc - 1) / kBc;
 
   // ---- Q as the B operand, resident for the whole loop: lane holds query
-  // my_q, elements [16kk + 8hi, 16kk + 8hi + 8).
+  // row_i, elements [16kk + 8hi, 16kk + 8hi + 8).
   bf16x8 qf[G::kNkk];
-  if (my_q < Nq) {
-    const __bf16* qrow = qg + (int64_t)my_q * p.q_sn + 8 * hi;
+  if (row_live) {
+    const __bf16* qrow = qg + (int64_t)row_i * p.q_sn + 8 * hi;
 #pragma unroll
     for (int kk = 0; kk < G::kNkk; ++kk)
       qf[kk] = *reinterpret_cast<const bf16x8*>(qrow + 16 * kk);
@@ -354,8 +372,8 @@ __global__ __launch_bounds__(64 * W, 2) void fwd_bf16_kernel(FwdParams p, TileMa
 
   const float* brow = nullptr;
   if (HAS_BIAS) {
-    const int qrow = min(my_q, Nq - 1);
-    brow = p.bias + b * p.bias_sb + h * p.bias_sh + (int64_t)qrow * p.bias_sn + kbeg + 8 * hi;
+    const int qrow = min(row_i, Nq - 1);
+    brow = p.bias + b * p.bias_sb + row_h * p.bias_sh + (int64_t)qrow * p.bias_sn + kbeg + 8 * hi;
   }
 
   // Bias and masks of tile j. Register r of block bb holds key
@@ -389,9 +407,9 @@ __global__ __launch_bounds__(64 * W, 2) void fwd_bf16_kernel(FwdParams p, TileMa
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[bb][r] = __builtin_fmaf(s[bb][r], c2, bia[bb][r] * kLog2e);
     }
-    const bool need_mask = (kv0 + kBc > kend) || (CAUSAL && kv0 + kBc - 1 > qw0 + off);
+    const bool need_mask = (kv0 + kBc > kend) || (CAUSAL && kv0 + kBc - 1 > qmin_w + off);
     if (need_mask) {
-      const int lim_c = my_q + off;  // last key this query may see (causal)
+      const int lim_c = row_i + off;  // last key this query may see (causal)
 #pragma unroll
       for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
@@ -581,9 +599,9 @@ __global__ __launch_bounds__(64 * W, 2) void fwd_bf16_kernel(FwdParams p, TileMa
     wait_tiles();
     __syncthreads();
     qk_plain(klane, sa);
-    // iteration 0 overwrites K buffer 0 with K_2: every wave must be done
-    // reading K_0 first
-    if (nt > 2) __syncthreads();
+    // iteration 0 overwrites K buffer 0 (with K_2, or with K_1 again when
+    // there are two tiles): every wave must be done reading K_0 first
+    if (nt > 1) __syncthreads();
     mask_bias(0, sa);
     m_run = tile_max(sa);
     int j = 0;
@@ -601,11 +619,12 @@ __global__ __launch_bounds__(64 * W, 2) void fwd_bf16_kernel(FwdParams p, TileMa
 
   // ---- epilogue: one division per row, O and LSE written once
   const float l_tot = lane_pair_sum(l_run);
-  if (SPLIT && my_q < Nq) {
+  if constexpr (SPLIT) {
+    if (!row_live) return;
     // one split of the keys: its normalised output and log-sum-exp in fp32,
     // merged with the other splits by the combine kernel
     const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
-    const int64_t row = (((int64_t)split * p.B + b) * p.H + h) * Nq + my_q;
+    const int64_t row = (((int64_t)split * p.B + b) * p.H + row_h) * Nq + row_i;
     float* orow = p.part_o + row * D;
 #pragma unroll
     for (int cb = 0; cb < G::kNcb; ++cb)
@@ -618,7 +637,7 @@ __global__ __launch_bounds__(64 * W, 2) void fwd_bf16_kernel(FwdParams p, TileMa
       }
     if (hi == 0)
       p.part_lse[row] = (l_tot > 0.f) ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
-  } else if (my_q < Nq) {
+  } else if (my_q < Nq) {  // not split: the final result
     const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
     __bf16* orow = static_cast<__bf16*>(p.o) + b * p.o_sb + h * p.o_sh + (int64_t)my_q * p.o_sn;
     // register r of block cb holds column 32cb + 8(r/4) + 4hi + (r%4)
@@ -676,7 +695,13 @@ hipError_t launch_dw(const FwdParams& p, const TileMap& tm, int d, int waves, hi
 
 }  // namespace
 
-int fwd_bf16_rows(int d, int64_t nq, bool causal, bool bias, bool split) {
+int fwd_bf16_pack(int64_t head_group, int64_t nq) {
+  // decoding-sized query counts only: with many rows per head the packed
+  // row space would also blur the causal tile skipping
+  return (head_group > 1 && nq <= 64) ? (int)head_group : 1;
+}
+
+int fwd_bf16_rows(int d, int64_t nrows, bool causal, bool bias, bool split) {
   // d = 64 with a causal mask or a bias: 4-wave (128-row) workgroups, so
   // that two run on a CU at once and the uneven per-workgroup work (diagonal
   // tiles, per-batch key lengths) is spread more finely. A split launch with
@@ -684,16 +709,19 @@ int fwd_bf16_rows(int d, int64_t nq, bool causal, bool bias, bool split) {
   // are wasted matrix work, and 4-wave workgroups put half as much of it on
   // each SIMD. Otherwise 8 waves.
   if (d == 64 && (causal || bias)) return 128;
-  if (split && nq <= 128) return 128;
+  if (split && nrows <= 128) return 128;
   return 256;
 }
 
 int launch_fwd_bf16(const FwdParams& p, int d, void* stream) {
-  const int br = fwd_bf16_rows(d, p.Nq, p.causal != 0, p.bias != nullptr, p.n_split > 1);
+  const bool split = p.n_split > 1;
+  const bool packed = split && p.pack > 1;
+  const int64_t nrows = packed ? (int64_t)p.pack * p.Nq : p.Nq;
+  const int br = fwd_bf16_rows(d, nrows, p.causal != 0, p.bias != nullptr, split);
   const int waves = br / 32;
   TileMap tm;
-  tm.n_qtiles = (p.Nq + br - 1) / br;
-  const int64_t total = (int64_t)p.B * p.H * tm.n_qtiles;
+  tm.n_qtiles = (int)((nrows + br - 1) / br);
+  const int64_t total = (int64_t)p.B * (packed ? p.Hk : p.H) * tm.n_qtiles;
   tm.total = (int)total;
   tm.per_xcd = (int)((total + 7) / 8);
   tm.batch_inner = (p.bias != nullptr && p.bias_sb == 0 && p.B > 1) ? 1 : 0;
@@ -707,7 +735,7 @@ int launch_fwd_bf16(const FwdParams& p, int d, void* stream) {
     tm.batch_inner = 0;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return p.n_split > 1 ? (int)launch_dw<true>(p, tm, d, waves, s) : (int)launch_dw<false>(p, tm, d, waves, s);
+  return split ? (int)launch_dw<true>(p, tm, d, waves, s) : (int)launch_dw<false>(p, tm, d, waves, s);
 }
 
 }  // namespace attn

@@ -39,6 +39,11 @@ struct FwdParams {
   int32_t n_split;
   float* part_o;             // [n_split, B, H, Nq, d]
   float* part_lse;           // [n_split, B, H, Nq]
+  // Split launches only: > 1 packs the `pack` (= H / Hk) query heads that
+  // share a key/value head into one row space of pack * Nq rows per
+  // (batch, key/value head), so each workgroup reads K/V once for all of
+  // them. 1: one row space of Nq rows per query head.
+  int32_t pack;
 };
 
 // How the flat workgroup index maps onto (batch, head, query tile).
@@ -56,7 +61,10 @@ int launch_fwd_bf16(const FwdParams& p, int d, void* stream);
 int launch_fwd_f32(const FwdParams& p, int d, void* stream);
 // Merge of the n_split partial results of a split launch into o / lse (bf16 o).
 int launch_combine_bf16(const FwdParams& p, int d, void* stream);
-// Query rows per workgroup of the bf16 forward (split: a split-key launch).
-int fwd_bf16_rows(int d, int64_t nq, bool causal, bool bias, bool split);
+// Query rows per workgroup of the bf16 forward. nrows: rows of one row
+// space (Nq, or pack * Nq when heads are packed); split: a split-key launch.
+int fwd_bf16_rows(int d, int64_t nrows, bool causal, bool bias, bool split);
+// Heads packed per row space for a split launch (1: none).
+int fwd_bf16_pack(int64_t head_group, int64_t nq);
 
 }  // namespace attn

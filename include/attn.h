@@ -144,12 +144,13 @@ attn_status_t attn_fwd(const attn_tensor_t* q, const attn_tensor_t* k,
 int64_t attn_fwd_splitkv_workspace_size(int64_t B, int64_t H, int64_t Nq, int64_t d,
                                         int32_t num_splits);
 
-/* A split count for this shape on MI355X: enough splits for about two rounds
-   of workgroups on its 256 compute units, with at least 256 keys per split,
-   at most 1024. Returns 1 (no split) when splitting does not help or the
-   shape is empty or unsupported. A host-only computation. */
-int32_t attn_fwd_splitkv_num_splits(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
-                                    int causal, int has_bias);
+/* A split count for this shape on MI355X (H query heads, Hk key/value
+   heads): enough splits for one round of workgroups on its 256 compute
+   units (two per unit), with at least 256 keys per split, at most 1024. Returns 1
+   (no split) when splitting does not help or the shape is empty or
+   unsupported. A host-only computation. */
+int32_t attn_fwd_splitkv_num_splits(int64_t B, int64_t H, int64_t Hk, int64_t Nq, int64_t Nk,
+                                    int64_t d, int causal, int has_bias);
 
 /*
  * attn_fwd_splitkv - enqueue the split-key forward on `stream`.
@@ -169,6 +170,10 @@ int32_t attn_fwd_splitkv_num_splits(int64_t B, int64_t H, int64_t Nq, int64_t Nk
  *                    that run concurrently need distinct workspaces.
  *   workspace_bytes  at least attn_fwd_splitkv_workspace_size(B, H, Nq, d,
  *                    num_splits) (checked against the split count used).
+ *
+ * With grouped key/value heads (Hk < H) and Nq <= 64, the H / Hk query
+ * heads that share a key/value head are computed by the same workgroups, so
+ * K and V are read once per key/value head rather than once per query head.
  *
  * Enqueues two kernels (the split forward, then the merge) and returns; the
  * error behaviour is that of attn_fwd. Results agree with attn_fwd up to

@@ -216,10 +216,15 @@ def test_splitkv_workspace_size():
 
 def test_splitkv_num_splits_choice():
     n = ea.splitkv_num_splits
-    # decoding: 8 x 32 single-row tiles -> 4 splits make 1024 workgroups
-    assert n(8, 32, 1, 16384, 128) == 4
-    # one sequence, 32 heads, 64K keys: 32 splits of 2048 keys
-    assert n(1, 32, 1, 65536, 128) == 32
+    # decoding: 8 x 32 single-row tiles -> 2 splits make 512 workgroups,
+    # one round on 256 CUs
+    assert n(8, 32, 1, 16384, 128) == 2
+    # 8 key/value heads: the 4 query heads of a group share a workgroup, so
+    # there are 64 workgroups per split -> 8 splits
+    assert n(8, 32, 1, 16384, 128, Hk=8) == 8
+    assert n(8, 32, 1, 16384, 128, Hk=5) == 1      # Hk must divide H
+    # one sequence, 32 heads, 64K keys: 16 splits of 4096 keys
+    assert n(1, 32, 1, 65536, 128) == 16
     # every split keeps at least 256 keys
     assert n(1, 1, 1, 1000, 128) == 3
     assert n(1, 1, 1, 200, 64) == 1

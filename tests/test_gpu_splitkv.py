@@ -115,6 +115,27 @@ def test_split_grouped_kv_heads(hk):
     compare(o, lse, ro, rl, "bf16", f"split gqa Hk={hk}")
 
 
+# Packed heads (Nq <= 64, Hk < H): the H / Hk query heads of a key/value head
+# share one row space of (H / Hk) * Nq rows. Row counts that leave a wave or
+# a workgroup spanning two heads check the causal bounds; Nq = 65 is past
+# the packing limit.
+@pytest.mark.parametrize("H,Hk,Nq,d,causal,bias", [
+    (8, 2, 5, 128, True, True),
+    (8, 2, 33, 128, True, False),     # 132 rows: waves straddle heads
+    (4, 1, 64, 64, True, False),      # 256 rows, 8-wave workgroups
+    (16, 2, 3, 64, False, True),      # 24 rows
+    (6, 3, 65, 128, True, False),     # not packed
+])
+def test_split_packed_heads(H, Hk, Nq, d, causal, bias):
+    kv_len = [900, 333]
+    inp = _inputs(2, H, Nq, 900, d, causal=causal, Hk=Hk, bias=bias, seed=27 + Nq,
+                  kv_len=kv_len)
+    _banner(f"split packed H={H} Hk={Hk} Nq={Nq} d={d} causal={causal} bias={bias}")
+    o, lse = run_split(inp, 3)
+    ro, rl = _oracle(inp)
+    compare(o, lse, ro, rl, "bf16", f"split packed H={H} Hk={Hk} Nq={Nq}")
+
+
 def test_split_large_scores_move_reference():
     # scores near +-1e3, and each split's maximum differs widely: the merge
     # weights exp(LSE_s - M) span many orders of magnitude
