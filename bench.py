@@ -57,6 +57,22 @@ def _traffic(workload, dtype):
         return None
 
 
+def window_flops(w):
+    """4 d FLOPs per (query, key) pair inside the sliding window (the band
+    around the bottom-right-aligned diagonal, clipped to the key range)."""
+    import numpy as np
+    left, right = w.window
+    if w.causal:
+        right = 0
+    i = np.arange(w.Nq, dtype=np.int64)
+    diag = i + (w.Nk - w.Nq)
+    lo = np.zeros_like(i) if left is None or left < 0 else np.maximum(diag - left, 0)
+    hi = (np.full_like(i, w.Nk - 1) if right is None or right < 0
+          else np.minimum(diag + right, w.Nk - 1))
+    pairs = int(np.maximum(hi - lo + 1, 0).sum())
+    return 4.0 * w.B * w.H * w.d * pairs
+
+
 def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -80,12 +96,12 @@ def cpu_baseline(inp, w, budget_s=15.0):
         oracle.attention_forward(q[b:b + 1, h:h + 1].double().numpy(),
                                  k[b:b + 1, hk:hk + 1].double().numpy(),
                                  v[b:b + 1, hk:hk + 1].double().numpy(),
-                                 scale=inp["scale"], causal=w.causal)
+                                 scale=inp["scale"], causal=w.causal, window=w.window)
         done += 1
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
-    flops = w.flops() * done / len(heads)
+    flops = (w.flops() if w.window is None else window_flops(w)) * done / len(heads)
     return {
         "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": _blas_threads(),
         "kind": "oracle",
@@ -176,7 +192,7 @@ def main(argv=None):
     # arguments marshalled once: a step is the launch(es) alone
     step, _, _ = ea.prepare_call(q, k, v, bias=bias, kv_len=kv_len, causal=w.causal,
                                  scale=inp["scale"], out=o, lse=lse, split=split,
-                                 num_splits=n_split)
+                                 num_splits=n_split, window=w.window)
 
     for _ in range(args.warmup):
         step()
@@ -191,7 +207,7 @@ def main(argv=None):
     torch.cuda.synchronize()
     ms = start.elapsed_time(stop) / args.steps
 
-    flops = w.flops()
+    flops = w.flops() if w.window is None else window_flops(w)
     tflops = flops / (ms * 1e-3) / 1e12
     extra = {}
     if inp["kv_len"] is not None and not w.causal:

@@ -40,7 +40,9 @@ class AttnTensor(ctypes.Structure):
 
 
 class AttnMask(ctypes.Structure):
-    _fields_ = [("bias", ctypes.POINTER(AttnTensor)), ("kv_len", ctypes.c_void_p)]
+    _fields_ = [("bias", ctypes.POINTER(AttnTensor)), ("kv_len", ctypes.c_void_p),
+                ("window", ctypes.c_int32), ("window_left", ctypes.c_int32),
+                ("window_right", ctypes.c_int32)]
 
 
 class AttnError(RuntimeError):
@@ -151,7 +153,7 @@ def _torch_desc(t, name):
     return make_desc(t.data_ptr(), dt, t.shape, t.stride())
 
 
-def _prepare(q, k, v, bias, kv_len, scale, out, lse):
+def _prepare(q, k, v, bias, kv_len, scale, out, lse, window=None):
     import torch
     if not (q.is_cuda and k.is_cuda and v.is_cuda):
         raise ValueError("q, k and v must be GPU tensors (no CPU path exists)")
@@ -169,8 +171,13 @@ def _prepare(q, k, v, bias, kv_len, scale, out, lse):
     ld = make_desc(lse.data_ptr(), ATTN_F32, (*lse.shape, 1), (*lse.stride(), 1))
     mask = None
     keep = []
-    if bias is not None or kv_len is not None:
+    if bias is not None or kv_len is not None or window is not None:
         mask = AttnMask()
+        if window is not None:
+            wl, wr = window
+            mask.window = 1
+            mask.window_left = -1 if wl is None else int(wl)
+            mask.window_right = -1 if wr is None else int(wr)
         if bias is not None:
             if bias.dtype != torch.float32 or not bias.is_cuda or bias.dim() != 4:
                 raise ValueError("bias must be a float32 4-D GPU tensor")
@@ -188,7 +195,7 @@ def _prepare(q, k, v, bias, kv_len, scale, out, lse):
 
 def attn_fwd_splitkv(q, k, v, bias=None, kv_len=None, causal: bool = False,
                      scale: Optional[float] = None, num_splits: Optional[int] = None,
-                     workspace=None, out=None, lse=None):
+                     workspace=None, out=None, lse=None, window=None):
     """``attn_fwd`` with the keys split across workgroups (flash-decoding).
 
     Same arguments and result as ``attn_fwd`` (bfloat16 only). num_splits
@@ -202,7 +209,7 @@ def attn_fwd_splitkv(q, k, v, bias=None, kv_len=None, causal: bool = False,
     if num_splits is None:
         num_splits = splitkv_num_splits(B, H, Nq, Nk, d, causal, bias is not None, k.shape[1])
     scale, out, lse, (qd, kd, vd, od, ld, mask, _keep) = _prepare(q, k, v, bias, kv_len, scale,
-                                                                    out, lse)
+                                                                    out, lse, window)
     need = splitkv_workspace_size(B, H, Nq, d, num_splits)
     if need < 0:
         raise AttnError(ATTN_ERR_INVALID, f"invalid split count {num_splits} for this shape")
@@ -222,7 +229,7 @@ def attn_fwd_splitkv(q, k, v, bias=None, kv_len=None, causal: bool = False,
 
 def prepare_call(q, k, v, bias=None, kv_len=None, causal: bool = False,
                  scale: Optional[float] = None, out=None, lse=None, split: bool = False,
-                 num_splits: Optional[int] = None, workspace=None):
+                 num_splits: Optional[int] = None, workspace=None, window=None):
     """Marshal the arguments once; return ``(enqueue, out, lse)``.
 
     ``enqueue()`` launches the forward (``split``: the split-key forward) on
@@ -233,7 +240,7 @@ def prepare_call(q, k, v, bias=None, kv_len=None, causal: bool = False,
     import torch
     B, H, Nq, d = q.shape
     scale, out, lse, (qd, kd, vd, od, ld, mask, keep) = _prepare(q, k, v, bias, kv_len, scale,
-                                                                   out, lse)
+                                                                   out, lse, window)
     lib = load_library()
     stream = torch.cuda.current_stream(q.device).cuda_stream
     refs = (qd, kd, vd, od, ld, mask, keep)
@@ -265,19 +272,22 @@ def prepare_call(q, k, v, bias=None, kv_len=None, causal: bool = False,
 
 
 def attn_fwd(q, k, v, bias=None, kv_len=None, causal: bool = False,
-             scale: Optional[float] = None, out=None, lse=None):
+             scale: Optional[float] = None, out=None, lse=None, window=None):
     """O = softmax_row(scale * Q K^T + bias) V and the row log-sum-exp.
 
     q: [B, H, Nq, d], k and v: [B, Hk, Nk, d] (Hk divides H), bfloat16 or
     float32 CUDA/HIP tensors with a contiguous last dimension. bias: optional
     float32 [B|1, H|1, Nq, Nk], added unscaled. kv_len: optional int32 [B] on
     the same device; keys at or past kv_len[b] are masked. causal hides key j
-    from query i when j > i + (Nk - Nq). scale defaults to 1/sqrt(d).
+    from query i when j > i + (Nk - Nq). window: optional (left, right) —
+    key j takes part only if i + (Nk - Nq) - left <= j <= i + (Nk - Nq) +
+    right; None or a negative value leaves that side open (causal sets right
+    to 0). scale defaults to 1/sqrt(d).
     Returns (o [B, H, Nq, d] in q's dtype, lse [B, H, Nq] float32).
     """
     import torch
     scale, out, lse, (qd, kd, vd, od, ld, mask, _keep) = _prepare(q, k, v, bias, kv_len, scale,
-                                                                    out, lse)
+                                                                    out, lse, window)
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
         rc = attn_fwd_raw(qd, kd, vd, mask, causal, scale, od, ld, stream)

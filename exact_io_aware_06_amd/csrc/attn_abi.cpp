@@ -188,6 +188,22 @@ attn_status_t prepare(const attn_tensor_t* q, const attn_tensor_t* k, const attn
   p.n_split = 1;
   p.pack = 1;
 
+  // Mask kind: none, causal (a window with right bound 0 and no left
+  // bound), or a general window, launched on the causal instantiations with
+  // both bounds clamped to values that exclude nothing more than intended.
+  const bool win = bias_or_mask != nullptr && bias_or_mask->window != 0;
+  int64_t wl = win ? bias_or_mask->window_left : -1;
+  int64_t wr = win ? bias_or_mask->window_right : -1;
+  if (causal) wr = 0;
+  if (wl >= 0 || wr > 0) {
+    p.causal = 1;
+    p.local = 1;
+    p.win_left = (int32_t)(wl < 0 ? Nk : std::min<int64_t>(wl, Nk));
+    p.win_right = (int32_t)(wr < 0 ? Nq : std::min<int64_t>(wr, Nq));
+  } else {
+    p.causal = wr == 0 ? 1 : 0;
+  }
+
   // grid size: 8 * ceil(B*H*ceil(Nq/16)/8) workgroups at most (f32 tiles are smallest)
   const int64_t tiles = B * H * ((Nq + 15) / 16);
   if (tiles > ((int64_t)1 << 31) - 64)

@@ -90,7 +90,12 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdParams p, TileMap 
   const int q0 = qt * kBr;
   const int qw0 = q0 + wave * 16;
   const int my_q = qw0 + l16;
-  const int off = Nk - Nq;
+  // causal alignment: key j hidden from query i when j > i + off; with a
+  // window (p.local, on the causal instantiations) also when j < i + off_l
+  const int off = Nk - Nq + (p.local ? p.win_right : 0);
+  const int off_l = Nk - Nq - p.win_left;
+  // first tile any row of this workgroup may see
+  const int j0 = p.local ? max(q0 + off_l, 0) / kBc : 0;
 
   int kend = Nk;
   if (p.kv_len != nullptr) kend = min(max(p.kv_len[b], 0), Nk);
@@ -120,7 +125,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdParams p, TileMap 
   if (HAS_BIAS)
     brow = p.bias + b * p.bias_sb + h * p.bias_sh + (int64_t)min(my_q, Nq - 1) * p.bias_sn;
 
-  for (int j = 0; j < nt; ++j) {
+  for (int j = j0; j < nt; ++j) {
     const int kv0 = j * kBc;
     __syncthreads();
     for (int c = tid; c < kBc * D / 4; c += kThreads) {
@@ -136,7 +141,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdParams p, TileMap 
       *reinterpret_cast<f32x4*>(&vs[key * D + col]) = vx;
     }
     __syncthreads();
-    if (kv0 >= wave_keys) continue;
+    if (kv0 >= wave_keys || (p.local && kv0 + kBc <= qw0 + off_l)) continue;
 
     // S^T blocks: register i of block kb holds key kv0 + 16kb + 4g + i
     f32x4 sacc[2] = {f32x4{}, f32x4{}};
@@ -160,7 +165,8 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdParams p, TileMap 
         } else {
           t = sacc[kb][i] * c2;
         }
-        const bool hide = (key >= kend) || (CAUSAL && key > my_q + off);
+        const bool hide = (key >= kend) || (CAUSAL && key > my_q + off) ||
+                          (p.local && key < my_q + off_l);
         sacc[kb][i] = hide ? -INFINITY : t;
       }
 

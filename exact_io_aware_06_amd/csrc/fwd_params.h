@@ -44,6 +44,14 @@ struct FwdParams {
   // (batch, key/value head), so each workgroup reads K/V once for all of
   // them. 1: one row space of Nq rows per query head.
   int32_t pack;
+  // Sliding window (local attention): local != 0 hides key j from query i
+  // unless i + (Nk - Nq) - win_left <= j <= i + (Nk - Nq) + win_right. Both
+  // bounds are >= 0 (an open side is given as a bound that excludes
+  // nothing). Launched on the causal instantiations (causal is a window
+  // with win_right = 0 and no left bound).
+  int32_t local;
+  int32_t win_left;
+  int32_t win_right;
 };
 
 // How the flat workgroup index maps onto (batch, head, query tile).

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 2
+#define ATTN_ABI_VERSION 3
 
 typedef enum {
   ATTN_OK = 0,
@@ -71,7 +71,7 @@ typedef struct {
   int64_t stride[4];   /* in elements; stride[3] must be 1 */
 } attn_tensor_t;
 
-/* Optional additive terms on the scores. Both fields may be NULL. */
+/* Optional terms on the scores. A zero-initialised struct adds nothing. */
 typedef struct {
   /* NULL, or float32 [B|1, H|1, Nq, Nk]: added to scale*QK^T (it is NOT
      multiplied by `scale`). A dimension of extent 1 is broadcast (its stride
@@ -83,6 +83,18 @@ typedef struct {
      only if j < kv_len[b] (values are clamped to [0, Nk]); the same as an
      additive -inf bias on the padded keys. */
   const int32_t* kv_len;
+  /* Sliding window (local attention), used when `window` is non-zero: key j
+     takes part for query i only if
+         i + (Nk - Nq) - window_left <= j <= i + (Nk - Nq) + window_right,
+     the band around the bottom-right-aligned diagonal; a negative bound
+     leaves that side open. `causal` != 0 sets window_right to 0 whatever
+     its value. Whole key tiles outside the band are skipped. ("Understanding
+     FlashAttention Pt 1", section 3.5, connection to local attention;
+     "FlashAttention, Explained", section 14, sliding-window masks skip
+     every tile outside the band; "flash-attention", Part III, window_size.) */
+  int32_t window;
+  int32_t window_left;
+  int32_t window_right;
 } attn_mask_t;
 
 /*

@@ -17,6 +17,15 @@ Conventions (the readings of the pages this file takes):
   Q10 on unequal query/key lengths]. With Nq == Nk this is "j > i".
 * ``kv_len[b]`` hides keys j >= kv_len[b] of batch entry b, the same as an
   additive -inf bias on the padded keys.
+* A sliding window (left, right) keeps key j for query i only when
+  i + (Nk - Nq) - left <= j <= i + (Nk - Nq) + right, a band around the same
+  bottom-right-aligned diagonal; a negative (or None) bound leaves that side
+  open, and causal masking is the band with right = 0 and no left bound. The
+  pages name the window (left and right sizes, -1 for "no window") and the
+  band of tiles it leaves, but print no formula; this is the plainest reading
+  that agrees with their causal alignment [Understanding FlashAttention Pt 1,
+  §3.5, connection to local attention; FlashAttention, Explained, §14;
+  flash-attention, Part III and Lab 3, window_size_left/right].
 * A row whose scores are all -inf yields O = 0 and LSE = -inf (log of a zero
   denominator) instead of NaN [flash-attention, Part VI, fully masked rows].
 * LSE is the natural logarithm of the row's denominator, in the units of the
@@ -36,7 +45,7 @@ def _f64(x) -> np.ndarray:
 
 
 def score_matrix(qh, kh, scale, bias=None, valid_keys=None, causal=False,
-                 q_positions=None, n_q=None) -> np.ndarray:
+                 q_positions=None, n_q=None, window=None) -> np.ndarray:
     """Scores of one head: S = scale * Q K^T + B, then the masks as -inf.
 
     qh: [nq, d] queries (rows of Q), kh: [Nk, d] keys.
@@ -46,6 +55,9 @@ def score_matrix(qh, kh, scale, bias=None, valid_keys=None, causal=False,
     q_positions: absolute query index of each row of ``qh`` (default 0..nq-1);
       n_q: the full query length Nq that the causal alignment uses
       (default nq). These two let a caller evaluate a subset of rows.
+    window: None or (left, right); key j is kept for query i only when
+      i + (Nk - n_q) - left <= j <= i + (Nk - n_q) + right (None or a
+      negative bound: that side open).
 
     [Understanding FlashAttention Pt 1, §0.2 "Notation" for S;
      §3.5 "Causal Masking and Tile Skipping" for the causal pattern.]
@@ -65,8 +77,15 @@ def score_matrix(qh, kh, scale, bias=None, valid_keys=None, causal=False,
     hide = np.zeros((nq, nk), dtype=bool)
     if valid_keys is not None:
         hide |= (j >= int(valid_keys))[None, :]
+    diag = q_positions[:, None] + (nk - int(n_q))   # the aligned diagonal
     if causal:
-        hide |= j[None, :] > (q_positions[:, None] + (nk - int(n_q)))
+        hide |= j[None, :] > diag
+    if window is not None:
+        left, right = window
+        if left is not None and left >= 0:
+            hide |= j[None, :] < diag - int(left)
+        if right is not None and right >= 0:
+            hide |= j[None, :] > diag + int(right)
     if hide.any():
         s = np.where(hide, -np.inf, s)
     return s
@@ -93,8 +112,9 @@ def masked_softmax(s) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
     return p, m, l
 
 
-def _head_forward(qh, kh, vh, scale, bias, valid_keys, causal, q_positions, n_q):
-    s = score_matrix(qh, kh, scale, bias, valid_keys, causal, q_positions, n_q)
+def _head_forward(qh, kh, vh, scale, bias, valid_keys, causal, q_positions, n_q,
+                  window=None):
+    s = score_matrix(qh, kh, scale, bias, valid_keys, causal, q_positions, n_q, window)
     p, m, l = masked_softmax(s)
     o = p @ _f64(vh)
     with np.errstate(divide="ignore"):
@@ -111,12 +131,14 @@ def _bias_for(bias, b, h):
     return bias[b if bias.shape[0] > 1 else 0, h if bias.shape[1] > 1 else 0]
 
 
-def attention_forward(q, k, v, *, scale, bias=None, kv_len=None, causal=False):
+def attention_forward(q, k, v, *, scale, bias=None, kv_len=None, causal=False,
+                      window=None):
     """O = softmax_row(scale * Q K^T + B) V and LSE, for [B, H, N, d] inputs.
 
     q: [B, H, Nq, d], k: [B, H, Nk, d], v: [B, H, Nk, dv] (any real dtype;
     widened to float64). bias: None or [B|1, H|1, Nq, Nk]. kv_len: None or
-    B integers. Returns (O [B, H, Nq, dv], LSE [B, H, Nq]) in float64.
+    B integers. window: None or (left, right), see ``score_matrix``.
+    Returns (O [B, H, Nq, dv], LSE [B, H, Nq]) in float64.
 
     Each head materialises its full S and P, exactly the three-pass standard
     algorithm the fused kernel replaces [Understanding FlashAttention Pt 1,
@@ -132,12 +154,12 @@ def attention_forward(q, k, v, *, scale, bias=None, kv_len=None, causal=False):
         for h in range(H):
             o[b, h], lse[b, h] = _head_forward(
                 q[b, h], k[b, h], v[b, h], scale, _bias_for(bias, b, h), vk,
-                causal, None, Nq)
+                causal, None, Nq, window)
     return o, lse
 
 
 def attention_rows(q, k, v, rows: Iterable[Sequence[int]], *, scale, bias=None,
-                   kv_len=None, causal=False):
+                   kv_len=None, causal=False, window=None):
     """The same function as ``attention_forward`` for selected rows only.
 
     rows: iterable of (b, h, i). Returns (O [n, dv], LSE [n]) in row order.
@@ -158,7 +180,7 @@ def attention_rows(q, k, v, rows: Iterable[Sequence[int]], *, scale, bias=None,
         bsel = None if bh is None else bh[idx]
         vk = None if kv_len is None else int(kv_len[b])
         oh, lh = _head_forward(_f64(q[b, h][idx]), _f64(k[b, h]), _f64(v[b, h]),
-                               scale, bsel, vk, causal, idx, Nq)
+                               scale, bsel, vk, causal, idx, Nq, window)
         for r, (n, _) in enumerate(items):
             o[n] = oh[r]
             lse[n] = lh[r]

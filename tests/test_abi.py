@@ -55,10 +55,12 @@ def test_struct_layout_matches_header():
     #include <stddef.h>
     #include "attn.h"
     int main(void) {
-      printf("%zu %zu %zu %zu %zu %zu %zu\n", sizeof(attn_tensor_t),
+      printf("%zu %zu %zu %zu %zu %zu %zu %zu %zu %zu\n", sizeof(attn_tensor_t),
              offsetof(attn_tensor_t, dtype), offsetof(attn_tensor_t, shape),
              offsetof(attn_tensor_t, stride), sizeof(attn_mask_t),
-             offsetof(attn_mask_t, kv_len), sizeof(attn_status_t));
+             offsetof(attn_mask_t, kv_len), offsetof(attn_mask_t, window),
+             offsetof(attn_mask_t, window_left), offsetof(attn_mask_t, window_right),
+             sizeof(attn_status_t));
       return 0;
     }
     """
@@ -72,7 +74,8 @@ def test_struct_layout_matches_header():
                                                check=True).stdout.split()]
     T, M = ea.AttnTensor, ea.AttnMask
     assert vals == [ctypes.sizeof(T), T.dtype.offset, T.shape.offset, T.stride.offset,
-                    ctypes.sizeof(M), M.kv_len.offset, 4]
+                    ctypes.sizeof(M), M.kv_len.offset, M.window.offset, M.window_left.offset,
+                    M.window_right.offset, 4]
 
 
 # ------------------------------------------------------------ host-side rejections

@@ -23,7 +23,7 @@ _orig = {name: getattr(oa, name) for name in (
 
 def _scores(variant):
     def score_matrix(qh, kh, scale, bias=None, valid_keys=None, causal=False,
-                     q_positions=None, n_q=None):
+                     q_positions=None, n_q=None, window=None):
         qh = np.asarray(qh, dtype=np.float64)
         kh = np.asarray(kh, dtype=np.float64)
         nq, nk = qh.shape[0], kh.shape[0]
@@ -51,6 +51,18 @@ def _scores(variant):
                 hide |= j[None, :] >= qp[:, None] + (nk - int(n_q))
             else:
                 hide |= j[None, :] > qp[:, None] + (nk - int(n_q))
+        if window is not None:
+            left, right = window
+            diag = qp[:, None] + (0 if variant == "window_top_left" else nk - int(n_q))
+            if variant == "window_sides_swapped":
+                left, right = right, left
+            if left is not None and left >= 0:
+                if variant == "window_left_exclusive":
+                    hide |= j[None, :] <= diag - int(left)
+                else:
+                    hide |= j[None, :] < diag - int(left)
+            if right is not None and right >= 0 and variant != "window_drop_right":
+                hide |= j[None, :] > diag + int(right)
         return np.where(hide, -np.inf, s)
     return score_matrix
 
@@ -77,8 +89,9 @@ def _softmax(variant):
 
 
 def _head(variant):
-    def _head_forward(qh, kh, vh, scale, bias, valid_keys, causal, q_positions, n_q):
-        s = oa.score_matrix(qh, kh, scale, bias, valid_keys, causal, q_positions, n_q)
+    def _head_forward(qh, kh, vh, scale, bias, valid_keys, causal, q_positions, n_q,
+                      window=None):
+        s = oa.score_matrix(qh, kh, scale, bias, valid_keys, causal, q_positions, n_q, window)
         p, m, l = oa.masked_softmax(s)
         vh = np.asarray(vh, dtype=np.float64)
         if variant == "pv_transposed" and p.shape[0] == p.shape[1]:
@@ -159,6 +172,10 @@ MUTATIONS = {
     "kv_len_off_by_one": ("score_matrix", _scores),
     "causal_top_left": ("score_matrix", _scores),
     "causal_diag_masked": ("score_matrix", _scores),
+    "window_top_left": ("score_matrix", _scores),
+    "window_sides_swapped": ("score_matrix", _scores),
+    "window_left_exclusive": ("score_matrix", _scores),
+    "window_drop_right": ("score_matrix", _scores),
     "no_dead_row_guard": ("masked_softmax", _softmax),
     "sign_flip": ("masked_softmax", _softmax),
     "pv_transposed": ("_head_forward", _head),

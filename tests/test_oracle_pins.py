@@ -396,3 +396,68 @@ def test_layout_is_batch_head_seq_dim():
     ot, _ = oracle.attention_forward(q.transpose(0, 2, 1, 3), k.transpose(0, 2, 1, 3),
                                      v.transpose(0, 2, 1, 3), scale=0.5)
     assert not np.allclose(ot.transpose(0, 2, 1, 3), o, atol=1e-3)
+
+
+# ----------------------------------------------------------- sliding window
+# The kept key sets below are listed by hand from the reading of the pages'
+# window (left, right) around the bottom-right-aligned diagonal i + Nk - Nq,
+# not computed by the oracle's formula.
+WINDOW_CASES = [
+    # (Nq, Nk, window, kept keys of each query row)
+    (6, 6, (2, 0), [[0], [0, 1], [0, 1, 2], [1, 2, 3], [2, 3, 4], [3, 4, 5]]),
+    (3, 7, (1, 1), [[3, 4, 5], [4, 5, 6], [5, 6]]),
+    (5, 5, (2, -1), [[0, 1, 2, 3, 4], [0, 1, 2, 3, 4], [0, 1, 2, 3, 4], [1, 2, 3, 4],
+                     [2, 3, 4]]),
+    (4, 4, (-1, 1), [[0, 1], [0, 1, 2], [0, 1, 2, 3], [0, 1, 2, 3]]),
+    (5, 3, (0, 1), [[], [0], [0, 1], [1, 2], [2]]),
+    (2, 6, (0, 0), [[4], [5]]),
+]
+
+
+def test_window_kept_keys():
+    for nq, nk, window, kept in WINDOW_CASES:
+        _check_window_case(nq, nk, window, kept)
+
+
+def _check_window_case(nq, nk, window, kept):
+    # Uniform scores (q = 0): each row's output is the mean of the values of
+    # its kept keys and its LSE is ln(count); a row with none is 0 / -inf.
+    r = _rng(30 + nq * nk)
+    q = np.zeros((1, 1, nq, 4))
+    k = r.normal(size=(1, 1, nk, 4))
+    v = r.normal(size=(1, 1, nk, 3))
+    o, lse = oracle.attention_forward(q, k, v, scale=1.0, window=window)
+    for i, keys in enumerate(kept):
+        if keys:
+            assert np.allclose(o[0, 0, i], v[0, 0, keys].mean(axis=0), atol=1e-14)
+            assert abs(lse[0, 0, i] - math.log(len(keys))) < 1e-14
+        else:
+            assert np.all(o[0, 0, i] == 0.0) and lse[0, 0, i] == -np.inf
+    # random queries: each row equals plain attention over its kept keys only
+    q = r.normal(size=(1, 1, nq, 4))
+    o, lse = oracle.attention_forward(q, k, v, scale=0.7, window=window)
+    for i, keys in enumerate(kept):
+        if not keys:
+            continue
+        ro, rl = oracle.attention_forward(q[:, :, i:i + 1], k[:, :, keys], v[:, :, keys],
+                                          scale=0.7)
+        assert np.allclose(o[0, 0, i], ro[0, 0, 0], atol=1e-14)
+        assert abs(lse[0, 0, i] - rl[0, 0, 0]) < 1e-13
+
+
+def test_window_special_cases():
+    r = _rng(40)
+    q = r.normal(size=(2, 2, 9, 4))
+    k = r.normal(size=(2, 2, 11, 4))
+    v = r.normal(size=(2, 2, 11, 3))
+    plain = oracle.attention_forward(q, k, v, scale=0.5)
+    causal = oracle.attention_forward(q, k, v, scale=0.5, causal=True)
+    for w in [(-1, -1), (None, None), (11, 11), (100, 9)]:
+        o, lse = oracle.attention_forward(q, k, v, scale=0.5, window=w)
+        assert np.array_equal(o, plain[0]) and np.array_equal(lse, plain[1])
+    for w in [(-1, 0), (20, 0)]:
+        o, lse = oracle.attention_forward(q, k, v, scale=0.5, window=w)
+        assert np.array_equal(o, causal[0]) and np.array_equal(lse, causal[1])
+    # causal and a right bound: the causal side wins
+    o, lse = oracle.attention_forward(q, k, v, scale=0.5, causal=True, window=(-1, 3))
+    assert np.array_equal(o, causal[0])

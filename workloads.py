@@ -19,6 +19,10 @@ Recipe (fixed here, stated again in the design notes):
   sequence (the pages give no decode shape; these are typical serving ones:
   batch 8 at 16K keys, and one sequence at 64K keys, the length up to which
   the pages report near-constant decode latency).
+* Sliding-window workloads: the long-context shape (B=1, H=16, N=16384,
+  d=128) with a causal window of 4096 keys (a common local-attention size;
+  the pages' example is 128 neighbouring tokens, too few tiles per row to
+  measure anything but launch overhead).
 """
 
 from __future__ import annotations
@@ -47,6 +51,7 @@ class Workload:
     kv_len_range: Optional[tuple] = None    # (lo, hi) inclusive integer range
     seed: int = 0
     Hk: Optional[int] = None                # key/value heads (None: H)
+    window: Optional[tuple] = None          # (left, right) sliding window
 
     @property
     def kv_heads(self) -> int:
@@ -70,6 +75,7 @@ class Workload:
             "Nk": self.Nk, "d": self.d, "dtype": self.dtype,
             "causal": self.causal, "scale": self.softmax_scale,
             "seed": self.seed, **({} if self.Hk is None else {"Hk": self.Hk}),
+            **({} if self.window is None else {"window": list(self.window)}),
         }
 
     def kv_bytes(self) -> int:
@@ -110,7 +116,14 @@ DECODE = {
                                         seed=7),
 }
 
-ALL = {**CONFIGS, **DECODE}
+# Sliding-window (local) attention.
+WINDOW = {
+    "local_b1_h16_n16k_w4096_d128": Workload("local_b1_h16_n16k_w4096_d128", 1, 16, 16384,
+                                             16384, 128, causal=True, window=(4096, 0),
+                                             seed=8),
+}
+
+ALL = {**CONFIGS, **DECODE, **WINDOW}
 
 
 def _storage(dtype: str):
