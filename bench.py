@@ -29,13 +29,18 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3     # MI355X dense fp32 matrix
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
-KERNEL_SRC = {"bf16": "exact_io_aware_06_amd/csrc/fwd_bf16.hip",
-              "f32": "exact_io_aware_06_amd/csrc/fwd_f32.hip"}
+# the sources a kernel's HBM traffic depends on (kernel body and its launch)
+KERNEL_SRC = {"bf16": ["exact_io_aware_06_amd/csrc/fwd_bf16_kernel.h",
+                       "exact_io_aware_06_amd/csrc/fwd_bf16.hip"],
+              "f32": ["exact_io_aware_06_amd/csrc/fwd_f32.hip"]}
 
 
-def _src_hash(rel):
-    with open(os.path.join(ROOT, rel), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def _src_hash(rels):
+    h = hashlib.sha256()
+    for rel in rels:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def _traffic(workload, dtype):

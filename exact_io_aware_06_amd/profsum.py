@@ -3,7 +3,7 @@
     python -m exact_io_aware_06_amd.profsum stats  <kernel_stats.csv> <out.txt> <command...>
     python -m exact_io_aware_06_amd.profsum counters <workload> <out.txt> <pmc_dir>... -- <command...>
     python -m exact_io_aware_06_amd.profsum traffic <workload> <fetch_dir> <write_dir> \
-        <copy_fetch_dir> <copy_write_dir> <copy_mib> <kernel_src> <out.txt> <command...>
+        <copy_fetch_dir> <copy_write_dir> <copy_mib> <kernel_src[,src...]> <out.txt> <command...>
 
 `stats` copies the per-kernel duration table. `counters` averages the SQ/GRBM
 counters of the attention kernel over its dispatches and derives MFMA busy
@@ -83,17 +83,27 @@ def counters(workload, out, dirs, cmd):
     open(out, "w").write("\n".join(lines) + "\n")
 
 
+def source_sha256(paths):
+    """sha256 over the concatenated bytes of the kernel's source files."""
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
 def traffic(workload, fdir, wdir, cfdir, cwdir, copy_mib, src, out, cmd):
-    fetch, nf = _counter(fdir, "FETCH_SIZE", "attn")
-    write, nw = _counter(wdir, "WRITE_SIZE", "attn")
+    # the forward kernel only (a split launch also runs the merge kernel)
+    fetch, nf = _counter(fdir, "FETCH_SIZE", "fwd_")
+    write, nw = _counter(wdir, "WRITE_SIZE", "fwd_")
     cfetch, _ = _counter(cfdir, "FETCH_SIZE", "copyBuffer")
     cwrite, _ = _counter(cwdir, "WRITE_SIZE", "copyBuffer")
     copy_kib = float(copy_mib) * 1024.0
     kf, kw = copy_kib / cfetch, copy_kib / cwrite
     hbm = fetch * kf * 1024 + write * kw * 1024
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    sha = source_sha256(src.split(","))
     with open(out, "w") as f:
-        f.write(f"# HBM traffic of the attention kernel, workload {workload}\n")
+        f.write(f"# HBM traffic of the attention forward kernel, workload {workload}\n")
         f.write(f"# command: {cmd}\n")
         f.write(f"# counters: FETCH_SIZE and WRITE_SIZE in separate rocprofv3 --pmc runs "
                 f"({nf} and {nw} dispatches averaged)\n")
@@ -104,7 +114,7 @@ def traffic(workload, fdir, wdir, cfdir, cwdir, copy_mib, src, out, cmd):
         f.write(f"fetch_scale: {kf:.4f}\n")
         f.write(f"write_scale: {kw:.4f}\n")
         f.write(f"hbm_bytes_per_launch: {hbm:.0f}\n")
-        f.write(f"kernel_source: {os.path.relpath(src)}\n")
+        f.write(f"kernel_source: {','.join(os.path.relpath(x) for x in src.split(','))}\n")
         f.write(f"source_sha256: {sha}\n")
 
 
