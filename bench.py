@@ -115,6 +115,112 @@ def cpu_baseline(inp, w, budget_s=15.0):
     }
 
 
+def varlen_flops(w, lens):
+    """4 d FLOPs per (query, key) pair of every packed sequence (halved when
+    causal, like the other causal workloads)."""
+    pairs = sum(int(n) * int(n) for n in lens)
+    return 4.0 * w.H * w.d * pairs * (0.5 if w.causal else 1.0)
+
+
+def bench_varlen(args, w):
+    """Packed variable-length batch: one step = one attn_fwd_varlen call.
+    The same sequences padded to the length cap and masked with kv_len (the
+    padded rectangle of the pages' Lab 5) are timed too, for the speedup."""
+    import torch
+    import workloads
+    import exact_io_aware_06_amd as ea
+
+    inp = workloads.make_varlen_inputs(w)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, k, v = (inp[x].to(dev) for x in ("q", "k", "v"))
+    cu = inp["cu"].to(dev)
+    lens = inp["lens"]
+    step, _, _ = ea.prepare_varlen_call(q, k, v, cu, cu, inp["max_len"], causal=w.causal,
+                                        scale=inp["scale"])
+
+    # the padded rectangle: [B, H, cap, d] with keys past each length masked
+    L = w.Nq
+    qp = torch.zeros(w.B, w.H, L, w.d, dtype=q.dtype, device=dev)
+    kp = torch.zeros(w.B, w.kv_heads, L, w.d, dtype=q.dtype, device=dev)
+    vp = torch.zeros_like(kp)
+    c = inp["cu"].tolist()
+    for b in range(w.B):
+        n = c[b + 1] - c[b]
+        qp[b, :, :n] = q[c[b]:c[b + 1]].transpose(0, 1)
+        kp[b, :, :n] = k[c[b]:c[b + 1]].transpose(0, 1)
+        vp[b, :, :n] = v[c[b]:c[b + 1]].transpose(0, 1)
+    kv_len = lens.to(torch.int32).to(dev)
+    step_p, _, _ = ea.prepare_call(qp, kp, vp, kv_len=kv_len, causal=w.causal, scale=inp["scale"])
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(args.steps):
+            fn()
+        stop.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop) / args.steps
+
+    ms = timed(step)
+    ms_padded = timed(step_p)
+    flops = varlen_flops(w, lens)
+    tflops = flops / (ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline_varlen(inp, w, args.cpu_budget)
+        cpu["value"] = round(cpu["value"], 6)
+    out = {
+        "metric": "attention fwd TFLOP/s and % of bf16 MFMA peak at 1 MI355X (N=4096,d=128)",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {**w.describe(), "total_tokens": int(lens.sum()),
+                   "lens": [int(x) for x in lens], "flops_per_step": flops,
+                   "padded_ms_per_step": round(ms_padded, 4),
+                   "speedup_vs_padded": round(ms_padded / ms, 3), "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def cpu_baseline_varlen(inp, w, budget_s=15.0):
+    """The oracle on whole (sequence, head) pairs of the packed batch until
+    the time budget is spent; TFLOP/s over the pairs done."""
+    import oracle
+    c = inp["cu"].tolist()
+    rep = w.H // w.kv_heads
+    done_flops, done, total = 0.0, 0, w.B * w.H
+    t0 = time.perf_counter()
+    for s in range(w.B):
+        n = c[s + 1] - c[s]
+        for h in range(w.H):
+            hk = h // rep
+            qs = inp["q"][c[s]:c[s + 1], h].double().numpy()[None, None]
+            ks = inp["k"][c[s]:c[s + 1], hk].double().numpy()[None, None]
+            vs = inp["v"][c[s]:c[s + 1], hk].double().numpy()[None, None]
+            oracle.attention_forward(qs, ks, vs, scale=inp["scale"], causal=w.causal)
+            done_flops += 4.0 * w.d * n * n * (0.5 if w.causal else 1.0)
+            done += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": done_flops / dt / 1e12, "unit": "TFLOP/s", "cores": _blas_threads(),
+            "kind": "oracle",
+            "sample": f"{done} of {total} (sequence, head) pairs of {w.name}, fp64 "
+                      f"materialising S and P, {dt:.1f} s"}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -182,6 +288,8 @@ def main(argv=None):
     name = args.workload or workloads.HEADLINE
     w = workloads.ALL[name]
     split = name in workloads.DECODE
+    if name in workloads.VARLEN:
+        return bench_varlen(args, w)
     inp = workloads.make_inputs(w)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

@@ -23,6 +23,7 @@ import os
 from typing import Optional
 
 __all__ = ["attn_fwd", "attn_fwd_raw", "attn_fwd_splitkv", "attn_fwd_splitkv_raw",
+           "attn_fwd_varlen", "prepare_varlen_call",
            "splitkv_num_splits", "splitkv_workspace_size", "prepare_call", "AttnError", "load_library", "library_path",
            "AttnTensor", "AttnMask", "ATTN_OK", "ATTN_ERR_INVALID",
            "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_HIP", "ATTN_BF16", "ATTN_F32"]
@@ -81,6 +82,10 @@ def load_library():
     lib.attn_fwd_splitkv_workspace_size.restype = ctypes.c_int64
     lib.attn_fwd_splitkv_num_splits.argtypes = [ctypes.c_int64] * 6 + [ctypes.c_int] * 2
     lib.attn_fwd_splitkv_num_splits.restype = ctypes.c_int32
+    lib.attn_fwd_varlen.argtypes = [P, P, P, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                    ctypes.c_int32, ctypes.POINTER(AttnMask), ctypes.c_int,
+                                    ctypes.c_float, P, P, ctypes.c_void_p]
+    lib.attn_fwd_varlen.restype = ctypes.c_int
     lib.attn_last_error.argtypes = []
     lib.attn_last_error.restype = ctypes.c_char_p
     lib.attn_abi_version.argtypes = []
@@ -265,6 +270,94 @@ def prepare_call(q, k, v, bias=None, kv_len=None, causal: bool = False,
 
     def enqueue(_refs=refs, _ws=workspace):
         rc = fn(*args)
+        if rc != ATTN_OK:
+            raise AttnError(rc, last_error())
+
+    return enqueue, out, lse
+
+
+def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int,
+                    causal: bool = False, scale: Optional[float] = None, window=None,
+                    out=None, lse=None):
+    """Attention over packed variable-length sequences (no padding).
+
+    q: [total_q, H, d], k and v: [total_k, Hk, d] (token-major packing,
+    last dimension contiguous), bfloat16 or float32 GPU tensors.
+    cu_seqlens_q / cu_seqlens_k: int32 [num_seqs + 1] GPU tensors of
+    cumulative offsets; sequence s owns rows cu_seqlens_q[s]:cu_seqlens_q[s+1]
+    and keys cu_seqlens_k[s]:cu_seqlens_k[s+1]. max_seqlen_q: at least the
+    longest query sequence. causal / window apply per sequence (bottom-right
+    aligned). Returns (o [total_q, H, d], lse [H, total_q] float32).
+    """
+    enqueue, out, lse = prepare_varlen_call(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+                                            causal, scale, window, out, lse)
+    enqueue()
+    return out, lse
+
+
+def prepare_varlen_call(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int,
+                        causal: bool = False, scale: Optional[float] = None, window=None,
+                        out=None, lse=None):
+    """``attn_fwd_varlen``'s arguments marshalled once; returns ``(enqueue,
+    out, lse)`` like ``prepare_call``.
+
+    q: [total_q, H, d], k and v: [total_k, Hk, d] (token-major packing,
+    last dimension contiguous), bfloat16 or float32 GPU tensors.
+    cu_seqlens_q / cu_seqlens_k: int32 [num_seqs + 1] GPU tensors of
+    cumulative offsets; sequence s owns rows cu_seqlens_q[s]:cu_seqlens_q[s+1]
+    and keys cu_seqlens_k[s]:cu_seqlens_k[s+1]. max_seqlen_q: at least the
+    longest query sequence. causal / window apply per sequence (bottom-right
+    aligned). Returns (o [total_q, H, d], lse [H, total_q] float32).
+    """
+    import torch
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k and v must be GPU tensors (no CPU path exists)")
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        if t.dim() != 3:
+            raise ValueError(f"{n} must be 3-D [total, heads, d], got {tuple(t.shape)}")
+    for cu, n in ((cu_seqlens_q, "cu_seqlens_q"), (cu_seqlens_k, "cu_seqlens_k")):
+        if cu.dtype != torch.int32 or not cu.is_cuda or cu.dim() != 1 or not cu.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous 1-D int32 GPU tensor")
+    if cu_seqlens_q.numel() != cu_seqlens_k.numel() or cu_seqlens_q.numel() < 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both hold num_seqs + 1 offsets")
+    Tq, H, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((H, Tq), dtype=torch.float32, device=q.device)
+    if lse.shape != (H, Tq) or lse.dtype != torch.float32:
+        raise ValueError("lse must be a float32 [H, total_q] tensor")
+
+    def view4(t, name):
+        # [total, heads, d] seen as [1, heads, total, d]
+        dd = _torch_desc(t.unsqueeze(0), name)
+        st = t.stride()
+        return make_desc(t.data_ptr(), dd.dtype, (1, t.shape[1], t.shape[0], t.shape[2]),
+                         (t.numel(), st[1], st[0], st[2]))
+
+    qd, kd, vd, od = view4(q, "q"), view4(k, "k"), view4(v, "v"), view4(out, "out")
+    ld = make_desc(lse.data_ptr(), ATTN_F32, (1, H, Tq, 1), (lse.numel(), lse.stride(0),
+                                                              lse.stride(1), 1))
+    mask = None
+    if window is not None:
+        mask = AttnMask()
+        wl, wr = window
+        mask.window = 1
+        mask.window_left = -1 if wl is None else int(wl)
+        mask.window_right = -1 if wr is None else int(wr)
+    lib = load_library()
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    refs = (qd, kd, vd, od, ld, mask)
+    args = [ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(vd),
+            ctypes.c_void_p(cu_seqlens_q.data_ptr()), ctypes.c_void_p(cu_seqlens_k.data_ptr()),
+            cu_seqlens_q.numel() - 1, int(max_seqlen_q),
+            ctypes.byref(mask) if mask is not None else None, 1 if causal else 0,
+            float(scale), ctypes.byref(od), ctypes.byref(ld), ctypes.c_void_p(stream)]
+
+    def enqueue(_refs=refs):
+        rc = lib.attn_fwd_varlen(*args)
         if rc != ATTN_OK:
             raise AttnError(rc, last_error())
 

@@ -320,4 +320,38 @@ attn_status_t attn_fwd_splitkv(const attn_tensor_t* q, const attn_tensor_t* k,
   return ATTN_OK;
 }
 
+attn_status_t attn_fwd_varlen(const attn_tensor_t* q, const attn_tensor_t* k,
+                              const attn_tensor_t* v, const int32_t* cu_seqlens_q,
+                              const int32_t* cu_seqlens_k, int32_t num_seqs, int32_t max_seqlen_q,
+                              const attn_mask_t* window_mask, int causal, float scale,
+                              const attn_tensor_t* o, const attn_tensor_t* lse, void* stream) {
+  g_last_error.clear();
+  if (window_mask != nullptr && (window_mask->bias != nullptr || window_mask->kv_len != nullptr))
+    return fail(ATTN_ERR_INVALID, "packed sequences take no bias or kv_len (their lengths are "
+                                  "the offsets)");
+  for (const attn_tensor_t* t : {q, k, v, o, lse})
+    if (t != nullptr && t->shape[0] != 1)
+      return fail(ATTN_ERR_INVALID, "packed tensors are [1, heads, total rows, d] (got %lld in dim 0)",
+                  (long long)t->shape[0]);
+  if (num_seqs < 0 || max_seqlen_q < 0)
+    return fail(ATTN_ERR_INVALID, "num_seqs and max_seqlen_q must be >= 0");
+  attn::FwdParams p;
+  bool empty;
+  attn_status_t s = prepare(q, k, v, window_mask, causal, scale, o, lse, p, empty);
+  if (s != ATTN_OK || empty) return s;
+  if (num_seqs == 0 || max_seqlen_q == 0) return ATTN_OK;
+  for (const int32_t* cu : {cu_seqlens_q, cu_seqlens_k})
+    if (cu == nullptr || (reinterpret_cast<uintptr_t>(cu) & 3u) != 0)
+      return fail(ATTN_ERR_INVALID, "cu_seqlens_q and cu_seqlens_k must be non-NULL, 4-byte aligned");
+  const int64_t max_q = std::min<int64_t>(max_seqlen_q, p.Nq);
+  if ((int64_t)num_seqs * p.H * ((max_q + 15) / 16) > ((int64_t)1 << 31) - 64)
+    return fail(ATTN_ERR_UNSUPPORTED, "problem needs more than 2^31 workgroups");
+  p.B = num_seqs;
+  p.cu_q = cu_seqlens_q;
+  p.cu_k = cu_seqlens_k;
+  p.max_q = (int32_t)max_q;
+  p.q_sb = p.k_sb = p.v_sb = p.o_sb = p.l_sb = 0;
+  return launch(p, q->dtype, (int)q->shape[3], stream);
+}
+
 }  // extern "C"

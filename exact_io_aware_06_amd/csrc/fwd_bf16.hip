@@ -33,7 +33,9 @@ int fwd_bf16_rows(int d, int64_t nrows, bool causal, bool bias, bool split) {
 int launch_fwd_bf16(const FwdParams& p, int d, void* stream) {
   const bool split = p.n_split > 1;
   const bool packed = split && p.pack > 1;
-  const int64_t nrows = packed ? (int64_t)p.pack * p.Nq : p.Nq;
+  const bool varlen = p.cu_q != nullptr;
+  // rows of one row space: Nq, pack * Nq, or the longest packed sequence
+  const int64_t nrows = varlen ? p.max_q : packed ? (int64_t)p.pack * p.Nq : p.Nq;
   const int br = fwd_bf16_rows(d, nrows, p.causal != 0, p.bias != nullptr, split);
   const int waves = br / 32;
   TileMap tm;
@@ -51,7 +53,13 @@ int launch_fwd_bf16(const FwdParams& p, int d, void* stream) {
     tm.per_xcd = (int)((all + 7) / 8);
     tm.batch_inner = 0;
   }
+  if (varlen) {
+    // groups of query tiles dealt round-robin over the XCDs (decode_tile)
+    const int64_t groups = (int64_t)p.B * p.H;
+    tm.per_xcd = (int)((groups + 7) / 8 * tm.n_qtiles);
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (varlen) return (int)launch_bf16_varlen(p, tm, d, waves, s);
   if (p.local) return (int)launch_bf16_local(p, tm, d, waves, s);
   return split ? (int)launch_bf16_split(p, tm, d, waves, s) : (int)launch_bf16_plain(p, tm, d, waves, s);
 }

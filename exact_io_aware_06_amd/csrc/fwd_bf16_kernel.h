@@ -166,15 +166,28 @@ __device__ __forceinline__ void dma16(const uint8_t* tile, uint32_t off, uint8_t
   asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(tile), "{m0}"(lds));
 }
 
-template <bool SPLIT>
+template <bool SPLIT, bool VARLEN = false>
 __device__ __forceinline__ bool decode_tile(const TileMap& tm, int B, int H,
                                             int& b, int& h, int& qt, int& split) {
   const int w = blockIdx.x;
-  const int logical = (w & 7) * tm.per_xcd + (w >> 3);
-  if (logical >= tm.total) return false;
   int rest;
   int qi;
   split = 0;
+  if (VARLEN) {
+    // (batch, head) groups dealt round-robin over the 8 XCDs (workgroup w
+    // runs on XCD w % 8): one group's query tiles stay on one XCD and share
+    // its L2, and sequences of very different lengths spread evenly
+    const int x = w & 7, j = w >> 3;
+    const int g = (j / tm.n_qtiles) * 8 + x;
+    if (g >= B * H) return false;
+    qi = j % tm.n_qtiles;
+    h = g % H;
+    b = g / H;
+    qt = tm.reverse_q ? (tm.n_qtiles - 1 - qi) : qi;
+    return true;
+  }
+  const int logical = (w & 7) * tm.per_xcd + (w >> 3);
+  if (logical >= tm.total) return false;
   if (SPLIT) {
     // query tile fastest (they read the same key range), then the split
     qi = logical % tm.n_qtiles;
@@ -202,9 +215,12 @@ __device__ __forceinline__ bool decode_tile(const TileMap& tm, int B, int H,
 // workspace (p.n_split > 1); otherwise all keys, results to o / lse.
 // CAUSAL: keys j > i + (Nk - Nq) hidden from query i, or, with LOCAL, keys
 // outside the window [i + (Nk - Nq) - win_left, i + (Nk - Nq) + win_right].
-template <int D, int W, bool CAUSAL, bool HAS_BIAS, bool SPLIT, bool LOCAL>
+// VARLEN: the batch index is a packed sequence of its own length (rows and
+// keys from the cumulative offsets p.cu_q / p.cu_k).
+template <int D, int W, bool CAUSAL, bool HAS_BIAS, bool SPLIT, bool LOCAL, bool VARLEN = false>
 __global__ __launch_bounds__(64 * W, 2) void fwd_bf16_kernel(FwdParams p, TileMap tm) {
   static_assert(CAUSAL || !LOCAL, "a window is a two-sided causal mask");
+  static_assert(!VARLEN || (!HAS_BIAS && !SPLIT), "packed sequences take neither a bias nor a split");
   using G = Geo<D, W>;
   constexpr int kWaves = G::kWaves;
   constexpr int kBr = G::kBr;
@@ -213,7 +229,7 @@ __global__ __launch_bounds__(64 * W, 2) void fwd_bf16_kernel(FwdParams p, TileMa
   // packed: the query heads of one key/value head share the workgroup's rows
   const bool packed = SPLIT && p.pack > 1;
   int b, h, qt, split;
-  if (!decode_tile<SPLIT>(tm, p.B, packed ? p.Hk : p.H, b, h, qt, split)) return;
+  if (!decode_tile<SPLIT, VARLEN>(tm, p.B, packed ? p.Hk : p.H, b, h, qt, split)) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -222,7 +238,20 @@ __global__ __launch_bounds__(64 * W, 2) void fwd_bf16_kernel(FwdParams p, TileMa
   const int hi = lane >> 5;
   const int hk = packed ? h : h / p.head_group;
 
-  const int Nq = p.Nq;
+  // Rows [0, Nq) and keys [0, NkAll) of this (batch, head); packed
+  // sequences start at row q_lo / key k_lo of the packed tensors, with the
+  // offsets clamped into the tensors whatever the offset arrays hold.
+  int Nq = p.Nq, NkAll = p.Nk;
+  int64_t q_lo = 0, k_lo = 0;
+  if (VARLEN) {
+    const int a0 = min(max(p.cu_q[b], 0), p.Nq), a1 = min(max(p.cu_q[b + 1], a0), p.Nq);
+    const int c0 = min(max(p.cu_k[b], 0), p.Nk), c1 = min(max(p.cu_k[b + 1], c0), p.Nk);
+    q_lo = a0;
+    Nq = a1 - a0;
+    k_lo = c0;
+    NkAll = c1 - c0;
+    if (qt * kBr >= Nq) return;  // past this sequence's rows (the grid covers the longest)
+  }
   const int q0 = qt * kBr;
   const int qw0 = q0 + wave * 32;
   const int my_q = qw0 + l32;   // this lane's row of the workgroup's row space
@@ -246,7 +275,8 @@ __global__ __launch_bounds__(64 * W, 2) void fwd_bf16_kernel(FwdParams p, TileMa
     qbeg = (q0 / Nq == gl / Nq) ? q0 % Nq : 0;
   }
   const bool row_live = my_q < nrows;
-  const __bf16* qg = static_cast<const __bf16*>(p.q) + b * p.q_sb + row_h * p.q_sh;
+  const __bf16* qg = static_cast<const __bf16*>(p.q) + (VARLEN ? q_lo * p.q_sn : b * p.q_sb) +
+                     row_h * p.q_sh;
 
   // Key range. Split over keys: this workgroup covers keys [s * kv_split,
   // (s + 1) * kv_split) of its rows. Window: whole tiles before the window
@@ -254,14 +284,16 @@ __global__ __launch_bounds__(64 * W, 2) void fwd_bf16_kernel(FwdParams p, TileMa
   // indices below are relative to kbeg (the K/V and bias base addresses,
   // the key count and the mask offsets are shifted by it).
   int kbeg = SPLIT ? split * p.kv_split : 0;
-  if (LOCAL) kbeg = max(kbeg, max(qbeg + p.Nk - Nq - p.win_left, 0) & ~(kBc - 1));
-  const __bf16* kgp = static_cast<const __bf16*>(p.k) + b * p.k_sb + hk * p.k_sh + (int64_t)kbeg * p.k_sn;
-  const __bf16* vgp = static_cast<const __bf16*>(p.v) + b * p.v_sb + hk * p.v_sh + (int64_t)kbeg * p.v_sn;
-  const int Nk = p.Nk - kbeg;  // keys from kbeg on
+  if (LOCAL) kbeg = max(kbeg, max(qbeg + NkAll - Nq - p.win_left, 0) & ~(kBc - 1));
+  const __bf16* kgp = static_cast<const __bf16*>(p.k) + (VARLEN ? k_lo * p.k_sn : b * p.k_sb) +
+                      hk * p.k_sh + (int64_t)kbeg * p.k_sn;
+  const __bf16* vgp = static_cast<const __bf16*>(p.v) + (VARLEN ? k_lo * p.v_sn : b * p.v_sb) +
+                      hk * p.v_sh + (int64_t)kbeg * p.v_sn;
+  const int Nk = NkAll - kbeg;  // keys from kbeg on
   // causal alignment: key j hidden from query i when j > i + off (and, with
   // a window, when j < i + off_l)
-  const int off = p.Nk - Nq - kbeg + (LOCAL ? p.win_right : 0);
-  const int off_l = p.Nk - Nq - kbeg - p.win_left;
+  const int off = NkAll - Nq - kbeg + (LOCAL ? p.win_right : 0);
+  const int off_l = NkAll - Nq - kbeg - p.win_left;
 
   int kend = Nk;
   if (p.kv_len != nullptr) kend = min(max(p.kv_len[b] - kbeg, 0), Nk);
@@ -656,7 +688,8 @@ __global__ __launch_bounds__(64 * W, 2) void fwd_bf16_kernel(FwdParams p, TileMa
       p.part_lse[row] = (l_tot > 0.f) ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
   } else if (my_q < Nq) {  // not split: the final result
     const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
-    __bf16* orow = static_cast<__bf16*>(p.o) + b * p.o_sb + h * p.o_sh + (int64_t)my_q * p.o_sn;
+    __bf16* orow = static_cast<__bf16*>(p.o) + (VARLEN ? q_lo * p.o_sn : b * p.o_sb) + h * p.o_sh +
+                   (int64_t)my_q * p.o_sn;
     // register r of block cb holds column 32cb + 8(r/4) + 4hi + (r%4)
 #pragma unroll
     for (int cb = 0; cb < G::kNcb; ++cb)
@@ -668,17 +701,17 @@ __global__ __launch_bounds__(64 * W, 2) void fwd_bf16_kernel(FwdParams p, TileMa
         *reinterpret_cast<bf16x4*>(orow + 32 * cb + 8 * g + 4 * hi) = w;
       }
     if (hi == 0) {
-      float* lrow = p.lse + b * p.l_sb + h * p.l_sh;
+      float* lrow = p.lse + (VARLEN ? q_lo : b * p.l_sb) + h * p.l_sh;
       lrow[my_q] = (l_tot > 0.f) ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
     }
   }
 }
 
-template <int D, int W, bool CAUSAL, bool HAS_BIAS, bool SPLIT, bool LOCAL>
+template <int D, int W, bool CAUSAL, bool HAS_BIAS, bool SPLIT, bool LOCAL, bool VARLEN>
 hipError_t launch_one(const FwdParams& p, const TileMap& tm, hipStream_t stream) {
   using G = Geo<D, W>;
   static bool attr_set = false;  // benign race: every caller sets the same value
-  auto kern = fwd_bf16_kernel<D, W, CAUSAL, HAS_BIAS, SPLIT, LOCAL>;
+  auto kern = fwd_bf16_kernel<D, W, CAUSAL, HAS_BIAS, SPLIT, LOCAL, VARLEN>;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, G::kSmem);
@@ -692,18 +725,25 @@ hipError_t launch_one(const FwdParams& p, const TileMap& tm, hipStream_t stream)
 
 // Dispatch over head dimension, workgroup size, mask kind and bias for one
 // family of instantiations (each family is compiled in its own source file).
-template <bool SPLIT, bool LOCAL>
+template <bool SPLIT, bool LOCAL, bool VARLEN = false>
 hipError_t launch_family(const FwdParams& p, const TileMap& tm, int d, int waves, hipStream_t s) {
   auto go = [&](auto dc, auto wc) -> hipError_t {
     constexpr int D = decltype(dc)::value, W = decltype(wc)::value;
-    const bool bias = p.bias != nullptr;
-    if (LOCAL || p.causal)
-      return bias ? launch_one<D, W, true, true, SPLIT, LOCAL>(p, tm, s)
-                  : launch_one<D, W, true, false, SPLIT, LOCAL>(p, tm, s);
-    if constexpr (!LOCAL)
-      return bias ? launch_one<D, W, false, true, SPLIT, false>(p, tm, s)
-                  : launch_one<D, W, false, false, SPLIT, false>(p, tm, s);
-    return hipErrorInvalidValue;
+    if constexpr (VARLEN) {
+      if (p.bias != nullptr) return hipErrorInvalidValue;
+      if (LOCAL || p.causal) return launch_one<D, W, true, false, false, LOCAL, true>(p, tm, s);
+      if constexpr (!LOCAL) return launch_one<D, W, false, false, false, false, true>(p, tm, s);
+      return hipErrorInvalidValue;
+    } else {
+      const bool bias = p.bias != nullptr;
+      if (LOCAL || p.causal)
+        return bias ? launch_one<D, W, true, true, SPLIT, LOCAL, false>(p, tm, s)
+                    : launch_one<D, W, true, false, SPLIT, LOCAL, false>(p, tm, s);
+      if constexpr (!LOCAL)
+        return bias ? launch_one<D, W, false, true, SPLIT, false, false>(p, tm, s)
+                    : launch_one<D, W, false, false, SPLIT, false, false>(p, tm, s);
+      return hipErrorInvalidValue;
+    }
   };
   using D128 = std::integral_constant<int, 128>;
   using D64 = std::integral_constant<int, 64>;
@@ -725,5 +765,6 @@ hipError_t launch_family(const FwdParams& p, const TileMap& tm, int d, int waves
 hipError_t launch_bf16_plain(const FwdParams& p, const TileMap& tm, int d, int waves, hipStream_t s);
 hipError_t launch_bf16_split(const FwdParams& p, const TileMap& tm, int d, int waves, hipStream_t s);
 hipError_t launch_bf16_local(const FwdParams& p, const TileMap& tm, int d, int waves, hipStream_t s);
+hipError_t launch_bf16_varlen(const FwdParams& p, const TileMap& tm, int d, int waves, hipStream_t s);
 
 }  // namespace attn

@@ -83,10 +83,24 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdParams p, TileMap 
   const int g = lane >> 4;
   const int hk = h / p.head_group;
 
-  const float* qg = static_cast<const float*>(p.q) + b * p.q_sb + h * p.q_sh;
-  const float* kgp = static_cast<const float*>(p.k) + b * p.k_sb + hk * p.k_sh;
-  const float* vgp = static_cast<const float*>(p.v) + b * p.v_sb + hk * p.v_sh;
-  const int Nq = p.Nq, Nk = p.Nk;
+  // packed variable-length sequences: b is a sequence with rows [q_lo,
+  // q_lo + Nq) and keys [k_lo, k_lo + Nk) of the packed tensors (offsets
+  // clamped into the tensors)
+  int Nq = p.Nq, Nk = p.Nk;
+  int64_t q_lo = 0, k_lo = 0;
+  const bool varlen = p.cu_q != nullptr;
+  if (varlen) {
+    const int a0 = min(max(p.cu_q[b], 0), p.Nq), a1 = min(max(p.cu_q[b + 1], a0), p.Nq);
+    const int c0 = min(max(p.cu_k[b], 0), p.Nk), c1 = min(max(p.cu_k[b + 1], c0), p.Nk);
+    q_lo = a0;
+    Nq = a1 - a0;
+    k_lo = c0;
+    Nk = c1 - c0;
+    if (qt * kBr >= Nq) return;
+  }
+  const float* qg = static_cast<const float*>(p.q) + (varlen ? q_lo * p.q_sn : b * p.q_sb) + h * p.q_sh;
+  const float* kgp = static_cast<const float*>(p.k) + (varlen ? k_lo * p.k_sn : b * p.k_sb) + hk * p.k_sh;
+  const float* vgp = static_cast<const float*>(p.v) + (varlen ? k_lo * p.v_sn : b * p.v_sb) + hk * p.v_sh;
   const int q0 = qt * kBr;
   const int qw0 = q0 + wave * 16;
   const int my_q = qw0 + l16;
@@ -210,13 +224,14 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdParams p, TileMap 
   l_tot = xor32_sum(l_tot);
   if (my_q < Nq) {
     const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
-    float* orow = static_cast<float*>(p.o) + b * p.o_sb + h * p.o_sh + (int64_t)my_q * p.o_sn;
+    float* orow = static_cast<float*>(p.o) + (varlen ? q_lo * p.o_sn : b * p.o_sb) + h * p.o_sh +
+                  (int64_t)my_q * p.o_sn;
     // register i of block cb holds column 16cb + 4g + i
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
       *reinterpret_cast<f32x4*>(orow + 16 * cb + 4 * g) = oacc[cb] * inv;
     if (g == 0) {
-      float* lrow = p.lse + b * p.l_sb + h * p.l_sh;
+      float* lrow = p.lse + (varlen ? q_lo : b * p.l_sb) + h * p.l_sh;
       lrow[my_q] = (l_tot > 0.f) ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
     }
   }
@@ -240,7 +255,7 @@ hipError_t launch_d(const FwdParams& p, const TileMap& tm, hipStream_t s) {
 
 int launch_fwd_f32(const FwdParams& p, int d, void* stream) {
   TileMap tm{};
-  tm.n_qtiles = (p.Nq + kBr - 1) / kBr;
+  tm.n_qtiles = ((p.cu_q != nullptr ? p.max_q : p.Nq) + kBr - 1) / kBr;
   const int64_t total = (int64_t)p.B * p.H * tm.n_qtiles;
   tm.total = (int)total;
   tm.per_xcd = (int)((total + 7) / 8);

@@ -52,6 +52,14 @@ struct FwdParams {
   int32_t local;
   int32_t win_left;
   int32_t win_right;
+  // Packed variable-length sequences: non-null cu_q / cu_k (device, int32
+  // [B + 1]) give sequence b the rows [cu_q[b], cu_q[b+1]) of the packed
+  // query rows (Nq of them in all) and the keys [cu_k[b], cu_k[b+1]) of the
+  // packed keys (Nk in all); B counts sequences, the batch strides are 0 and
+  // the grid covers max_q rows per sequence.
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int32_t max_q;
 };
 
 // How the flat workgroup index maps onto (batch, head, query tile).

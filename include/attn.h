@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 3
+#define ATTN_ABI_VERSION 4
 
 typedef enum {
   ATTN_OK = 0,
@@ -197,6 +197,49 @@ attn_status_t attn_fwd_splitkv(const attn_tensor_t* q, const attn_tensor_t* k,
                                int causal, float scale, int32_t num_splits, void* workspace,
                                int64_t workspace_bytes, const attn_tensor_t* o,
                                const attn_tensor_t* lse, void* stream);
+
+/*
+ * attn_fwd_varlen - the forward over packed variable-length sequences.
+ *
+ * A ragged batch is stored without padding: the rows of all sequences are
+ * concatenated (the [total, heads, d] layout, token-major), and
+ * cumulative offsets say where each sequence starts, so padding is never
+ * computed ("flash-attention" (stanleyjacob.dev), Part II "Variable-length
+ * batches: stop padding", and Lab 5; "FlashAttention, Explained", section
+ * 14, document masking of packed batches). Sequence s attends its own
+ * rows to its own keys only:
+ *
+ *     rows  [cu_seqlens_q[s], cu_seqlens_q[s+1])  of q, o, lse
+ *     keys  [cu_seqlens_k[s], cu_seqlens_k[s+1])  of k, v
+ *
+ * with the same function per sequence as attn_fwd, including the
+ * bottom-right causal alignment and the window of that sequence's lengths.
+ *
+ *   q    [1, H,  total_q, d]  bf16 or f32 (a [total_q, H, d] tensor is the
+ *                             view with strides {., d, H*d, 1})
+ *   k, v [1, Hk, total_k, d]  same dtype; Hk divides H
+ *   cu_seqlens_q, cu_seqlens_k  DEVICE int32[num_seqs + 1], non-decreasing,
+ *                             starting at 0 and ending at total_q / total_k.
+ *                             Values outside [0, total] are clamped (the
+ *                             kernels never leave the tensors), but then
+ *                             the result is unspecified.
+ *   num_seqs                  number of sequences (>= 0)
+ *   max_seqlen_q              at least the longest query sequence (sizes
+ *                             the grid; rows past it are not computed)
+ *   window_mask               NULL, or an attn_mask_t with only the window
+ *                             fields used (bias and kv_len must be NULL)
+ *   causal, scale, stream     as for attn_fwd
+ *   o    [1, H, total_q, d]   output, same dtype as q
+ *   lse  [1, H, total_q, 1]   output, float32; stride[2] must be 1
+ *
+ * Rows of o / lse outside every sequence are not written. Layout,
+ * alignment and error rules are those of attn_fwd.
+ */
+attn_status_t attn_fwd_varlen(const attn_tensor_t* q, const attn_tensor_t* k,
+                              const attn_tensor_t* v, const int32_t* cu_seqlens_q,
+                              const int32_t* cu_seqlens_k, int32_t num_seqs, int32_t max_seqlen_q,
+                              const attn_mask_t* window_mask, int causal, float scale,
+                              const attn_tensor_t* o, const attn_tensor_t* lse, void* stream);
 
 /* Text describing the last non-OK status returned on the calling thread
    ("" if none). The pointer stays valid until the next call on this thread. */

@@ -28,6 +28,7 @@ Every function here is pinned by a test under ``tests/`` (see
 from .attention import (  # noqa: F401
     attention_forward,
     attention_rows,
+    attention_varlen,
     score_matrix,
     masked_softmax,
     online_softmax_scalar,

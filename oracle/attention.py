@@ -95,13 +95,16 @@ def masked_softmax(s) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
     """Row softmax with the max subtracted first (the "safe" softmax).
 
     Returns (P, m, l): P = exp(S - m) / l with m the row maximum and l the
-    row sum of exp(S - m). A row that is entirely -inf gets P = 0, m = -inf,
-    l = 0 rather than NaN.
+    row sum of exp(S - m). A row that is entirely -inf, or has no keys at
+    all, gets P = 0, m = -inf, l = 0 rather than NaN.
 
     [Understanding FlashAttention Pt 1, §2.2 "Softmax Is the Difficult Part of
      Streaming"; FlashAttention, Explained, §9.]
     """
     s = _f64(s)
+    if s.shape[-1] == 0:                      # no keys at all: an empty row
+        z = np.zeros(s.shape[:-1])
+        return np.zeros(s.shape), np.full(s.shape[:-1], -np.inf), z
     m = s.max(axis=-1)
     dead = ~np.isfinite(m) & (m < 0)          # m == -inf: every key masked
     m_ref = np.where(dead, 0.0, m)
@@ -184,6 +187,37 @@ def attention_rows(q, k, v, rows: Iterable[Sequence[int]], *, scale, bias=None,
         for r, (n, _) in enumerate(items):
             o[n] = oh[r]
             lse[n] = lh[r]
+    return o, lse
+
+
+def attention_varlen(q, k, v, cu_q, cu_k, *, scale, causal=False, window=None):
+    """The forward over packed variable-length sequences.
+
+    q: [Tq, H, d], k: [Tk, Hk, d], v: [Tk, Hk, dv] (token-major packing);
+    cu_q, cu_k: num_seqs + 1 cumulative offsets. Sequence s is plain
+    attention (``attention_forward``, with its causal alignment and window)
+    of rows q[cu_q[s]:cu_q[s+1]] against keys k[cu_k[s]:cu_k[s+1]]; query
+    head h reads key/value head h // (H / Hk). Returns (O [Tq, H, dv],
+    LSE [H, Tq]); rows outside every sequence are NaN.
+    [flash-attention (stanleyjacob.dev), Part II, variable-length batches
+     and grouped-query attention.]
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    Tq, H, _ = q.shape
+    rep = H // k.shape[1]
+    o = np.full((Tq, H, v.shape[2]), np.nan)
+    lse = np.full((H, Tq), np.nan)
+    for s in range(len(cu_q) - 1):
+        a0, a1 = int(cu_q[s]), int(cu_q[s + 1])
+        c0, c1 = int(cu_k[s]), int(cu_k[s + 1])
+        if a1 <= a0:
+            continue
+        qs = q[a0:a1].transpose(1, 0, 2)[None]                      # [1, H, n, d]
+        ks = np.repeat(k[c0:c1].transpose(1, 0, 2), rep, axis=0)[None]
+        vs = np.repeat(v[c0:c1].transpose(1, 0, 2), rep, axis=0)[None]
+        os_, ls_ = attention_forward(qs, ks, vs, scale=scale, causal=causal, window=window)
+        o[a0:a1] = os_[0].transpose(1, 0, 2)
+        lse[:, a0:a1] = ls_[0]
     return o, lse
 
 

@@ -35,7 +35,7 @@ def test_exports_every_declared_function():
     names = _declared_functions()
     assert names == ["attn_abi_version", "attn_fwd", "attn_fwd_splitkv",
                      "attn_fwd_splitkv_num_splits", "attn_fwd_splitkv_workspace_size",
-                     "attn_last_error"]
+                     "attn_fwd_varlen", "attn_last_error"]
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", ea.library_path()],
@@ -272,3 +272,37 @@ def test_splitkv_rejections():
     assert "6 splits" in ea.last_error()
     # the common argument checks still apply
     assert _split_call(shape=(2, 4, 1, 96)) == ea.ATTN_ERR_UNSUPPORTED
+
+
+# ------------------------------------------------------------ packed sequences
+
+def _varlen_call(shape0=1, cu_q=0x80000, cu_k=0x90000, num_seqs=3, max_q=64, mask=None,
+                 dtype=ea.ATTN_BF16):
+    T, H, d = 256, 4, 64
+    q = _desc((shape0, H, T, d), dtype, stride=[T * H * d, d, H * d, 1])
+    k = _desc((shape0, H, T, d), dtype, data=0x20000, stride=[T * H * d, d, H * d, 1])
+    v = _desc((shape0, H, T, d), dtype, data=0x30000, stride=[T * H * d, d, H * d, 1])
+    o = _desc((shape0, H, T, d), dtype, data=0x40000, stride=[T * H * d, d, H * d, 1])
+    lse = _desc((shape0, H, T, 1), ea.ATTN_F32, data=0x50000, stride=[H * T, T, 1, 1])
+    lib = _lib()
+    return lib.attn_fwd_varlen(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v),
+                               ctypes.c_void_p(cu_q), ctypes.c_void_p(cu_k), num_seqs, max_q,
+                               ctypes.byref(mask) if mask is not None else None, 0, 0.125,
+                               ctypes.byref(o), ctypes.byref(lse), None)
+
+
+def test_varlen_rejections():
+    # every call below is refused on the host before any launch
+    assert _varlen_call(shape0=2) == ea.ATTN_ERR_INVALID
+    assert "packed" in ea.last_error()
+    assert _varlen_call(cu_q=0) == ea.ATTN_ERR_INVALID
+    assert _varlen_call(cu_k=0x90002) == ea.ATTN_ERR_INVALID
+    assert _varlen_call(num_seqs=-1) == ea.ATTN_ERR_INVALID
+    assert _varlen_call(max_q=-5) == ea.ATTN_ERR_INVALID
+    m = ea.AttnMask()
+    m.kv_len = 0x70000
+    assert _varlen_call(mask=m) == ea.ATTN_ERR_INVALID
+    assert "kv_len" in ea.last_error()
+    # nothing to compute: OK without touching the device
+    assert _varlen_call(num_seqs=0) == ea.ATTN_OK
+    assert _varlen_call(max_q=0) == ea.ATTN_OK

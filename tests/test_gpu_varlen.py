@@ -1,0 +1,156 @@
+"""Parity of the packed variable-length forward with the oracle.
+
+attn_fwd_varlen on token-major packed tensors against the oracle's
+``attention_varlen`` (plain attention per sequence) on the same seeded
+bytes, at the bars of the other parity tests. Cases: empty sequences, one-
+row sequences, lengths that span several tiles with ragged tails, causal
+and not, both head dimensions and dtypes, grouped K/V heads, different query
+and key offsets per sequence (bottom-right causal alignment per sequence),
+a window, rows past the last sequence left untouched, a generous
+max_seqlen_q, offsets outside the tensors (clamped: no access leaves them),
+and the packed workload at full size on sampled rows. [flash-attention
+(stanleyjacob.dev), Part II "Variable-length batches: stop padding", Lab 5.]
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+import exact_io_aware_06_amd as ea
+
+from tests.test_gpu_parity import _banner, compare
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("these tests need a GPU")
+    ea.load_library()
+    yield
+
+
+def _packed(lens_q, lens_k, H, Hk, d, dtype, seed):
+    g = torch.Generator().manual_seed(seed)
+    st = torch.bfloat16 if dtype == "bf16" else torch.float32
+    cu_q = torch.tensor([0] + list(np.cumsum(lens_q)), dtype=torch.int32)
+    cu_k = torch.tensor([0] + list(np.cumsum(lens_k)), dtype=torch.int32)
+    q = torch.randn(int(cu_q[-1]), H, d, generator=g).to(st)
+    k = torch.randn(int(cu_k[-1]), Hk, d, generator=g).to(st)
+    v = torch.randn(int(cu_k[-1]), Hk, d, generator=g).to(st)
+    return q, k, v, cu_q, cu_k
+
+
+def _run(q, k, v, cu_q, cu_k, max_q, causal, window=None, scale=None, out=None, lse=None):
+    o, l = ea.attn_fwd_varlen(q.cuda(), k.cuda(), v.cuda(), cu_q.cuda(), cu_k.cuda(), max_q,
+                              causal=causal, window=window, scale=scale, out=out, lse=lse)
+    torch.cuda.synchronize()
+    return o, l
+
+
+CASES = [
+    # (lens_q, lens_k, H, Hk, d, dtype, causal)
+    ([300, 1, 0, 513, 64, 1000], None, 2, 2, 128, "bf16", True),
+    ([300, 1, 0, 513, 64, 1000], None, 2, 2, 64, "bf16", False),
+    ([257, 700, 5], None, 4, 1, 128, "bf16", True),          # grouped K/V heads
+    ([17, 200], [90, 650], 2, 2, 64, "bf16", True),          # fewer queries than keys
+    ([40, 3], [10, 0], 2, 2, 128, "bf16", False),            # a sequence without keys
+    ([129, 31, 260], None, 2, 2, 64, "f32", True),
+    ([70, 200], [100, 150], 2, 1, 128, "f32", False),
+]
+
+
+@pytest.mark.parametrize("lens_q,lens_k,H,Hk,d,dtype,causal", CASES)
+def test_varlen_matches_oracle(lens_q, lens_k, H, Hk, d, dtype, causal):
+    lens_k = lens_q if lens_k is None else lens_k
+    _banner(f"varlen q={lens_q} k={lens_k} H={H} Hk={Hk} d={d} {dtype} causal={causal}")
+    q, k, v, cu_q, cu_k = _packed(lens_q, lens_k, H, Hk, d, dtype, seed=sum(lens_q) + d)
+    o, lse = _run(q, k, v, cu_q, cu_k, max(lens_q), causal)
+    ro, rl = oracle.attention_varlen(q.double().numpy(), k.double().numpy(), v.double().numpy(),
+                                     cu_q.numpy(), cu_k.numpy(), scale=d ** -0.5, causal=causal)
+    compare(o.double().cpu().numpy(), lse.double().cpu().numpy().T, ro, rl.T, dtype,
+            f"varlen {lens_q}")
+
+
+def test_varlen_window():
+    lens = [900, 77, 600]
+    q, k, v, cu_q, cu_k = _packed(lens, lens, 2, 2, 128, "bf16", seed=61)
+    for causal, window in ((True, (150, 0)), (False, (64, 100))):
+        _banner(f"varlen window causal={causal} window={window}")
+        o, lse = _run(q, k, v, cu_q, cu_k, max(lens), causal, window=window)
+        ro, rl = oracle.attention_varlen(q.double().numpy(), k.double().numpy(),
+                                         v.double().numpy(), cu_q.numpy(), cu_k.numpy(),
+                                         scale=128 ** -0.5, causal=causal, window=window)
+        compare(o.double().cpu().numpy(), lse.double().cpu().numpy().T, ro, rl.T, "bf16",
+                f"varlen window {window}")
+
+
+def test_varlen_rows_outside_sequences_untouched_and_generous_max():
+    # the sequences cover rows [0, 400) of 420 packed rows (offsets are
+    # contiguous, so rows past the last offset are the only uncovered ones);
+    # those rows of o and lse keep their contents. The second sequence has
+    # 50 rows and no keys (zero rows, -inf LSE).
+    q, k, v, _, _ = _packed([420], [420], 2, 2, 64, "bf16", seed=62)
+    cu_q = torch.tensor([0, 250, 300, 400], dtype=torch.int32)
+    cu_k = torch.tensor([0, 250, 250, 400], dtype=torch.int32)
+    out = torch.full((420, 2, 64), 7.0, dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((2, 420), 7.0, dtype=torch.float32, device="cuda")
+    o, l = _run(q, k, v, cu_q, cu_k, 4096, True, out=out, lse=lse)
+    oc, lc = o.cpu(), l.cpu()
+    assert torch.all(oc[400:] == 7.0) and torch.all(lc[:, 400:] == 7.0)
+    ro, rl = oracle.attention_varlen(q.double().numpy(), k.double().numpy(), v.double().numpy(),
+                                     cu_q.numpy(), cu_k.numpy(), scale=0.125, causal=True)
+    compare(oc.double().numpy()[:400], lc.double().numpy().T[:400], ro[:400], rl.T[:400],
+            "bf16", "varlen partial cover")
+
+
+def test_varlen_offsets_outside_tensors_are_clamped():
+    # Offsets outside the packed tensors and a decreasing pair: the kernels
+    # clamp each sequence to start = clamp(cu[s], 0, total), end =
+    # clamp(cu[s+1], start, total), so every access stays inside the tensors.
+    # Here that gives [0, 120), an empty sequence, and [80, 200); rows both
+    # cover are unspecified, the rest follow the clamped sequences.
+    q, k, v, _, _ = _packed([200], [200], 2, 2, 128, "bf16", seed=63)
+    cu = torch.tensor([-7, 120, 80, 1 << 30], dtype=torch.int32)
+    o, l = _run(q, k, v, cu, cu, 256, False)
+    oc, lc = o.cpu().double().numpy(), l.cpu().double().numpy().T
+    assert not np.isnan(oc).any()
+    f = lambda t: t.double().numpy()
+    for lo, hi, keep in ((0, 120, np.r_[0:80]), (80, 200, np.r_[120:200])):
+        ro, rl = oracle.attention_varlen(f(q), f(k), f(v), np.array([lo, hi]), np.array([lo, hi]),
+                                         scale=128 ** -0.5)
+        compare(oc[keep], lc[keep], ro[keep], rl.T[keep], "bf16",
+                f"varlen clamped offsets [{lo}, {hi})")
+
+
+@pytest.mark.parametrize("name", sorted(workloads.VARLEN))
+def test_varlen_full_size_sampled(name):
+    w = workloads.VARLEN[name]
+    _banner(f"varlen full {name}")
+    inp = workloads.make_varlen_inputs(w)
+    cu = inp["cu"]
+    o, lse = _run(inp["q"], inp["k"], inp["v"], cu, cu, inp["max_len"], w.causal,
+                  scale=inp["scale"])
+    oc, lc = o.cpu(), lse.cpu()
+    assert not torch.isnan(oc.float()).any() and torch.isfinite(lc).all()
+    r = np.random.default_rng(w.seed)
+    c = cu.tolist()
+    go, gl, ro, rl = [], [], [], []
+    for s in list(range(w.B)):
+        n = c[s + 1] - c[s]
+        idx = sorted(set([0, n - 1] + [int(x) for x in r.integers(0, n, 2)]))
+        h = int(r.integers(w.H))
+        f = lambda t: t[c[s]:c[s + 1], h].double().numpy()[None, None]
+        oo, ll = oracle.attention_rows(f(inp["q"]), f(inp["k"]), f(inp["v"]),
+                                       [(0, 0, i) for i in idx], scale=inp["scale"],
+                                       causal=w.causal)
+        for j, i in enumerate(idx):
+            go.append(oc[c[s] + i, h].double().numpy())
+            gl.append(float(lc[h, c[s] + i]))
+            ro.append(oo[j])
+            rl.append(ll[j])
+    compare(np.stack(go), np.array(gl), np.stack(ro), np.array(rl), w.dtype,
+            f"varlen full {name} sampled")

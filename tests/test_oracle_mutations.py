@@ -18,7 +18,7 @@ from tests import test_oracle_pins as pins
 
 _orig = {name: getattr(oa, name) for name in (
     "score_matrix", "masked_softmax", "_head_forward", "online_softmax_blocked",
-    "online_softmax_scalar", "merge_partials")}
+    "online_softmax_scalar", "merge_partials", "attention_varlen")}
 
 
 def _scores(variant):
@@ -165,6 +165,23 @@ def _merge(variant):
     return merge_partials
 
 
+def _varlen(variant):
+    def attention_varlen(q, k, v, cu_q, cu_k, *, scale, causal=False, window=None):
+        if variant == "varlen_keys_from_query_offsets":
+            return _orig["attention_varlen"](q, k, v, cu_q, cu_q, scale=scale, causal=causal,
+                                             window=window)
+        if variant == "varlen_keys_of_all_sequences":
+            n = len(cu_k) - 1
+            whole = np.array([0] + [int(cu_k[-1])] * n)
+            starts = np.array([0] * (n + 1))
+            o, lse = _orig["attention_varlen"](q, k, v, cu_q, whole, scale=scale,
+                                               causal=causal, window=window)
+            return o, lse
+        return _orig["attention_varlen"](q, k, v, cu_q, cu_k, scale=scale, causal=causal,
+                                         window=window)
+    return attention_varlen
+
+
 MUTATIONS = {
     "scale_squared": ("score_matrix", _scores),
     "drop_bias": ("score_matrix", _scores),
@@ -185,6 +202,8 @@ MUTATIONS = {
     "blocked_no_rescale_a": ("online_softmax_blocked", _blocked),
     "scalar_no_rescale_a": ("online_softmax_scalar", _scalar),
     "merge_plain_mean": ("merge_partials", _merge),
+    "varlen_keys_from_query_offsets": ("attention_varlen", _varlen),
+    "varlen_keys_of_all_sequences": ("attention_varlen", _varlen),
 }
 
 

@@ -461,3 +461,75 @@ def test_window_special_cases():
     # causal and a right bound: the causal side wins
     o, lse = oracle.attention_forward(q, k, v, scale=0.5, causal=True, window=(-1, 3))
     assert np.array_equal(o, causal[0])
+
+
+# ------------------------------------------------------- packed sequences
+def _varlen_case(seed, lens_q, lens_k, H=3, Hk=3, d=4):
+    r = _rng(seed)
+    cu_q = np.concatenate([[0], np.cumsum(lens_q)]).astype(np.int64)
+    cu_k = np.concatenate([[0], np.cumsum(lens_k)]).astype(np.int64)
+    q = r.normal(size=(int(cu_q[-1]), H, d))
+    k = r.normal(size=(int(cu_k[-1]), Hk, d))
+    v = r.normal(size=(int(cu_k[-1]), Hk, 2))
+    return q, k, v, cu_q, cu_k
+
+
+def test_varlen_equals_padded_batch_with_key_lengths():
+    # Another route to the same rows: pad every sequence to the longest, mask
+    # the padded keys with kv_len, and read back the real rows only.
+    lens = [5, 1, 7, 0, 3]
+    q, k, v, cu_q, cu_k = _varlen_case(50, lens, lens)
+    L = max(lens)
+    for causal in (False, True):
+        o, lse = oracle.attention_varlen(q, k, v, cu_q, cu_k, scale=0.6, causal=causal)
+        qp = np.zeros((len(lens), 3, L, 4))
+        kp = np.zeros((len(lens), 3, L, 4))
+        vp = np.zeros((len(lens), 3, L, 2))
+        for s, n in enumerate(lens):
+            qp[s, :, :n] = q[cu_q[s]:cu_q[s + 1]].transpose(1, 0, 2)
+            kp[s, :, :n] = k[cu_k[s]:cu_k[s + 1]].transpose(1, 0, 2)
+            vp[s, :, :n] = v[cu_k[s]:cu_k[s + 1]].transpose(1, 0, 2)
+        po, pl = oracle.attention_forward(qp, kp, vp, scale=0.6, kv_len=lens, causal=causal)
+        for s, n in enumerate(lens):
+            for i in range(n):
+                row = cu_q[s] + i
+                assert np.allclose(o[row], po[s, :, i], atol=1e-14)
+                assert np.allclose(lse[:, row], pl[s, :, i], atol=1e-14)
+
+
+def test_varlen_single_sequence_and_unequal_lengths():
+    # one sequence covering the packed tensors is the plain forward; with
+    # fewer query rows than keys each sequence keeps its own bottom-right
+    # causal alignment (its last query sees all of its keys)
+    q, k, v, cu_q, cu_k = _varlen_case(51, [6], [6])
+    o, lse = oracle.attention_varlen(q, k, v, cu_q, cu_k, scale=0.4, causal=True)
+    ro, rl = oracle.attention_forward(q.transpose(1, 0, 2)[None], k.transpose(1, 0, 2)[None],
+                                      v.transpose(1, 0, 2)[None], scale=0.4, causal=True)
+    assert np.allclose(o, ro[0].transpose(1, 0, 2), atol=1e-15)
+    assert np.allclose(lse, rl[0], atol=1e-15)
+    q, k, v, cu_q, cu_k = _varlen_case(52, [2, 3], [4, 6])
+    o, lse = oracle.attention_varlen(q, k, v, cu_q, cu_k, scale=0.4, causal=True)
+    for s in range(2):
+        last = cu_q[s + 1] - 1
+        ro, rl = oracle.attention_forward(q[last:last + 1].transpose(1, 0, 2)[None],
+                                          k[cu_k[s]:cu_k[s + 1]].transpose(1, 0, 2)[None],
+                                          v[cu_k[s]:cu_k[s + 1]].transpose(1, 0, 2)[None],
+                                          scale=0.4)
+        assert np.allclose(o[last], ro[0, :, 0], atol=1e-14)
+    # a sequence with no keys: zero rows, -inf LSE
+    q, k, v, cu_q, cu_k = _varlen_case(53, [2, 2], [3, 0])
+    o, lse = oracle.attention_varlen(q, k, v, cu_q, cu_k, scale=1.0)
+    assert np.all(o[2:] == 0.0) and np.all(lse[:, 2:] == -np.inf)
+
+
+def test_varlen_grouped_heads():
+    # query head h reads key/value head h // (H / Hk): with Hk = 1 every
+    # query head of a sequence sees the same keys
+    q, k, v, cu_q, cu_k = _varlen_case(54, [3, 4], [5, 2], H=4, Hk=1)
+    o, lse = oracle.attention_varlen(q, k, v, cu_q, cu_k, scale=0.5)
+    for s in range(2):
+        for h in range(4):
+            ro, rl = oracle.attention_forward(
+                q[cu_q[s]:cu_q[s + 1], h][None, None], k[cu_k[s]:cu_k[s + 1], 0][None, None],
+                v[cu_k[s]:cu_k[s + 1], 0][None, None], scale=0.5)
+            assert np.allclose(o[cu_q[s]:cu_q[s + 1], h], ro[0, 0], atol=1e-14)

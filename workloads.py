@@ -23,6 +23,12 @@ Recipe (fixed here, stated again in the design notes):
   d=128) with a causal window of 4096 keys (a common local-attention size;
   the pages' example is 128 neighbouring tokens, too few tiles per row to
   measure anything but launch overhead).
+* Packed variable-length batches (the pages' Lab 5: a ragged batch with
+  lengths from a lognormal capped at 4096): the B sequence lengths are drawn
+  first, n = clamp(round(exp(mu + sigma * z)), lo, cap) with z ~ N(0, 1),
+  then Q, K, V packed token-major as [total, heads, d]; cu_seqlens are the
+  cumulative lengths. Every sequence attends to itself (same lengths for
+  queries and keys).
 """
 
 from __future__ import annotations
@@ -52,6 +58,7 @@ class Workload:
     seed: int = 0
     Hk: Optional[int] = None                # key/value heads (None: H)
     window: Optional[tuple] = None          # (left, right) sliding window
+    varlen: Optional[tuple] = None          # (mu, sigma, lo, cap): packed lognormal lengths
 
     @property
     def kv_heads(self) -> int:
@@ -76,6 +83,8 @@ class Workload:
             "causal": self.causal, "scale": self.softmax_scale,
             "seed": self.seed, **({} if self.Hk is None else {"Hk": self.Hk}),
             **({} if self.window is None else {"window": list(self.window)}),
+            **({} if self.varlen is None else {"lengths": "lognormal(mu=%g, sigma=%g) in [%d, %d]"
+                                               % tuple(self.varlen), "sequences": self.B}),
         }
 
     def kv_bytes(self) -> int:
@@ -123,7 +132,14 @@ WINDOW = {
                                              seed=8),
 }
 
-ALL = {**CONFIGS, **DECODE, **WINDOW}
+# Packed variable-length sequences (Nq = Nk = the length cap).
+VARLEN = {
+    "varlen_s16_h16_d128_lognormal_causal": Workload(
+        "varlen_s16_h16_d128_lognormal_causal", 16, 16, 4096, 4096, 128, causal=True,
+        varlen=(math.log(1024.0), 0.8, 32, 4096), seed=9),
+}
+
+ALL = {**CONFIGS, **DECODE, **WINDOW, **VARLEN}
 
 
 def _storage(dtype: str):
@@ -169,6 +185,30 @@ def make_inputs(w: Workload, seed: Optional[int] = None) -> dict:
         "v": v.to(st).contiguous(), "bias": bias, "kv_len": kv_len,
         "causal": bool(w.causal), "scale": scale32,
     }
+
+
+def make_varlen_inputs(w: Workload, seed: Optional[int] = None) -> dict:
+    """Draw a packed variable-length batch for workload ``w`` (w.varlen set).
+
+    Returns q [T, H, d], k, v [T, Hk, d] (storage dtype, contiguous), lens
+    (int64 [B]), cu (int32 [B + 1] cumulative lengths), max_len, causal,
+    scale.
+    """
+    g = torch.Generator().manual_seed(w.seed if seed is None else int(seed))
+    mu, sigma, lo, cap = w.varlen
+    z = torch.randn((w.B,), generator=g, dtype=torch.float32)
+    lens = torch.exp(mu + sigma * z).round().clamp(lo, cap).to(torch.int64)
+    T = int(lens.sum())
+    st = _storage(w.dtype)
+    q = torch.randn((T, w.H, w.d), generator=g, dtype=torch.float32)
+    k = torch.randn((T, w.kv_heads, w.d), generator=g, dtype=torch.float32)
+    v = torch.randn((T, w.kv_heads, w.d), generator=g, dtype=torch.float32)
+    cu = torch.zeros(w.B + 1, dtype=torch.int64)
+    cu[1:] = torch.cumsum(lens, 0)
+    scale32 = float(torch.tensor(w.softmax_scale, dtype=torch.float32))
+    return {"q": q.to(st).contiguous(), "k": k.to(st).contiguous(), "v": v.to(st).contiguous(),
+            "lens": lens, "cu": cu.to(torch.int32), "max_len": int(lens.max()),
+            "causal": bool(w.causal), "scale": scale32}
 
 
 def small(name: str, **overrides) -> Workload:
