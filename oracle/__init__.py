@@ -26,6 +26,7 @@ Every function here is pinned by a test under ``tests/`` (see
 """
 
 from .attention import (  # noqa: F401
+    attention_backward,
     attention_forward,
     attention_rows,
     attention_varlen,

@@ -221,6 +221,47 @@ def attention_varlen(q, k, v, cu_q, cu_k, *, scale, causal=False, window=None):
     return o, lse
 
 
+def attention_backward(q, k, v, do, *, scale, bias=None, kv_len=None, causal=False,
+                       window=None):
+    """Gradients of the forward with respect to Q, K and V, in float64.
+
+    For an upstream gradient dO of O = P V with P = softmax_row(S),
+    S = scale * Q K^T + B (masks as -inf):
+        dV = P^T dO,   dP = dO V^T,   D_i = sum_j P_ij dP_ij,
+        dS = P o (dP - D[:, None]),   dQ = scale * dS K,   dK = scale * dS^T Q.
+    A masked pair has P_ij = 0 and therefore dS_ij = 0; a row with no
+    visible key contributes nothing. q, do: [B, H, Nq, d], k, v: [B, Hk,
+    Nk, d] with query head h reading key/value head h // (H / Hk); dK and dV
+    of a key/value head sum over the query heads that read it. The bias is a
+    constant here (no gradient is returned for it).
+    Returns (dQ, dK, dV) with the shapes of q, k, v.
+    [Understanding FlashAttention Pt 1, §3.6; FlashAttention, Explained,
+     §17; FlashAttention: Mathematical Foundations..., §4.]
+    """
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    B, H, Nq, _ = q.shape
+    Hk = k.shape[1]
+    rep = H // Hk
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b in range(B):
+        vk = None if kv_len is None else int(kv_len[b])
+        for h in range(H):
+            hk = h // rep
+            s = score_matrix(q[b, h], k[b, hk], scale, _bias_for(bias, b, h), vk, causal,
+                             None, Nq, window)
+            p, _, _ = masked_softmax(s)
+            dvh = p.T @ do[b, h]
+            dp = do[b, h] @ v[b, hk].T
+            dd = (p * dp).sum(axis=1)
+            ds = p * (dp - dd[:, None])
+            dq[b, h] = scale * (ds @ k[b, hk])
+            dk[b, hk] += scale * (ds.T @ q[b, h])
+            dv[b, hk] += dvh
+    return dq, dk, dv
+
+
 def online_softmax_scalar(scores, values):
     """One query row, one key at a time: the online normaliser with a value
     accumulator.

@@ -18,7 +18,7 @@ from tests import test_oracle_pins as pins
 
 _orig = {name: getattr(oa, name) for name in (
     "score_matrix", "masked_softmax", "_head_forward", "online_softmax_blocked",
-    "online_softmax_scalar", "merge_partials", "attention_varlen")}
+    "online_softmax_scalar", "merge_partials", "attention_varlen", "attention_backward")}
 
 
 def _scores(variant):
@@ -182,6 +182,35 @@ def _varlen(variant):
     return attention_varlen
 
 
+def _backward(variant):
+    def attention_backward(q, k, v, do, *, scale, bias=None, kv_len=None, causal=False,
+                           window=None):
+        q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
+        B, H, Nq, _ = q.shape
+        rep = H // k.shape[1]
+        dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+        for b in range(B):
+            vk = None if kv_len is None else int(kv_len[b])
+            for h in range(H):
+                hk = h // rep
+                s = oa.score_matrix(q[b, h], k[b, hk], scale, oa._bias_for(bias, b, h), vk,
+                                    causal, None, Nq, window)
+                p, _, _ = oa.masked_softmax(s)
+                dp = do[b, h] @ v[b, hk].T
+                dd = 0.0 if variant == "bwd_drop_D" else (p * dp).sum(axis=1)[:, None]
+                ds = p * (dp - dd)
+                dq[b, h] = (1.0 if variant == "bwd_dq_unscaled" else scale) * (ds @ k[b, hk])
+                dk[b, hk] += scale * ((ds @ q[b, h]) if variant == "bwd_dk_not_transposed"
+                                      and ds.shape[0] == ds.shape[1] else ds.T @ q[b, h])
+                dv[b, hk] += (p @ do[b, h] if variant == "bwd_dv_p_not_transposed"
+                              and p.shape[0] == p.shape[1] else p.T @ do[b, h])
+                if variant == "bwd_gqa_last_head_only" and rep > 1 and h % rep != rep - 1:
+                    dk[b, hk] *= 0.0
+                    dv[b, hk] *= 0.0
+        return dq, dk, dv
+    return attention_backward
+
+
 MUTATIONS = {
     "scale_squared": ("score_matrix", _scores),
     "drop_bias": ("score_matrix", _scores),
@@ -203,6 +232,11 @@ MUTATIONS = {
     "scalar_no_rescale_a": ("online_softmax_scalar", _scalar),
     "merge_plain_mean": ("merge_partials", _merge),
     "varlen_keys_from_query_offsets": ("attention_varlen", _varlen),
+    "bwd_drop_D": ("attention_backward", _backward),
+    "bwd_dq_unscaled": ("attention_backward", _backward),
+    "bwd_dk_not_transposed": ("attention_backward", _backward),
+    "bwd_dv_p_not_transposed": ("attention_backward", _backward),
+    "bwd_gqa_last_head_only": ("attention_backward", _backward),
     "varlen_keys_of_all_sequences": ("attention_varlen", _varlen),
 }
 

@@ -533,3 +533,95 @@ def test_varlen_grouped_heads():
                 q[cu_q[s]:cu_q[s + 1], h][None, None], k[cu_k[s]:cu_k[s + 1], 0][None, None],
                 v[cu_k[s]:cu_k[s + 1], 0][None, None], scale=0.5)
             assert np.allclose(o[cu_q[s]:cu_q[s + 1], h], ro[0, 0], atol=1e-14)
+
+
+# ----------------------------------------------------------------- backward
+def _loss(q, k, v, do, **kw):
+    # L = sum(O o dO): its gradient with respect to O is dO
+    o, _ = oracle.attention_forward(q, k, v, **kw)
+    return float((o * do).sum())
+
+
+def _finite_difference(f, x, eps=1e-6):
+    g = np.zeros_like(x)
+    it = np.nditer(x, flags=["multi_index"])
+    for _ in it:
+        idx = it.multi_index
+        old = x[idx]
+        x[idx] = old + eps
+        up = f()
+        x[idx] = old - eps
+        dn = f()
+        x[idx] = old
+        g[idx] = (up - dn) / (2 * eps)
+    return g
+
+
+def test_backward_matches_finite_differences():
+    # central differences of L = sum(O o dO) on tiny inputs: an independent
+    # route to the gradients (no softmax Jacobian written anywhere)
+    r = _rng(70)
+    cases = [dict(causal=False), dict(causal=True),
+             dict(bias=r.normal(size=(1, 2, 4, 5)) * 0.5, kv_len=[4, 3]),
+             dict(window=(1, 1)), dict(causal=True, window=(2, 0))]
+    for nq, nk in ((4, 5), (4, 4)):          # a square case too (a transposed P is square)
+        for kw in cases:
+            if nk == 4 and "bias" in kw:
+                continue
+            q = r.normal(size=(2, 2, nq, 3))
+            k = r.normal(size=(2, 2, nk, 3))
+            v = r.normal(size=(2, 2, nk, 3))
+            do = r.normal(size=(2, 2, nq, 3))
+            dq, dk, dv = oracle.attention_backward(q, k, v, do, scale=0.7, **kw)
+            for x, g in ((q, dq), (k, dk), (v, dv)):
+                fd = _finite_difference(lambda: _loss(q, k, v, do, scale=0.7, **kw), x)
+                assert np.allclose(g, fd, atol=1e-7), kw
+
+
+def test_backward_grouped_heads_sum_over_the_group():
+    # with Hk = 1 the key/value gradient is the sum over the query heads
+    r = _rng(71)
+    q = r.normal(size=(1, 3, 4, 2))
+    k = r.normal(size=(1, 1, 6, 2))
+    v = r.normal(size=(1, 1, 6, 2))
+    do = r.normal(size=(1, 3, 4, 2))
+    dq, dk, dv = oracle.attention_backward(q, k, v, do, scale=0.5, causal=True)
+    fd_k = _finite_difference(lambda: _loss_gqa(q, k, v, do), k)
+    assert np.allclose(dk, fd_k, atol=1e-7)
+    fd_v = _finite_difference(lambda: _loss_gqa(q, k, v, do), v)
+    assert np.allclose(dv, fd_v, atol=1e-7)
+
+
+def _loss_gqa(q, k, v, do):
+    kx = np.repeat(k, q.shape[1] // k.shape[1], axis=1)
+    vx = np.repeat(v, q.shape[1] // v.shape[1], axis=1)
+    return _loss(q, kx, vx, do, scale=0.5, causal=True)
+
+
+def test_backward_identities():
+    # D = rowsum(dO o O) = rowsum(dP o P) (the pages' identity), dS sums to
+    # zero along each row, a fully masked row has zero dQ, keys past kv_len
+    # get zero dK and dV, and a uniform shift of dO along V's row space does
+    # not change dQ / dK (softmax is invariant to it)
+    r = _rng(72)
+    q = r.normal(size=(1, 2, 5, 3))
+    k = r.normal(size=(1, 2, 7, 3))
+    v = r.normal(size=(1, 2, 7, 3))
+    do = r.normal(size=(1, 2, 5, 3))
+    o, _ = oracle.attention_forward(q, k, v, scale=0.9)
+    s = 0.9 * q[0, 0] @ k[0, 0].T
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    dp = do[0, 0] @ v[0, 0].T
+    assert np.allclose((do[0, 0] * o[0, 0]).sum(axis=1), (p * dp).sum(axis=1), atol=1e-14)
+    dq, dk, dv = oracle.attention_backward(q, k, v, do, scale=0.9, kv_len=[4])
+    assert np.all(dk[0, :, 4:] == 0.0) and np.all(dv[0, :, 4:] == 0.0)
+    q2 = r.normal(size=(1, 1, 6, 3))
+    dq2, _, _ = oracle.attention_backward(q2, k[:, :1, :4], v[:, :1, :4], r.normal(size=(1, 1, 6, 3)),
+                                          scale=1.0, causal=True)
+    assert np.all(dq2[0, 0, :2] == 0.0)          # rows 0, 1 see no key (Nq > Nk)
+    c = r.normal(size=(3,))
+    base = oracle.attention_backward(q, k, v, do, scale=0.9)
+    shifted = oracle.attention_backward(q, k, v + c, do, scale=0.9)
+    assert np.allclose(base[0], shifted[0], atol=1e-13)
+    assert np.allclose(base[1], shifted[1], atol=1e-13)
