@@ -23,7 +23,8 @@ import os
 from typing import Optional
 
 __all__ = ["attn_fwd", "attn_fwd_raw", "attn_fwd_splitkv", "attn_fwd_splitkv_raw",
-           "attn_fwd_varlen", "prepare_varlen_call",
+           "attn_fwd_varlen", "prepare_varlen_call", "attn_bwd", "prepare_bwd_call",
+           "bwd_workspace_size",
            "splitkv_num_splits", "splitkv_workspace_size", "prepare_call", "AttnError", "load_library", "library_path",
            "AttnTensor", "AttnMask", "ATTN_OK", "ATTN_ERR_INVALID",
            "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_HIP", "ATTN_BF16", "ATTN_F32"]
@@ -86,6 +87,12 @@ def load_library():
                                     ctypes.c_int32, ctypes.POINTER(AttnMask), ctypes.c_int,
                                     ctypes.c_float, P, P, ctypes.c_void_p]
     lib.attn_fwd_varlen.restype = ctypes.c_int
+    lib.attn_bwd.argtypes = [P, P, P, P, P, P, ctypes.POINTER(AttnMask), ctypes.c_int,
+                             ctypes.c_float, ctypes.c_void_p, ctypes.c_int64, P, P, P,
+                             ctypes.c_void_p]
+    lib.attn_bwd.restype = ctypes.c_int
+    lib.attn_bwd_workspace_size.argtypes = [ctypes.c_int64] * 3
+    lib.attn_bwd_workspace_size.restype = ctypes.c_int64
     lib.attn_last_error.argtypes = []
     lib.attn_last_error.restype = ctypes.c_char_p
     lib.attn_abi_version.argtypes = []
@@ -362,6 +369,63 @@ def prepare_varlen_call(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int,
             raise AttnError(rc, last_error())
 
     return enqueue, out, lse
+
+
+def bwd_workspace_size(B: int, H: int, Nq: int) -> int:
+    """Workspace bytes ``attn_bwd`` needs (-1 for invalid extents)."""
+    return int(load_library().attn_bwd_workspace_size(B, H, Nq))
+
+
+def prepare_bwd_call(q, k, v, o, lse, dout, bias=None, kv_len=None, causal: bool = False,
+                     scale: Optional[float] = None, window=None, dq=None, dk=None, dv=None,
+                     workspace=None):
+    """The backward's arguments marshalled once; returns ``(enqueue, dq, dk,
+    dv)``. Inputs as for ``attn_bwd``."""
+    import torch
+    B, H, Nq, d = q.shape
+    scale, _, lse, (qd, kd, vd, od, ld, mask, keep) = _prepare(q, k, v, bias, kv_len, scale,
+                                                               o, lse, window)
+    if not dout.is_cuda or dout.dtype != q.dtype or dout.shape != q.shape:
+        raise ValueError("dout must be a GPU tensor with q's shape and dtype")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = bwd_workspace_size(B, H, Nq)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    dod, dqd, dkd, dvd = (_torch_desc(t, n) for t, n in ((dout, "dout"), (dq, "dq"),
+                                                          (dk, "dk"), (dv, "dv")))
+    lib = load_library()
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    refs = (qd, kd, vd, od, ld, mask, keep, dod, dqd, dkd, dvd, workspace)
+    args = [ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(vd), ctypes.byref(od),
+            ctypes.byref(ld), ctypes.byref(dod), ctypes.byref(mask) if mask is not None else None,
+            1 if causal else 0, float(scale), ctypes.c_void_p(workspace.data_ptr()),
+            workspace.numel() * workspace.element_size(), ctypes.byref(dqd), ctypes.byref(dkd),
+            ctypes.byref(dvd), ctypes.c_void_p(stream)]
+
+    def enqueue(_refs=refs):
+        rc = lib.attn_bwd(*args)
+        if rc != ATTN_OK:
+            raise AttnError(rc, last_error())
+
+    return enqueue, dq, dk, dv
+
+
+def attn_bwd(q, k, v, o, lse, dout, bias=None, kv_len=None, causal: bool = False,
+             scale: Optional[float] = None, window=None, dq=None, dk=None, dv=None,
+             workspace=None):
+    """Gradients (dq, dk, dv) of ``attn_fwd`` for the upstream gradient dout.
+
+    q, k, v, bias, kv_len, causal, scale, window: as passed to ``attn_fwd``
+    (bfloat16 only); o, lse: what it returned. dk and dv of a key/value head
+    sum over the query heads that read it; no gradient is returned for the
+    bias. Deterministic.
+    """
+    enqueue, dq, dk, dv = prepare_bwd_call(q, k, v, o, lse, dout, bias, kv_len, causal, scale,
+                                           window, dq, dk, dv, workspace)
+    enqueue()
+    return dq, dk, dv
 
 
 def attn_fwd(q, k, v, bias=None, kv_len=None, causal: bool = False,

@@ -19,7 +19,7 @@ LIB = os.path.join(HERE, "libattn.so")
 
 SOURCES = ["attn_abi.cpp", "runtime.hip", "fwd_bf16.hip", "fwd_bf16_split.hip",
            "fwd_bf16_local.hip", "fwd_bf16_local_split.hip", "fwd_bf16_varlen.hip",
-           "fwd_f32.hip", "combine.hip"]
+           "fwd_f32.hip", "combine.hip", "bwd_bf16.hip"]
 
 # -packed-fp32-ops: keep the compiler from emitting v_pk_{add,mul,fma}_f32.
 HIPCC_FLAGS = [

@@ -12,6 +12,8 @@
 
 #include <algorithm>
 #include <cmath>
+#include <tuple>
+#include <utility>
 #include <cstdarg>
 #include <cstdio>
 #include <string>
@@ -352,6 +354,76 @@ attn_status_t attn_fwd_varlen(const attn_tensor_t* q, const attn_tensor_t* k,
   p.max_q = (int32_t)max_q;
   p.q_sb = p.k_sb = p.v_sb = p.o_sb = p.l_sb = 0;
   return launch(p, q->dtype, (int)q->shape[3], stream);
+}
+
+int64_t attn_bwd_workspace_size(int64_t B, int64_t H, int64_t Nq) {
+  if (B < 0 || H < 0 || Nq < 0 || B > kMaxExtent || H > kMaxExtent || Nq > kMaxExtent) return -1;
+  const double bytes = 8.0 * (double)B * (double)H * (double)Nq;
+  if (bytes > 9.0e18) return -1;
+  return 8 * B * H * Nq;  // D and the base-2 log-sum-exp, fp32, per query row
+}
+
+attn_status_t attn_bwd(const attn_tensor_t* q, const attn_tensor_t* k, const attn_tensor_t* v,
+                       const attn_tensor_t* o, const attn_tensor_t* lse,
+                       const attn_tensor_t* dout, const attn_mask_t* bias_or_mask, int causal,
+                       float scale, void* workspace, int64_t workspace_bytes,
+                       const attn_tensor_t* dq, const attn_tensor_t* dk,
+                       const attn_tensor_t* dv, void* stream) {
+  g_last_error.clear();
+  // the forward's own checks cover q, k, v, o, lse, the mask and the scale
+  attn::FwdParams f;
+  bool empty;
+  attn_status_t s = prepare(q, k, v, bias_or_mask, causal, scale, o, lse, f, empty);
+  if (s != ATTN_OK) return s;
+  if (q->dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "the backward supports bf16 only");
+  if (dout == nullptr || dq == nullptr || dk == nullptr || dv == nullptr)
+    return fail(ATTN_ERR_INVALID, "dout, dq, dk and dv descriptors must be non-NULL");
+  for (auto [name, t, ref] : {std::tuple{"dout", dout, q}, std::tuple{"dq", dq, q},
+                               std::tuple{"dk", dk, k}, std::tuple{"dv", dv, v}}) {
+    if ((s = check_view(name, t, ATTN_BF16)) != ATTN_OK) return s;
+    for (int i = 0; i < 4; ++i)
+      if (t->shape[i] != ref->shape[i])
+        return fail(ATTN_ERR_INVALID, "%s must have the shape of %s", name, ref == q ? "q" : "k / v");
+  }
+  if (empty) return ATTN_OK;  // B, H or Nq is 0: dk, dv need Nq > 0 to be non-zero
+  for (auto [name, t] : {std::pair{"dout", dout}, std::pair{"dq", dq}})
+    if ((s = check_rows(name, t)) != ATTN_OK) return s;
+  if (f.Nk > 0)
+    for (auto [name, t] : {std::pair{"dk", dk}, std::pair{"dv", dv}})
+      if ((s = check_rows(name, t)) != ATTN_OK) return s;
+  const int64_t need = attn_bwd_workspace_size(f.B, f.H, f.Nq);
+  if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 15u) != 0)
+    return fail(ATTN_ERR_INVALID, "workspace is NULL or not 16-byte aligned");
+  if (need < 0 || workspace_bytes < need)
+    return fail(ATTN_ERR_INVALID, "workspace of %lld bytes is too small (%lld needed)",
+                (long long)workspace_bytes, (long long)need);
+
+  attn::BwdParams p{};
+  p.q = f.q; p.k = f.k; p.v = f.v; p.o = f.o; p.lse = f.lse;
+  p.do_ = dout->data;
+  p.dq = dq->data; p.dk = dk->data; p.dv = dv->data;
+  p.bias = f.bias; p.kv_len = f.kv_len;
+  p.dsum = static_cast<float*>(workspace);
+  p.lse2 = p.dsum + (int64_t)f.B * f.H * f.Nq;
+  p.q_sb = f.q_sb; p.q_sh = f.q_sh; p.q_sn = f.q_sn;
+  p.k_sb = f.k_sb; p.k_sh = f.k_sh; p.k_sn = f.k_sn;
+  p.v_sb = f.v_sb; p.v_sh = f.v_sh; p.v_sn = f.v_sn;
+  p.o_sb = f.o_sb; p.o_sh = f.o_sh; p.o_sn = f.o_sn;
+  p.do_sb = st(dout, 0); p.do_sh = st(dout, 1); p.do_sn = st(dout, 2);
+  p.dq_sb = st(dq, 0); p.dq_sh = st(dq, 1); p.dq_sn = st(dq, 2);
+  p.dk_sb = st(dk, 0); p.dk_sh = st(dk, 1); p.dk_sn = st(dk, 2);
+  p.dv_sb = st(dv, 0); p.dv_sh = st(dv, 1); p.dv_sn = st(dv, 2);
+  p.l_sb = f.l_sb; p.l_sh = f.l_sh;
+  p.bias_sb = f.bias_sb; p.bias_sh = f.bias_sh; p.bias_sn = f.bias_sn;
+  p.B = f.B; p.H = f.H; p.Hk = f.Hk; p.Nq = f.Nq; p.Nk = f.Nk;
+  p.head_group = f.head_group;
+  p.causal = f.causal; p.local = f.local;
+  p.win_left = f.win_left; p.win_right = f.win_right;
+  p.scale = scale;
+  p.scale_log2 = f.scale_log2;
+  const int rc = attn::launch_bwd_bf16(p, (int)q->shape[3], stream);
+  if (rc != 0) return fail(ATTN_ERR_HIP, "kernel launch failed: %s", attn::hip_error_text(rc));
+  return ATTN_OK;
 }
 
 }  // extern "C"

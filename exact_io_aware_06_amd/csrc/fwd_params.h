@@ -62,6 +62,48 @@ struct FwdParams {
   int32_t max_q;
 };
 
+// Parameter block of the backward (bf16). Same conventions as FwdParams;
+// q, o, do_, dq are [B, H, Nq, d], k, v, dk, dv are [B, Hk, Nk, d]; lse is
+// the forward's natural log-sum-exp [B, H, Nq]. The workspace holds, per
+// query row, D = rowsum(dO o O) and the log-sum-exp in base 2 (+inf for a
+// row with no visible key, so that every probability it recomputes is 0).
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* do_;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  const float* bias;
+  const int32_t* kv_len;
+  float* dsum;   // [B, H, Nq]: D
+  float* lse2;   // [B, H, Nq]: lse * log2(e)
+
+  int64_t q_sb, q_sh, q_sn;
+  int64_t k_sb, k_sh, k_sn;
+  int64_t v_sb, v_sh, v_sn;
+  int64_t o_sb, o_sh, o_sn;
+  int64_t do_sb, do_sh, do_sn;
+  int64_t dq_sb, dq_sh, dq_sn;
+  int64_t dk_sb, dk_sh, dk_sn;
+  int64_t dv_sb, dv_sh, dv_sn;
+  int64_t l_sb, l_sh;
+  int64_t bias_sb, bias_sh, bias_sn;
+
+  int32_t B, H, Hk, Nq, Nk;
+  int32_t head_group;
+  int32_t causal;      // right-bounded mask (also set for a window)
+  int32_t local;       // window: left bound as well
+  int32_t win_left, win_right;
+  float scale;
+  float scale_log2;
+};
+
+int launch_bwd_bf16(const BwdParams& p, int d, void* stream);
+
 // How the flat workgroup index maps onto (batch, head, query tile).
 struct TileMap {
   int32_t n_qtiles;      // ceil(Nq / tile rows)

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 4
+#define ATTN_ABI_VERSION 5
 
 typedef enum {
   ATTN_OK = 0,
@@ -240,6 +240,54 @@ attn_status_t attn_fwd_varlen(const attn_tensor_t* q, const attn_tensor_t* k,
                               const int32_t* cu_seqlens_k, int32_t num_seqs, int32_t max_seqlen_q,
                               const attn_mask_t* window_mask, int causal, float scale,
                               const attn_tensor_t* o, const attn_tensor_t* lse, void* stream);
+
+/*
+ * Backward pass (gradients of attn_fwd), recomputing the probabilities.
+ *
+ * Given the forward's inputs, its outputs O and LSE and the gradient dO of a
+ * scalar loss with respect to O, computes
+ *
+ *     D_i = rowsum(dO_i o O_i),          P_ij = exp(S_ij - LSE_i),
+ *     dV = P^T dO,   dP = dO V^T,       dS = P o (dP - D),
+ *     dQ = scale * dS K,                 dK = scale * dS^T Q,
+ *
+ * with S, the masks and the window exactly as in attn_fwd; P is rebuilt
+ * tile by tile from Q, K and LSE and never stored. ("Understanding
+ * FlashAttention Pt 1", section 3.6; "FlashAttention, Explained", sections
+ * 16-17; "FlashAttention: Mathematical Foundations...", section 4;
+ * "flash-attention" (stanleyjacob.dev), Part VII.) With grouped K/V heads,
+ * dK and dV of a K/V head sum over the query heads that read it. The bias,
+ * when given, is treated as a constant (no gradient is returned for it).
+ * The result is deterministic: no atomic accumulation is used.
+ */
+
+/* Bytes of workspace attn_bwd needs: 8 * B * H * Nq (two fp32 values per
+   query row). -1 for a negative or too large extent. */
+int64_t attn_bwd_workspace_size(int64_t B, int64_t H, int64_t Nq);
+
+/*
+ * attn_bwd - enqueue the backward on `stream` (three kernels).
+ *
+ *   q, k, v, bias_or_mask, causal, scale   as passed to attn_fwd (bf16 only)
+ *   o, lse     the outputs attn_fwd produced for them
+ *   dout       [B, H, Nq, d] bf16, gradient with respect to o
+ *   workspace  DEVICE pointer, 16-byte aligned, at least
+ *              attn_bwd_workspace_size(B, H, Nq) bytes; scratch owned by the
+ *              caller (contents on return undefined; concurrent calls need
+ *              distinct workspaces)
+ *   dq         [B, H, Nq, d] bf16 output
+ *   dk, dv     [B, Hk, Nk, d] bf16 outputs
+ *
+ * Layout and alignment rules are those of attn_fwd for every tensor; the
+ * outputs must not overlap the inputs or each other. Keys no query sees get
+ * dK = dV = 0 and a query row that sees no key gets dQ = 0.
+ */
+attn_status_t attn_bwd(const attn_tensor_t* q, const attn_tensor_t* k, const attn_tensor_t* v,
+                       const attn_tensor_t* o, const attn_tensor_t* lse,
+                       const attn_tensor_t* dout, const attn_mask_t* bias_or_mask, int causal,
+                       float scale, void* workspace, int64_t workspace_bytes,
+                       const attn_tensor_t* dq, const attn_tensor_t* dk,
+                       const attn_tensor_t* dv, void* stream);
 
 /* Text describing the last non-OK status returned on the calling thread
    ("" if none). The pointer stays valid until the next call on this thread. */

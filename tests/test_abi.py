@@ -33,7 +33,8 @@ def _declared_functions():
 def test_exports_every_declared_function():
     lib = _lib()
     names = _declared_functions()
-    assert names == ["attn_abi_version", "attn_fwd", "attn_fwd_splitkv",
+    assert names == ["attn_abi_version", "attn_bwd", "attn_bwd_workspace_size", "attn_fwd",
+                     "attn_fwd_splitkv",
                      "attn_fwd_splitkv_num_splits", "attn_fwd_splitkv_workspace_size",
                      "attn_fwd_varlen", "attn_last_error"]
     for n in names:
@@ -306,3 +307,42 @@ def test_varlen_rejections():
     # nothing to compute: OK without touching the device
     assert _varlen_call(num_seqs=0) == ea.ATTN_OK
     assert _varlen_call(max_q=0) == ea.ATTN_OK
+
+
+# ------------------------------------------------------------------ backward
+
+def _bwd_call(dtype=ea.ATTN_BF16, workspace=0xA0000, ws_bytes=1 << 20, dq_shape=None,
+              dout_dtype=None):
+    B, H, N, d = 2, 4, 64, 64
+    q = _desc((B, H, N, d), dtype)
+    k = _desc((B, H, N, d), dtype, data=0x20000)
+    v = _desc((B, H, N, d), dtype, data=0x30000)
+    o = _desc((B, H, N, d), dtype, data=0x40000)
+    lse = _desc((B, H, N, 1), ea.ATTN_F32, data=0x50000, stride=[H * N, N, 1, 1])
+    do = _desc((B, H, N, d), dout_dtype if dout_dtype is not None else dtype, data=0x60000)
+    dq = _desc(dq_shape or (B, H, N, d), dtype, data=0x70000)
+    dk = _desc((B, H, N, d), dtype, data=0x80000)
+    dv = _desc((B, H, N, d), dtype, data=0x90000)
+    lib = _lib()
+    return lib.attn_bwd(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), ctypes.byref(o),
+                        ctypes.byref(lse), ctypes.byref(do), None, 0, 0.125,
+                        ctypes.c_void_p(workspace), ws_bytes, ctypes.byref(dq), ctypes.byref(dk),
+                        ctypes.byref(dv), None)
+
+
+def test_bwd_workspace_size():
+    assert ea.bwd_workspace_size(2, 4, 64) == 8 * 2 * 4 * 64
+    assert ea.bwd_workspace_size(-1, 4, 64) == -1
+
+
+def test_bwd_rejections():
+    # every call below is refused on the host before any launch
+    assert _bwd_call(dtype=ea.ATTN_F32) == ea.ATTN_ERR_UNSUPPORTED
+    assert "bf16" in ea.last_error()
+    assert _bwd_call(dq_shape=(2, 4, 63, 64)) == ea.ATTN_ERR_INVALID
+    assert "shape" in ea.last_error()
+    assert _bwd_call(dout_dtype=ea.ATTN_F32) == ea.ATTN_ERR_INVALID
+    assert _bwd_call(workspace=0) == ea.ATTN_ERR_INVALID
+    assert _bwd_call(workspace=0xA0004) == ea.ATTN_ERR_INVALID
+    assert _bwd_call(ws_bytes=8 * 2 * 4 * 64 - 1) == ea.ATTN_ERR_INVALID
+    assert "too small" in ea.last_error()
