@@ -192,6 +192,77 @@ def bench_varlen(args, w):
     return 0
 
 
+def bench_backward(args, w):
+    """One step = one attn_bwd call (preprocess, dK/dV and dQ kernels) on the
+    workload, with Q, K, V, O, LSE and dO resident. FLOPs: 2.5 times the
+    forward's (five tile products against two), the pages' accounting."""
+    import torch
+    import workloads
+    import exact_io_aware_06_amd as ea
+
+    inp = workloads.make_inputs(w)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, k, v = (inp[x].to(dev) for x in ("q", "k", "v"))
+    bias = inp["bias"].to(dev) if inp["bias"] is not None else None
+    kv_len = inp["kv_len"].to(dev) if inp["kv_len"] is not None else None
+    g = torch.Generator().manual_seed(w.seed + 1000)
+    do = torch.randn(q.shape, generator=g).to(q.dtype).to(dev)
+    o, lse = ea.attn_fwd(q, k, v, bias=bias, kv_len=kv_len, causal=w.causal, scale=inp["scale"],
+                         window=w.window)
+    step, _, _, _ = ea.prepare_bwd_call(q, k, v, o, lse, do, bias=bias, kv_len=kv_len,
+                                        causal=w.causal, scale=inp["scale"], window=w.window)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        step()
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    fwd_flops = w.flops() if w.window is None else window_flops(w)
+    flops = 2.5 * fwd_flops
+    tflops = flops / (ms * 1e-3) / 1e12
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+        rep = w.H // w.kv_heads
+        done, t0 = 0, time.perf_counter()
+        do_c = do.cpu()
+        for b, h in heads:
+            sl = lambda t, hh: t[b:b + 1, hh:hh + 1].double().numpy()
+            oracle.attention_backward(sl(inp["q"], h), sl(inp["k"], h // rep), sl(inp["v"], h // rep),
+                                      sl(do_c, h), scale=inp["scale"], causal=w.causal,
+                                      window=w.window)
+            done += 1
+            if time.perf_counter() - t0 >= args.cpu_budget:
+                break
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(flops * done / len(heads) / dt / 1e12, 6), "unit": "TFLOP/s",
+               "cores": _blas_threads(), "kind": "oracle",
+               "sample": f"{done} of {len(heads)} (b,h) heads of {w.name} backward at full "
+                         f"Nq={w.Nq}, Nk={w.Nk}, fp64 materialising S, P, dP, dS, {dt:.1f} s"}
+    out = {
+        "metric": "attention fwd TFLOP/s and % of bf16 MFMA peak at 1 MI355X (N=4096,d=128)",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {**w.describe(), "pass": "backward", "flops_per_step": flops,
+                   "flops_rule": "2.5 x forward (5 tile products vs 2)",
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "timed": "preprocess + dK/dV + dQ (whole step)"},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def cpu_baseline_varlen(inp, w, budget_s=15.0):
     """The oracle on whole (sequence, head) pairs of the packed batch until
     the time budget is spent; TFLOP/s over the pairs done."""
@@ -227,6 +298,8 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default=None)
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward (attn_bwd) of the workload instead of the forward")
     ap.add_argument("--splits", type=int, default=None,
                     help="split count for a decoding workload (default: the library's choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -290,6 +363,8 @@ def main(argv=None):
     split = name in workloads.DECODE
     if name in workloads.VARLEN:
         return bench_varlen(args, w)
+    if args.backward:
+        return bench_backward(args, w)
     inp = workloads.make_inputs(w)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
