@@ -20,7 +20,8 @@
 //     head); each wavefront owns 32 keys and keeps their K and V rows and
 //     dK^T, dV^T in registers while Q, dO tiles of 64 query rows stream
 //     through LDS (all query heads of the group, so grouped heads sum in
-//     registers). S = Q K^T and dP = dO V^T are computed with the key in the
+//     registers; the tiles use a bank-rotated variant of the forward's K
+//     layout, below). S = Q K^T and dP = dO V^T are computed with the key in the
 //     lane (the query rows are fed in the bits-2/3 permuted order, so the
 //     accumulator registers 8t..8t+7 hold 8 consecutive queries): P and dS,
 //     converted to bf16 in place, are directly the B operands of
@@ -42,15 +43,44 @@ namespace {
 
 constexpr int kBt = 64;  // rows of one streamed tile (queries in dK/dV, keys in dQ)
 
-// Lane-constant part of the address of a 4-row LDS transpose read in a tile
-// of the K layout (16-row blocks, 16-byte chunk c of row r at slot
-// 16c + r % 16, rows permuted by perm_row): within its 16-lane group, lane
-// 4e + j addresses row e, columns 4j..4j+3 of the group's 16 columns. The
-// row within a block is e + 4*hi (+ 8 for the second read of a pair); the
-// caller adds block, column-block and half offsets as immediates.
-__device__ __forceinline__ int tr_lane_offset(int lane) {
+// LDS tile layout of the backward ("rotated"): blocks of 16 rows; in a
+// block, 16-byte chunk c of row r sits at slot 16c + ((r + 4c) mod 16), and
+// LDS row R holds tile row perm_row(R) (bits 2 and 3 swapped) as in the
+// forward's K tiles. Every tile is read two ways: as rows (A operands of S
+// and dP: 16 lanes read 16 rows of one chunk) and transposed (A operands of
+// the dV, dK, dQ products: ds_read_b64_tr_b16 over 4 rows x 4 chunks x 2
+// column groups per 32 lanes). Without the rotation the chunks of a
+// transposed read fall on the same 16 banks (a 4-way conflict); rotating
+// each chunk's rows by 4c spreads both kinds of read over all 64 banks.
+//
+// Source row of the 16 bytes that `lane` of wave `wave` copies in DMA
+// instruction i (instruction n writes LDS bytes [1024 n, 1024 n + 1024),
+// lane l at 16 l); the byte column is k_dma_col's.
+template <int D, int W>
+__device__ __forceinline__ int rot_dma_row(int wave, int lane, int i) {
+  const int a = 1024 * (wave + W * i) + 16 * lane;
+  constexpr int blk = 16 * (D / 8) * 16;
+  const int slot = (a % blk) / 16;
+  const int c = slot / 16;
+  return perm_row(16 * (a / blk) + ((slot % 16 - 4 * c) & 15));
+}
+
+// Row read (A operand) of chunk pair kk: lane-constant offset for even and
+// odd kk (the rotation of chunk 2kk + hi is 8kk + 4hi mod 16); the caller
+// adds 2 mbq * block + 512 kk.
+__device__ __forceinline__ int row_lane_offset(int lane, int G_block, int odd) {
+  const int l32 = lane & 31, hi = lane >> 5;
+  return (l32 >> 4) * G_block + 256 * hi + 16 * (((l32 & 15) + 4 * hi + 8 * odd) & 15);
+}
+
+// Transposed read: within its 16-lane group, lane 4e + j addresses tile row
+// e + 4 hi (+ 8 for the second read of a pair), columns 4j..4j+3 of the
+// group's 16 columns; lane-constant offset of each read of the pair. The
+// caller adds block and 1024 * (32-column block) offsets.
+__device__ __forceinline__ int tr_lane_offset(int lane, int half) {
   const int L = lane & 15, e = L >> 2, j = L & 3, g = (lane >> 4) & 1, hi = lane >> 5;
-  return 256 * (2 * g + (j >> 1)) + 16 * (e + 4 * hi) + 8 * (j & 1);
+  return 256 * (2 * g + (j >> 1)) + 16 * ((e + 4 * hi + 8 * g + 4 * (j >> 1) + 8 * half) & 15) +
+         8 * (j & 1);
 }
 
 // ------------------------------------------------------------- preprocess
@@ -88,9 +118,8 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
 // the kernel within 256 registers (the variants with a bias or a window
 // spill a few dwords) and was measured 1.31x faster than one wavefront per
 // SIMD with no register limit.
-template <int D, bool CAUSAL, bool HAS_BIAS, bool LOCAL>
-__global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p, TileMap tm) {
-  constexpr int W = 4;
+template <int D, int W, bool CAUSAL, bool HAS_BIAS, bool LOCAL>
+__global__ __launch_bounds__(64 * W, 2) void bwd_dkdv_kernel(BwdParams p, TileMap tm) {
   using G = Geo<D, W>;
   constexpr int kNkk = D / 16;   // d-steps of S and dP
   constexpr int kNcb = D / 32;   // d blocks of dK^T, dV^T
@@ -147,7 +176,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p, TileMap t
   int rrow[G::kDmaPerWave], rcol[G::kDmaPerWave];
 #pragma unroll
   for (int i = 0; i < G::kDmaPerWave; ++i) {
-    rrow[i] = k_dma_key<D, W>(wave, lane, i);
+    rrow[i] = rot_dma_row<D, W>(wave, lane, i);
     rcol[i] = k_dma_col<D, W>(wave, lane, i);
   }
   const int64_t qsn = p.q_sn * 2, dsn = p.do_sn * 2;  // row strides in bytes
@@ -191,8 +220,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p, TileMap t
     dv_acc[mb] = f32x16{};
   }
   // LDS read offsets: rows (A operands of S and dP) and transposed reads
-  const int rlane = (l32 >> 4) * G::kKBlock + hi * 256 + (l32 & 15) * 16;
-  const int tlane = tr_lane_offset(lane);
+  const int rl0 = row_lane_offset(lane, G::kKBlock, 0), rl1 = row_lane_offset(lane, G::kKBlock, 1);
+  const int tl0 = tr_lane_offset(lane, 0), tl1 = tr_lane_offset(lane, 1);
 
   if (ns > 0) {
     issue(0, 0);
@@ -220,8 +249,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p, TileMap t
       f32x16 sacc = f32x16{}, pacc = f32x16{};
 #pragma unroll
       for (int kk = 0; kk < kNkk; ++kk) {
-        const bf16x8 aq = *reinterpret_cast<const bf16x8*>(Qt + rlane + mbq * 2 * G::kKBlock + kk * 512);
-        const bf16x8 ad = *reinterpret_cast<const bf16x8*>(dOt + rlane + mbq * 2 * G::kKBlock + kk * 512);
+        const int ro = (kk & 1 ? rl1 : rl0) + mbq * 2 * G::kKBlock + kk * 512;
+        const bf16x8 aq = *reinterpret_cast<const bf16x8*>(Qt + ro);
+        const bf16x8 ad = *reinterpret_cast<const bf16x8*>(dOt + ro);
         sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[kk], sacc, 0, 0, 0);
         pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vf[kk], pacc, 0, 0, 0);
       }
@@ -267,9 +297,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p, TileMap t
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int mb = 0; mb < kNcb; ++mb) {
-          const int o = tlane + (2 * mbq + t) * G::kKBlock + 1024 * mb;
-          const bf16x8 a_do = lds_read_tr_pair(dOt + o, dOt + o + 128);
-          const bf16x8 a_q = lds_read_tr_pair(Qt + o, Qt + o + 128);
+          const int o = (2 * mbq + t) * G::kKBlock + 1024 * mb;
+          const bf16x8 a_do = lds_read_tr_pair(dOt + tl0 + o, dOt + tl1 + o);
+          const bf16x8 a_q = lds_read_tr_pair(Qt + tl0 + o, Qt + tl1 + o);
           dv_acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_do, __builtin_bit_cast(bf16x8, pb[t]), dv_acc[mb], 0, 0, 0);
           dk_acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_q, __builtin_bit_cast(bf16x8, db[t]), dk_acc[mb], 0, 0, 0);
         }
@@ -302,9 +332,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BwdParams p, TileMap t
 }
 
 // ------------------------------------------------------------------- dQ
-template <int D, bool CAUSAL, bool HAS_BIAS, bool LOCAL>
-__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p, TileMap tm) {
-  constexpr int W = 4;
+template <int D, int W, bool CAUSAL, bool HAS_BIAS, bool LOCAL>
+__global__ __launch_bounds__(64 * W, 2) void bwd_dq_kernel(BwdParams p, TileMap tm) {
   using G = Geo<D, W>;
   constexpr int kBr = 32 * W;
   constexpr int kNkk = D / 16;
@@ -363,7 +392,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p, TileMap tm)
   int rrow[G::kDmaPerWave], rcol[G::kDmaPerWave];
 #pragma unroll
   for (int i = 0; i < G::kDmaPerWave; ++i) {
-    rrow[i] = k_dma_key<D, W>(wave, lane, i);
+    rrow[i] = rot_dma_row<D, W>(wave, lane, i);
     rcol[i] = k_dma_col<D, W>(wave, lane, i);
   }
   const int64_t ksn = p.k_sn * 2, vsn = p.v_sn * 2;
@@ -387,8 +416,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p, TileMap tm)
   f32x16 dq_acc[kNcb];
 #pragma unroll
   for (int mb = 0; mb < kNcb; ++mb) dq_acc[mb] = f32x16{};
-  const int rlane = (l32 >> 4) * G::kKBlock + hi * 256 + (l32 & 15) * 16;
-  const int tlane = tr_lane_offset(lane);
+  const int rl0 = row_lane_offset(lane, G::kKBlock, 0), rl1 = row_lane_offset(lane, G::kKBlock, 1);
+  const int tl0 = tr_lane_offset(lane, 0), tl1 = tr_lane_offset(lane, 1);
   const float* brow = nullptr;
   if (HAS_BIAS) brow = p.bias + b * p.bias_sb + h * p.bias_sh + (int64_t)min(my_q, Nq - 1) * p.bias_sn;
 
@@ -407,7 +436,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p, TileMap tm)
     f32x16 sa[2] = {f32x16{}, f32x16{}}, da[2] = {f32x16{}, f32x16{}};
 #pragma unroll
     for (int i = 0; i < kNq; ++i) {
-      const int o = rlane + (i & 1) * 2 * G::kKBlock + (i >> 1) * 512;
+      const int o = (((i >> 1) & 1) ? rl1 : rl0) + (i & 1) * 2 * G::kKBlock + (i >> 1) * 512;
       const bf16x8 ak = *reinterpret_cast<const bf16x8*>(Kt + o);
       const bf16x8 av = *reinterpret_cast<const bf16x8*>(Vt + o);
       sa[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qf[i >> 1], sa[i & 1], 0, 0, 0);
@@ -442,8 +471,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p, TileMap tm)
     for (int u = 0; u < 4; ++u)
 #pragma unroll
       for (int mb = 0; mb < kNcb; ++mb) {
-        const int o = tlane + u * G::kKBlock + 1024 * mb;
-        const bf16x8 a = lds_read_tr_pair(Kt + o, Kt + o + 128);
+        const int o = u * G::kKBlock + 1024 * mb;
+        const bf16x8 a = lds_read_tr_pair(Kt + tl0 + o, Kt + tl1 + o);
         dq_acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, db[u >> 1][u & 1]), dq_acc[mb], 0, 0, 0);
       }
     if (j + 1 < nt) wait_tiles();
@@ -473,37 +502,40 @@ hipError_t set_lds(Kern kern, int bytes, bool& done) {
   return e;
 }
 
+// wavefronts per workgroup of the dK/dV and dQ kernels (32 keys or rows each)
+constexpr int kWkv = 4;
+constexpr int kWq = 4;
+
 template <int D, bool CAUSAL, bool HAS_BIAS, bool LOCAL>
 hipError_t launch_bwd_d(const BwdParams& p, hipStream_t s) {
-  using G = Geo<D, 4>;
-  // dK / dV: key tiles of 128
+  // dK / dV: key tiles of 32 * kWkv
   TileMap tk{};
-  tk.n_qtiles = (p.Nk + 127) / 128;
+  tk.n_qtiles = (p.Nk + 32 * kWkv - 1) / (32 * kWkv);
   tk.total = p.B * p.Hk * tk.n_qtiles;
   tk.per_xcd = (tk.total + 7) / 8;
   if (tk.total > 0) {
-    auto kern = bwd_dkdv_kernel<D, CAUSAL, HAS_BIAS, LOCAL>;
-    constexpr int lds = 2 * (2 * G::kKBytes + 2 * kBt * 4);
+    auto kern = bwd_dkdv_kernel<D, kWkv, CAUSAL, HAS_BIAS, LOCAL>;
+    constexpr int lds = 2 * (2 * Geo<D, kWkv>::kKBytes + 2 * kBt * 4);
     static bool done = false;
     hipError_t e = set_lds(kern, lds, done);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(8 * tk.per_xcd), dim3(256), lds, s, p, tk);
+    hipLaunchKernelGGL(kern, dim3(8 * tk.per_xcd), dim3(64 * kWkv), lds, s, p, tk);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  // dQ: query tiles of 128
+  // dQ: query tiles of 32 * kWq
   TileMap tq{};
-  tq.n_qtiles = (p.Nq + 127) / 128;
+  tq.n_qtiles = (p.Nq + 32 * kWq - 1) / (32 * kWq);
   tq.total = p.B * p.H * tq.n_qtiles;
   tq.per_xcd = (tq.total + 7) / 8;
   tq.reverse_q = CAUSAL ? 1 : 0;
   tq.n_split = 1;
   if (tq.total > 0) {
-    auto kern = bwd_dq_kernel<D, CAUSAL, HAS_BIAS, LOCAL>;
-    constexpr int lds = 2 * 2 * G::kKBytes;
+    auto kern = bwd_dq_kernel<D, kWq, CAUSAL, HAS_BIAS, LOCAL>;
+    constexpr int lds = 2 * 2 * Geo<D, kWq>::kKBytes;
     static bool done = false;
     hipError_t e = set_lds(kern, lds, done);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(8 * tq.per_xcd), dim3(256), lds, s, p, tq);
+    hipLaunchKernelGGL(kern, dim3(8 * tq.per_xcd), dim3(64 * kWq), lds, s, p, tq);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;
