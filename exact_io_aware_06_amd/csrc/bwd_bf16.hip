@@ -14,8 +14,9 @@
 //
 // Work decomposition on CDNA4 (three launches):
 //   * preprocess: d/8 lanes per query row (16-byte loads of O and dO)
-//     write D and the log-sum-exp in base 2 (+inf for a row that saw no
-//     key, so every probability it recomputes is exactly 0);
+//     write D and the negated log-sum-exp in base 2 (-inf for a row that
+//     saw no key, so every probability it recomputes is exactly 0; negated
+//     so that the exponent log2(e) S - LSE2 is one fused multiply-add);
 //   * dK/dV: one workgroup = 4 wavefronts = 128 keys of one (batch, K/V
 //     head); each wavefront owns 32 keys and keeps their K and V rows and
 //     dK^T, dV^T in registers while Q, dO tiles of 64 query rows stream
@@ -108,7 +109,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
   if (ok && sub == 0) {
     p.dsum[row] = acc;
     const float l = p.lse[b * p.l_sb + h * p.l_sh + i];
-    p.lse2[row] = (l == -INFINITY) ? INFINITY : l * kLog2e;
+    p.lse2[row] = (l == -INFINITY) ? -INFINITY : -l * kLog2e;
   }
 }
 
@@ -183,7 +184,7 @@ __global__ __launch_bounds__(64 * W, 2) void bwd_dkdv_kernel(BwdParams p, TileMa
   auto stage_head = [&](int s) { return hk * p.head_group + s / nqb; };
   auto stage_q0 = [&](int s) { return q_lo + (s % nqb) * kBt; };
   // copy the Q and dO tiles of stage s into buffer `buf` (rows past Nq read
-  // row Nq - 1: finite data whose probabilities are 0, their lse2 being +inf)
+  // row Nq - 1: finite data whose probabilities are 0, their -LSE2 being -inf)
   auto issue = [&](int s, int buf) {
     const int h = stage_head(s), q0 = stage_q0(s);
     const int lim = Nq - 1 - q0;
@@ -197,12 +198,12 @@ __global__ __launch_bounds__(64 * W, 2) void bwd_dkdv_kernel(BwdParams p, TileMa
       dma16(dt, (uint32_t)(r * (int)dsn + rcol[i]), st + G::kKBytes + 1024 * (wave + W * i));
     }
   };
-  // lse2 (wave 0) and D (wave 1) of stage s: one value per lane
+  // negated base-2 LSE (wave 0) and D (wave 1) of stage s: one value per lane
   auto load_stats = [&](int s) {
     const int h = stage_head(s), qi = stage_q0(s) + lane;
     const int64_t row = ((int64_t)b * p.H + h) * Nq + min(qi, Nq - 1);
     float x = 0.f;
-    if (wave == 0) x = (qi < Nq) ? p.lse2[row] : INFINITY;
+    if (wave == 0) x = (qi < Nq) ? p.lse2[row] : -INFINITY;
     else if (wave == 1) x = (qi < Nq) ? p.dsum[row] : 0.f;
     return x;
   };
@@ -255,11 +256,22 @@ __global__ __launch_bounds__(64 * W, 2) void bwd_dkdv_kernel(BwdParams p, TileMa
         sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kf[kk], sacc, 0, 0, 0);
         pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vf[kk], pacc, 0, 0, 0);
       }
-      // register r holds query q0 + 32 mbq + 16 (r / 8) + 8 hi + (r % 8)
+      // register r holds query q0 + 32 mbq + 16 (r / 8) + 8 hi + (r % 8).
+      // Keys past the key length are not masked: a key feeds only its own
+      // column of dK^T and dV^T, which the epilogue writes as zeros.
       const int qb = q0 + 32 * mbq + 8 * hi;
-      const bool need_mask = (k0 + 32 * W > kend) ||
-                             (CAUSAL && k0 + 32 * W - 1 > q0 + 32 * mbq + off) ||
+      const bool need_mask = (CAUSAL && k0 + 32 * W - 1 > q0 + 32 * mbq + off) ||
                              (LOCAL && k0 < q0 + 32 * mbq + 31 + off_l);
+      // hidden scores become -inf in place (scale > 0, so the exponent
+      // below stays -inf and P = 0); only tiles that cross the mask's edge
+      // take this branch
+      if ((CAUSAL || LOCAL) && need_mask) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int qi = qb + 16 * (r >> 3) + (r & 7);
+          if ((CAUSAL && my_k > qi + off) || (LOCAL && my_k < qi + off_l)) sacc[r] = -INFINITY;
+        }
+      }
       u32x4 pb[2], db[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
@@ -275,15 +287,10 @@ __global__ __launch_bounds__(64 * W, 2) void bwd_dkdv_kernel(BwdParams p, TileMa
             const int e = 2 * e2 + u;   // query qb + 16 t + e
             const int r = 8 * t + e;
             const int qi = qb + 16 * t + e;
-            float sv = HAS_BIAS ? __builtin_fmaf(sacc[r], c2, brow[(int64_t)min(qi, Nq - 1) * p.bias_sn] * kLog2e)
-                                : sacc[r] * c2;
-            if (need_mask) {
-              const bool hide = (my_k >= kend) || (CAUSAL && my_k > qi + off) || (LOCAL && my_k < qi + off_l);
-              if (hide) sv = -INFINITY;
-            }
-            const float lv = e < 4 ? l0[e & 3] : l1[e & 3];
+            const float nl = e < 4 ? l0[e & 3] : l1[e & 3];  // -LSE2 of the query
             const float dv = e < 4 ? d0[e & 3] : d1[e & 3];
-            pr[u] = __builtin_amdgcn_exp2f(sv - lv);
+            const float base = HAS_BIAS ? __builtin_fmaf(brow[(int64_t)min(qi, Nq - 1) * p.bias_sn], kLog2e, nl) : nl;
+            pr[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], c2, base));
             ds[u] = pr[u] * (pacc[r] - dv);
           }
           const bf16x2 pp = {(__bf16)pr[0], (__bf16)pr[1]};
@@ -311,8 +318,10 @@ __global__ __launch_bounds__(64 * W, 2) void bwd_dkdv_kernel(BwdParams p, TileMa
     __syncthreads();
   }
 
-  // ---- epilogue: register r of block mb holds column 32 mb + 8 (r/4) + 4 hi + r%4
+  // ---- epilogue: register r of block mb holds column 32 mb + 8 (r/4) + 4 hi + r%4;
+  // keys at or past the key length get zero gradients
   if (my_k < Nk) {
+    const float ks = my_k < kend ? p.scale : 0.f, vs = my_k < kend ? 1.f : 0.f;
     __bf16* dkrow = static_cast<__bf16*>(p.dk) + b * p.dk_sb + hk * p.dk_sh + (int64_t)my_k * p.dk_sn;
     __bf16* dvrow = static_cast<__bf16*>(p.dv) + b * p.dv_sb + hk * p.dv_sh + (int64_t)my_k * p.dv_sn;
 #pragma unroll
@@ -322,8 +331,8 @@ __global__ __launch_bounds__(64 * W, 2) void bwd_dkdv_kernel(BwdParams p, TileMa
         bf16x4 wk, wv;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          wk[e] = (__bf16)(dk_acc[mb][4 * g + e] * p.scale);
-          wv[e] = (__bf16)(dv_acc[mb][4 * g + e]);
+          wk[e] = (__bf16)(dk_acc[mb][4 * g + e] * ks);
+          wv[e] = (__bf16)(dv_acc[mb][4 * g + e] * vs);
         }
         *reinterpret_cast<bf16x4*>(dkrow + 32 * mb + 8 * g + 4 * hi) = wk;
         *reinterpret_cast<bf16x4*>(dvrow + 32 * mb + 8 * g + 4 * hi) = wv;
@@ -359,7 +368,7 @@ __global__ __launch_bounds__(64 * W, 2) void bwd_dq_kernel(BwdParams p, TileMap 
 
   // Q and dO rows of this lane's query, resident: B operands of S^T and dP^T
   bf16x8 qf[kNkk], df[kNkk];
-  float lse2 = INFINITY, dval = 0.f;
+  float nl = -INFINITY, dval = 0.f;  // -LSE2 and D of this lane's query
   {
     const int qr = min(my_q, Nq - 1);
     const __bf16* qrow = static_cast<const __bf16*>(p.q) + b * p.q_sb + h * p.q_sh + (int64_t)qr * p.q_sn + 8 * hi;
@@ -371,7 +380,7 @@ __global__ __launch_bounds__(64 * W, 2) void bwd_dq_kernel(BwdParams p, TileMap 
     }
     if (live) {
       const int64_t row = ((int64_t)b * p.H + h) * Nq + my_q;
-      lse2 = p.lse2[row];
+      nl = p.lse2[row];
       dval = p.dsum[row];
     }
   }
@@ -445,6 +454,18 @@ __global__ __launch_bounds__(64 * W, 2) void bwd_dq_kernel(BwdParams p, TileMap 
     // register r of block bb holds key kv0 + 32 bb + 16 (r/8) + 8 hi + (r%8)
     const bool need_mask = (kv0 + kBc > kend) || (CAUSAL && kv0 + kBc - 1 > qw0 + off) ||
                            (LOCAL && kv0 < qmax_w + off_l);
+    // hidden scores become -inf in place (scale > 0: P = 0 below); only
+    // tiles that cross the mask's edge or the key length take this branch
+    if (need_mask) {
+#pragma unroll
+      for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kv0 + 32 * bb + 16 * (r >> 3) + 8 * hi + (r & 7);
+          if ((key >= kend) || (CAUSAL && key > my_q + off) || (LOCAL && key < my_q + off_l))
+            sa[bb][r] = -INFINITY;
+        }
+    }
     u32x4 db[2][2];
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb)
@@ -455,12 +476,8 @@ __global__ __launch_bounds__(64 * W, 2) void bwd_dq_kernel(BwdParams p, TileMap 
         for (int u = 0; u < 2; ++u) {
           const int r = 2 * r2 + u;
           const int key = kv0 + 32 * bb + 16 * (r >> 3) + 8 * hi + (r & 7);
-          float sv = HAS_BIAS ? __builtin_fmaf(sa[bb][r], c2, brow[min(key, Nk - 1)] * kLog2e) : sa[bb][r] * c2;
-          if (need_mask) {
-            const bool hide = (key >= kend) || (CAUSAL && key > my_q + off) || (LOCAL && key < my_q + off_l);
-            if (hide) sv = -INFINITY;
-          }
-          const float pr = __builtin_amdgcn_exp2f(sv - lse2);
+          const float base = HAS_BIAS ? __builtin_fmaf(brow[min(key, Nk - 1)], kLog2e, nl) : nl;
+          const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[bb][r], c2, base));
           ds[u] = pr * (da[bb][r] - dval);
         }
         const bf16x2 dd = {(__bf16)ds[0], (__bf16)ds[1]};

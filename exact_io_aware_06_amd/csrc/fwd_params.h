@@ -80,7 +80,7 @@ struct BwdParams {
   const float* bias;
   const int32_t* kv_len;
   float* dsum;   // [B, H, Nq]: D
-  float* lse2;   // [B, H, Nq]: lse * log2(e)
+  float* lse2;   // [B, H, Nq]: -lse * log2(e) (-inf for a row that saw no key)
 
   int64_t q_sb, q_sh, q_sn;
   int64_t k_sb, k_sh, k_sn;
