@@ -128,13 +128,15 @@ __global__ __launch_bounds__(64 * W, 2) void bwd_dkdv_kernel(BwdParams p, TileMa
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
   // key tile fastest (neighbouring key tiles read the same Q / dO), then
-  // K/V head, batch; consecutive logical tiles share an XCD
+  // K/V head, batch; causal: heads dealt in small groups with the key tile
+  // slow inside a group; consecutive logical tiles share an XCD
   const int w = blockIdx.x;
   const int logical = (w & 7) * tm.per_xcd + (w >> 3);
   if (logical >= tm.total) return;
-  const int kt = logical % tm.n_qtiles;
-  const int hk = (logical / tm.n_qtiles) % p.Hk;
-  const int b = logical / (tm.n_qtiles * p.Hk);
+  int kt, hb;  // causal: key tile 0 sees the most queries (longest first)
+  split_logical(logical, tm.n_qtiles, p.B * p.Hk, tm.group, kt, hb);
+  const int hk = hb % p.Hk;
+  const int b = hb / p.Hk;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -530,6 +532,7 @@ hipError_t launch_bwd_d(const BwdParams& p, hipStream_t s) {
   tk.n_qtiles = (p.Nk + 32 * kWkv - 1) / (32 * kWkv);
   tk.total = p.B * p.Hk * tk.n_qtiles;
   tk.per_xcd = (tk.total + 7) / 8;
+  tk.group = CAUSAL ? dispatch_group(tk.n_qtiles, 2) : 1;  // two workgroups per CU
   if (tk.total > 0) {
     auto kern = bwd_dkdv_kernel<D, kWkv, CAUSAL, HAS_BIAS, LOCAL>;
     constexpr int lds = 2 * (2 * Geo<D, kWkv>::kKBytes + 2 * kBt * 4);
@@ -546,6 +549,7 @@ hipError_t launch_bwd_d(const BwdParams& p, hipStream_t s) {
   tq.per_xcd = (tq.total + 7) / 8;
   tq.reverse_q = CAUSAL ? 1 : 0;
   tq.n_split = 1;
+  tq.group = CAUSAL ? dispatch_group(tq.n_qtiles, 2) : 1;
   if (tq.total > 0) {
     auto kern = bwd_dq_kernel<D, kWq, CAUSAL, HAS_BIAS, LOCAL>;
     constexpr int lds = 2 * 2 * Geo<D, kWq>::kKBytes;

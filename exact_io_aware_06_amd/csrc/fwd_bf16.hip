@@ -46,6 +46,9 @@ int launch_fwd_bf16(const FwdParams& p, int d, void* stream) {
   tm.batch_inner = (p.bias != nullptr && p.bias_sb == 0 && p.B > 1) ? 1 : 0;
   tm.reverse_q = p.causal ? 1 : 0;
   tm.n_split = 1;
+  // causal tiles differ in length: deal heads in groups, longest tiles
+  // first (8 / waves workgroups fit on a CU: two waves per SIMD)
+  tm.group = p.causal ? dispatch_group(tm.n_qtiles, 8 / waves) : 1;
   if (p.n_split > 1) {
     tm.n_split = p.n_split;
     const int64_t all = total * p.n_split;

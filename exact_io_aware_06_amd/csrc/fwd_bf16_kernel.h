@@ -166,6 +166,27 @@ __device__ __forceinline__ void dma16(const uint8_t* tile, uint32_t off, uint8_t
   asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(tile), "{m0}"(lds));
 }
 
+// Work item `logical` as (tile, flat head index). group <= 1: tile fastest,
+// then head. group > 1: heads are dealt in groups of `group` (the last
+// group may be smaller) and within a group the tile is the slow index, so
+// with the longest tiles first (causal) the longest tiles of every head of
+// the group start before any shorter one, while the workgroups resident on
+// an XCD still read about `group` heads' K/V (a greedy dispatch of
+// longest-first work, as in list scheduling).
+__device__ __forceinline__ void split_logical(int logical, int n_tiles, int n_heads, int group,
+                                              int& tile, int& hb) {
+  if (group <= 1) {
+    tile = logical % n_tiles;
+    hb = logical / n_tiles;
+    return;
+  }
+  const int g0 = logical / (group * n_tiles) * group;
+  const int gs = min(group, n_heads - g0);
+  const int within = logical - g0 * n_tiles;
+  tile = within / gs;
+  hb = g0 + within % gs;
+}
+
 template <bool SPLIT, bool VARLEN = false>
 __device__ __forceinline__ bool decode_tile(const TileMap& tm, int B, int H,
                                             int& b, int& h, int& qt, int& split) {
@@ -202,8 +223,7 @@ __device__ __forceinline__ bool decode_tile(const TileMap& tm, int B, int H,
     qi = rest % tm.n_qtiles;
     h = rest / tm.n_qtiles;
   } else {
-    qi = logical % tm.n_qtiles;
-    rest = logical / tm.n_qtiles;
+    split_logical(logical, tm.n_qtiles, B * H, tm.group, qi, rest);
     h = rest % H;
     b = rest / H;
   }

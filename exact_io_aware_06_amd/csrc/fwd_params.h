@@ -112,7 +112,18 @@ struct TileMap {
   int32_t batch_inner;   // 1: batch index varies fastest (shared bias reuse)
   int32_t reverse_q;     // 1: longest query tiles first (causal)
   int32_t n_split;       // key splits per query tile (1: no split)
+  int32_t group;         // > 1: flat (batch, head) indices dealt in groups of
+                         // this many, tile index slow within a group
 };
+
+// Number of flat heads to deal together so that one XCD's resident
+// workgroups (32 CUs x wg_per_cu) cover the longest tiles of a whole group
+// before any shorter one: ceil(32 wg_per_cu / n_tiles), at least 1.
+inline int32_t dispatch_group(int n_tiles, int wg_per_cu) {
+  if (n_tiles <= 0) return 1;
+  const int slots = 32 * wg_per_cu;
+  return slots > n_tiles ? (slots + n_tiles - 1) / n_tiles : 1;
+}
 
 // Host-side launchers (one per kernel family). Return a hipError_t value.
 int launch_fwd_bf16(const FwdParams& p, int d, void* stream);
