@@ -1,12 +1,13 @@
 """Turn rocprofv3 CSV output into the short text summaries kept under profiles/.
 
     python -m exact_io_aware_06_amd.profsum stats  <kernel_stats.csv> <out.txt> <command...>
-    python -m exact_io_aware_06_amd.profsum counters <workload> <out.txt> <pmc_dir>... -- <command...>
+    python -m exact_io_aware_06_amd.profsum counters [--kernel SUBSTR] <workload> <out.txt> <pmc_dir>... -- <command...>
     python -m exact_io_aware_06_amd.profsum traffic <workload> <fetch_dir> <write_dir> \
         <copy_fetch_dir> <copy_write_dir> <copy_mib> <kernel_src[,src...]> <out.txt> <command...>
 
 `stats` copies the per-kernel duration table. `counters` averages the SQ/GRBM
-counters of the attention kernel over its dispatches and derives MFMA busy
+counters of one kernel (the kernels whose name contains SUBSTR, default
+"fwd_bf16") over its dispatches and derives MFMA busy
 fraction (per SIMD, from SQ_VALU_MFMA_BUSY_CYCLES over 1024 SIMDs and the
 per-XCD GRBM_GUI_ACTIVE), instruction mix per 256x64 wave tile and the LDS bank
 conflict rate. `traffic` turns FETCH_SIZE and
@@ -48,13 +49,13 @@ def stats(src, out, cmd):
                     f"{float(r['Percentage']):.2f}\n")
 
 
-def counters(workload, out, dirs, cmd):
+def counters(workload, out, dirs, cmd, kernel="fwd_bf16"):
     acc = {}
     for d in dirs:
         path = os.path.join(d, "pmc_counter_collection.csv")
         per = {}
         for r in csv.DictReader(open(path)):
-            if "attn" not in r["Kernel_Name"]:
+            if kernel not in r["Kernel_Name"]:
                 continue
             key = (r["Counter_Name"], int(r["Dispatch_Id"]))
             per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
@@ -64,7 +65,9 @@ def counters(workload, out, dirs, cmd):
         for n, vs in names.items():
             acc.setdefault(n, []).append(sum(vs) / len(vs))
     c = {n: sum(v) / len(v) for n, v in acc.items()}
-    lines = [f"# rocprofv3 --pmc counters of the attention kernel, workload {workload}",
+    if not acc:
+        raise SystemExit(f"no counter rows for kernels matching {kernel!r}")
+    lines = [f"# rocprofv3 --pmc counters of the kernels matching {kernel!r}, workload {workload}",
              f"# command (one run per counter group): {cmd}",
              "counter | mean per dispatch"]
     lines += [f"{n} | {c[n]:.1f}" for n in sorted(c)]
@@ -75,7 +78,7 @@ def counters(workload, out, dirs, cmd):
         lines.append(f"mfma_busy_fraction_per_simd | {c['SQ_VALU_MFMA_BUSY_CYCLES'] / 1024 / gui:.3f}")
         lines.append(f"mfma_coexec_over_busy | {c['SQ_VALU_MFMA_COEXEC_CYCLES'] / c['SQ_VALU_MFMA_BUSY_CYCLES']:.3f}")
         lines.append(f"lds_bank_conflict_over_idx_active | {c['SQ_LDS_BANK_CONFLICT'] / max(c['SQ_LDS_IDX_ACTIVE'], 1):.4f}")
-        if "SQ_INSTS_VALU" in c:
+        if "SQ_INSTS_VALU" in c and kernel.startswith("fwd_"):
             wt = mf / 32.0   # 32 MFMA instructions per wave per 64-key tile at d=128
             lines.append(f"valu_non_mfma_per_wave_tile | {(c['SQ_INSTS_VALU'] - mf) / wt:.1f}")
             lines.append(f"lds_insts_per_wave_tile | {c['SQ_INSTS_LDS'] / wt:.1f}")
@@ -123,9 +126,12 @@ if __name__ == "__main__":
     if mode == "stats":
         stats(sys.argv[2], sys.argv[3], " ".join(sys.argv[4:]))
     elif mode == "counters":
-        rest = sys.argv[4:]
-        cut = rest.index("--")
-        counters(sys.argv[2], sys.argv[3], rest[:cut], " ".join(rest[cut + 1:]))
+        args = sys.argv[2:]
+        kernel = "fwd_bf16"
+        if args[0] == "--kernel":
+            kernel, args = args[1], args[2:]
+        cut = args.index("--")
+        counters(args[0], args[1], args[2:cut], " ".join(args[cut + 1:]), kernel)
     elif mode == "traffic":
         traffic(*sys.argv[2:10], " ".join(sys.argv[10:]))
     else:
