@@ -388,6 +388,12 @@ attn_status_t attn_bwd(const attn_tensor_t* q, const attn_tensor_t* k, const att
   if (empty) return ATTN_OK;  // B, H or Nq is 0: dk, dv need Nq > 0 to be non-zero
   for (auto [name, t] : {std::pair{"dout", dout}, std::pair{"dq", dq}})
     if ((s = check_rows(name, t)) != ATTN_OK) return s;
+  // the dK/dV kernel streams 64-row tiles of q and dout, addressing their
+  // rows with 32-bit byte offsets
+  for (auto [name, t] : {std::pair{"q", q}, std::pair{"dout", dout}})
+    if (f.Nq > 1 && 64 * t->stride[2] * 2 >= (int64_t(1) << 31))
+      return fail(ATTN_ERR_UNSUPPORTED, "%s: row stride %lld elements is too large (64 rows must span < 2 GiB)",
+                  name, (long long)t->stride[2]);
   if (f.Nk > 0)
     for (auto [name, t] : {std::pair{"dk", dk}, std::pair{"dv", dv}})
       if ((s = check_rows(name, t)) != ATTN_OK) return s;

@@ -278,8 +278,10 @@ int64_t attn_bwd_workspace_size(int64_t B, int64_t H, int64_t Nq);
  *   dq         [B, H, Nq, d] bf16 output
  *   dk, dv     [B, Hk, Nk, d] bf16 outputs
  *
- * Layout and alignment rules are those of attn_fwd for every tensor; the
- * outputs must not overlap the inputs or each other. Keys no query sees get
+ * Layout and alignment rules are those of attn_fwd for every tensor, and
+ * the row stride of q and dout times 64 rows must also span less than
+ * 2 GiB (ATTN_ERR_UNSUPPORTED otherwise); the outputs must not overlap the
+ * inputs or each other. Keys no query sees get
  * dK = dV = 0 and a query row that sees no key gets dQ = 0.
  */
 attn_status_t attn_bwd(const attn_tensor_t* q, const attn_tensor_t* k, const attn_tensor_t* v,

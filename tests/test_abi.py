@@ -312,14 +312,15 @@ def test_varlen_rejections():
 # ------------------------------------------------------------------ backward
 
 def _bwd_call(dtype=ea.ATTN_BF16, workspace=0xA0000, ws_bytes=1 << 20, dq_shape=None,
-              dout_dtype=None):
+              dout_dtype=None, q_stride=None, dout_stride=None):
     B, H, N, d = 2, 4, 64, 64
-    q = _desc((B, H, N, d), dtype)
+    q = _desc((B, H, N, d), dtype, stride=q_stride)
     k = _desc((B, H, N, d), dtype, data=0x20000)
     v = _desc((B, H, N, d), dtype, data=0x30000)
     o = _desc((B, H, N, d), dtype, data=0x40000)
     lse = _desc((B, H, N, 1), ea.ATTN_F32, data=0x50000, stride=[H * N, N, 1, 1])
-    do = _desc((B, H, N, d), dout_dtype if dout_dtype is not None else dtype, data=0x60000)
+    do = _desc((B, H, N, d), dout_dtype if dout_dtype is not None else dtype, data=0x60000,
+               stride=dout_stride)
     dq = _desc(dq_shape or (B, H, N, d), dtype, data=0x70000)
     dk = _desc((B, H, N, d), dtype, data=0x80000)
     dv = _desc((B, H, N, d), dtype, data=0x90000)
@@ -346,3 +347,13 @@ def test_bwd_rejections():
     assert _bwd_call(workspace=0xA0004) == ea.ATTN_ERR_INVALID
     assert _bwd_call(ws_bytes=8 * 2 * 4 * 64 - 1) == ea.ATTN_ERR_INVALID
     assert "too small" in ea.last_error()
+    # 64 rows of q or dout must span < 2 GiB (the dK/dV kernel's tile
+    # offsets are 32-bit): 64 * 2^24 bf16 elements is exactly 2 GiB
+    big = 1 << 24
+    for kw in ("q_stride", "dout_stride"):
+        assert _bwd_call(**{kw: [64 * big, 64 * big, big, 1]}) == ea.ATTN_ERR_UNSUPPORTED
+        assert "row stride" in ea.last_error()
+        # just under the limit the stride is accepted: the call gets as far
+        # as the (too small) workspace, which is checked after the strides
+        assert _bwd_call(ws_bytes=8, **{kw: [64 * big, 64 * big, big - 8, 1]}) == ea.ATTN_ERR_INVALID
+        assert "too small" in ea.last_error()
