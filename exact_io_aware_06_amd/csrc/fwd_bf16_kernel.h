@@ -160,10 +160,16 @@ __device__ __forceinline__ bf16x8 lds_read_tr_pair(const uint8_t* p0, const uint
 // alias of the copy and wait for it (vmcnt(0)), nor drain the LDS read queue
 // (lgkmcnt(0)) after issuing it: the kernel orders the copies itself with
 // s_waitcnt vmcnt and a barrier before any wave reads the buffer.
+// The compiler's hazard pass cannot see that the asm is a vector-memory
+// load reading M0 and two SGPRs, so the asm carries its own wait states:
+// GFX9-family parts need 1 after a scalar write of M0 before an LDS-DMA load,
+// and 5 after a vector-ALU write of an SGPR (e.g. v_readlane restoring a
+// spilled address register) before a vector-memory instruction reads it.
+// s_nop 4 gives 5 whatever the compiler placed before the copy.
 __device__ __forceinline__ void dma16(const uint8_t* tile, uint32_t off, uint8_t* lds_base) {
   typedef __attribute__((address_space(3))) uint8_t lds_u8;
   const uint32_t lds = (uint32_t)(uintptr_t)(lds_u8*)lds_base;
-  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(tile), "{m0}"(lds));
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(tile), "{m0}"(lds));
 }
 
 // Work item `logical` as (tile, flat head index). group <= 1: tile fastest,
