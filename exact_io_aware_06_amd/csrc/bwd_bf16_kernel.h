@@ -72,6 +72,25 @@ __device__ __forceinline__ int rot_dma_row(int wave, int lane, int i) {
   return perm_row(16 * (a / blk) + ((slot % 16 - 4 * c) & 15));
 }
 
+// DMA instruction i + 1 of a wave copies the rows of instruction i moved on
+// by a fixed step, at the same byte column: its LDS bytes lie W KB further,
+// a whole number of 16-row blocks. So one row and one column per lane
+// describe all of a wave's copies of a tile.
+template <int D, int W>
+constexpr int dma_row_step() {
+  static_assert((W * 1024) % (32 * D) == 0, "a wave's copies must advance by whole 16-row blocks");
+  return 16 * (W * 1024) / (32 * D);
+}
+
+// A copy of a lane-constant value that the compiler must recompute where
+// it is used: at 256 registers, values derived from the lane index that are
+// hoisted out of the stage loop get spilled and reloaded every stage, while
+// recomputing them costs one or two VALU instructions.
+__device__ __forceinline__ int fresh(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 // Row read (A operand) of chunk pair kk: lane-constant offset for even and
 // odd kk (the rotation of chunk 2kk + hi is 8kk + 4hi mod 16); the caller
 // adds 2 mbq * block + 512 kk.
@@ -153,13 +172,12 @@ __global__ __launch_bounds__(64 * W, 2) void bwd_dkdv_kernel(BwdParams p, TileMa
   const int ns = nqb * p.head_group;  // stages: (query head of the group, query tile)
 
   // LDS DMA sources: instruction i of this wave copies 16 bytes of tile row
-  // rrow[i] (the K layout's permuted row), byte column rcol[i]
-  int rrow[G::kDmaPerWave], rcol[G::kDmaPerWave];
-#pragma unroll
-  for (int i = 0; i < G::kDmaPerWave; ++i) {
-    rrow[i] = rot_dma_row<D, W>(wave, lane, i);
-    rcol[i] = k_dma_col<D, W>(wave, lane, i);
-  }
+  // rrow0 + kRowStep * i (the rotated layout's permuted row), byte column
+  // rcol. Two registers instead of one pair per instruction: kept across the
+  // stage loop, per-instruction values were spilled and reloaded each stage.
+  constexpr int kRowStep = dma_row_step<D, W>();
+  const int rrow0 = rot_dma_row<D, W>(wave, lane, 0);
+  const int rcol = k_dma_col<D, W>(wave, lane, 0);
   const int64_t qsn = p.q_sn * 2, dsn = p.do_sn * 2;  // row strides in bytes
   auto stage_head = [&](int s) { return hk * p.head_group + s / nqb; };
   auto stage_q0 = [&](int s) { return q_lo + (s % nqb) * kBt; };
@@ -171,16 +189,17 @@ __global__ __launch_bounds__(64 * W, 2) void bwd_dkdv_kernel(BwdParams p, TileMa
     const uint8_t* qt = reinterpret_cast<const uint8_t*>(static_cast<const __bf16*>(p.q) + b * p.q_sb + h * p.q_sh) + q0 * qsn;
     const uint8_t* dt = reinterpret_cast<const uint8_t*>(static_cast<const __bf16*>(p.do_) + b * p.do_sb + h * p.do_sh) + q0 * dsn;
     uint8_t* st = smem + buf * kStage;
+    const int r0 = fresh(rrow0);
 #pragma unroll
     for (int i = 0; i < G::kDmaPerWave; ++i) {
-      const int r = min(rrow[i], lim);
-      dma16(qt, (uint32_t)(r * (int)qsn + rcol[i]), st + 1024 * (wave + W * i));
-      dma16(dt, (uint32_t)(r * (int)dsn + rcol[i]), st + G::kKBytes + 1024 * (wave + W * i));
+      const int r = min(r0 + kRowStep * i, lim);
+      dma16(qt, (uint32_t)(r * (int)qsn + rcol), st + 1024 * (wave + W * i));
+      dma16(dt, (uint32_t)(r * (int)dsn + rcol), st + G::kKBytes + 1024 * (wave + W * i));
     }
   };
   // negated base-2 LSE (wave 0) and D (wave 1) of stage s: one value per lane
   auto load_stats = [&](int s) {
-    const int h = stage_head(s), qi = stage_q0(s) + lane;
+    const int h = stage_head(s), qi = stage_q0(s) + fresh(lane);
     const int64_t row = ((int64_t)b * p.H + h) * Nq + min(qi, Nq - 1);
     float x = 0.f;
     if (wave == 0) x = (qi < Nq) ? p.lse2[row] : -INFINITY;
@@ -189,8 +208,9 @@ __global__ __launch_bounds__(64 * W, 2) void bwd_dkdv_kernel(BwdParams p, TileMa
   };
   auto store_stats = [&](int buf, float x) {
     float* st = reinterpret_cast<float*>(smem + buf * kStage + 2 * G::kKBytes);
-    if (wave == 0) st[lane] = x;
-    else if (wave == 1) st[kBt + lane] = x;
+    const int ln = fresh(lane);
+    if (wave == 0) st[ln] = x;
+    else if (wave == 1) st[kBt + ln] = x;
   };
   auto wait_tiles = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
@@ -220,7 +240,7 @@ __global__ __launch_bounds__(64 * W, 2) void bwd_dkdv_kernel(BwdParams p, TileMa
     const int h = stage_head(s), q0 = stage_q0(s);
     const uint8_t* Qt = smem + buf * kStage;
     const uint8_t* dOt = Qt + G::kKBytes;
-    const float* lt = reinterpret_cast<const float*>(Qt + 2 * G::kKBytes);
+    const float* lt = reinterpret_cast<const float*>(Qt + 2 * G::kKBytes) + fresh(8 * hi);
     const float* dtv = lt + kBt;
     const float* brow = nullptr;
     if (HAS_BIAS) brow = p.bias + b * p.bias_sb + h * p.bias_sh + min(my_k, Nk - 1);
@@ -255,10 +275,10 @@ __global__ __launch_bounds__(64 * W, 2) void bwd_dkdv_kernel(BwdParams p, TileMa
       u32x4 pb[2], db[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const f32x4 l0 = *reinterpret_cast<const f32x4*>(lt + 32 * mbq + 16 * t + 8 * hi);
-        const f32x4 l1 = *reinterpret_cast<const f32x4*>(lt + 32 * mbq + 16 * t + 8 * hi + 4);
-        const f32x4 d0 = *reinterpret_cast<const f32x4*>(dtv + 32 * mbq + 16 * t + 8 * hi);
-        const f32x4 d1 = *reinterpret_cast<const f32x4*>(dtv + 32 * mbq + 16 * t + 8 * hi + 4);
+        const f32x4 l0 = *reinterpret_cast<const f32x4*>(lt + 32 * mbq + 16 * t);
+        const f32x4 l1 = *reinterpret_cast<const f32x4*>(lt + 32 * mbq + 16 * t + 4);
+        const f32x4 d0 = *reinterpret_cast<const f32x4*>(dtv + 32 * mbq + 16 * t);
+        const f32x4 d1 = *reinterpret_cast<const f32x4*>(dtv + 32 * mbq + 16 * t + 4);
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) {
           float pr[2], ds[2];
@@ -378,12 +398,10 @@ __global__ __launch_bounds__(64 * W, 2) void bwd_dq_kernel(BwdParams p, TileMap 
   if (CAUSAL) wg_keys = min(kend, qend + off);
   const int nt = wg_keys > kstart ? (wg_keys - kstart + kBc - 1) / kBc : 0;
 
-  int rrow[G::kDmaPerWave], rcol[G::kDmaPerWave];
-#pragma unroll
-  for (int i = 0; i < G::kDmaPerWave; ++i) {
-    rrow[i] = rot_dma_row<D, W>(wave, lane, i);
-    rcol[i] = k_dma_col<D, W>(wave, lane, i);
-  }
+  // LDS DMA sources as in the dK/dV kernel: row rrow0 + kRowStep * i, column rcol
+  constexpr int kRowStep = dma_row_step<D, W>();
+  const int rrow0 = rot_dma_row<D, W>(wave, lane, 0);
+  const int rcol = k_dma_col<D, W>(wave, lane, 0);
   const int64_t ksn = p.k_sn * 2, vsn = p.v_sn * 2;
   const uint8_t* kbase = reinterpret_cast<const uint8_t*>(static_cast<const __bf16*>(p.k) + b * p.k_sb + hk * p.k_sh);
   const uint8_t* vbase = reinterpret_cast<const uint8_t*>(static_cast<const __bf16*>(p.v) + b * p.v_sb + hk * p.v_sh);
@@ -395,9 +413,9 @@ __global__ __launch_bounds__(64 * W, 2) void bwd_dq_kernel(BwdParams p, TileMap 
     uint8_t* st = smem + buf * kStage;
 #pragma unroll
     for (int i = 0; i < G::kDmaPerWave; ++i) {
-      const int r = min(rrow[i], lim);
-      dma16(kbase + kv0 * ksn, (uint32_t)(r * (int)ksn + rcol[i]), st + 1024 * (wave + W * i));
-      dma16(vbase + kv0 * vsn, (uint32_t)(r * (int)vsn + rcol[i]), st + G::kKBytes + 1024 * (wave + W * i));
+      const int r = min(rrow0 + kRowStep * i, lim);
+      dma16(kbase + kv0 * ksn, (uint32_t)(r * (int)ksn + rcol), st + 1024 * (wave + W * i));
+      dma16(vbase + kv0 * vsn, (uint32_t)(r * (int)vsn + rcol), st + G::kKBytes + 1024 * (wave + W * i));
     }
   };
   auto wait_tiles = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
