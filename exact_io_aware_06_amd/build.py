@@ -21,11 +21,14 @@ SOURCES = ["attn_abi.cpp", "runtime.hip", "fwd_bf16.hip", "fwd_bf16_split.hip",
            "fwd_bf16_local.hip", "fwd_bf16_local_split.hip", "fwd_bf16_varlen.hip",
            "fwd_f32.hip", "combine.hip", "bwd_bf16.hip", "bwd_bf16_masked.hip"]
 
-# Per-source additions. The unmasked backward kernels are scheduled with the
+# Per-source additions. The backward kernels are scheduled with the
 # compiler's iterative-maxocc strategy (measured: headline backward 1.91 ->
-# 1.76 ms; the masked variants are slower with it and keep the default).
+# 1.76 ms, c3 causal backward 1.13 -> 1.09 ms); on the forward it measured
+# within noise of the default and is not used.
+_BWD_SCHED = ["-mllvm", "--amdgpu-sched-strategy=iterative-maxocc"]
 EXTRA_FLAGS = {
-    "bwd_bf16.hip": ["-mllvm", "--amdgpu-sched-strategy=iterative-maxocc"],
+    "bwd_bf16.hip": _BWD_SCHED,
+    "bwd_bf16_masked.hip": _BWD_SCHED,
 }
 
 # -packed-fp32-ops: keep the compiler from emitting v_pk_{add,mul,fma}_f32.

@@ -1,8 +1,7 @@
 // Attention backward with recomputation, bfloat16 storage, gfx950 (MI355X):
 // kernel templates and the per-variant launcher. Instantiated in
 // bwd_bf16.hip (no mask edge: the preprocess, the dispatch and the
-// unmasked variants) and bwd_bf16_masked.hip (causal and window variants),
-// which the build compiles with different scheduler settings.
+// unmasked variants) and bwd_bf16_masked.hip (causal and window variants).
 //
 // What is computed: for an upstream gradient dO of O = softmax_row(S) V with
 // S = scale * Q K^T + Bias (masks as -inf),

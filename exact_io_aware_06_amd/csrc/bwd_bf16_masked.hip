@@ -1,6 +1,6 @@
 // Attention backward, bfloat16: the dK/dV and dQ instantiations with a
-// causal or window edge (default scheduling; the unmasked ones are in
-// bwd_bf16.hip).
+// causal or window edge (the unmasked ones, the preprocess and the dispatch
+// are in bwd_bf16.hip).
 
 #include "bwd_bf16_kernel.h"
 
