@@ -158,6 +158,29 @@ def test_bias_broadcast_and_key_lengths(dtype):
             assert np.all(o[1] == 0.0) and np.all(np.isneginf(lse[1]))
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_key_lengths_without_bias(d, dtype, causal):
+    # key lengths alone (no bias tensor): no keys, one key, exactly one and
+    # just over one 64-key tile, a ragged tail and all keys; the unbiased,
+    # unmasked bf16 kernel computes half of each tile's probabilities ahead
+    # of the tile, so partial and empty tiles pass through that path too
+    g = torch.Generator().manual_seed(18)
+    B, H, Nq, Nk = 6, 2, 150, 300
+    st = torch.bfloat16 if dtype == "bf16" else torch.float32
+    q = torch.randn(B, H, Nq, d, generator=g).to(st)
+    k = torch.randn(B, H, Nk, d, generator=g).to(st)
+    v = torch.randn(B, H, Nk, d, generator=g).to(st)
+    kv_len = torch.tensor([Nk, 0, 1, 64, 65, 190], dtype=torch.int32)
+    inp = {"q": q, "k": k, "v": v, "bias": None, "kv_len": kv_len, "causal": causal,
+           "scale": d ** -0.5}
+    o, lse = run_gpu(inp)
+    ro, rl = run_oracle(inp)
+    compare(o, lse, ro, rl, dtype, f"key lengths d={d} causal={causal}")
+    assert np.all(o[1] == 0.0) and np.all(np.isneginf(lse[1]))
+
+
 def test_no_keys_at_all():
     q = torch.randn(2, 2, 40, 64).to(torch.bfloat16)
     k = torch.zeros(2, 2, 0, 64, dtype=torch.bfloat16)
