@@ -187,6 +187,7 @@ attn_status_t prepare(const attn_tensor_t* q, const attn_tensor_t* k, const attn
   p.causal = causal ? 1 : 0;
   p.bias_vec = bias_vec ? 1 : 0;
   p.scale_log2 = scale * 1.44269504088896341f;
+  p.scale = scale;
   p.n_split = 1;
   p.pack = 1;
 

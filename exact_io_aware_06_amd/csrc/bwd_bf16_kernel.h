@@ -81,14 +81,6 @@ constexpr int dma_row_step() {
   return 16 * (W * 1024) / (32 * D);
 }
 
-// A copy of a lane-constant value that the compiler must recompute where
-// it is used: at 256 registers, values derived from the lane index that are
-// hoisted out of the stage loop get spilled and reloaded every stage, while
-// recomputing them costs one or two VALU instructions.
-__device__ __forceinline__ int fresh(int x) {
-  asm volatile("" : "+v"(x));
-  return x;
-}
 
 // Row read (A operand) of chunk pair kk: lane-constant offset for even and
 // odd kk (the rotation of chunk 2kk + hi is 8kk + 4hi mod 16); the caller

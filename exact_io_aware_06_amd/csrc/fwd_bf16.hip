@@ -30,7 +30,8 @@ int fwd_bf16_rows(int d, int64_t nrows, bool causal, bool bias, bool split) {
   return 256;
 }
 
-int launch_fwd_bf16(const FwdParams& p, int d, void* stream) {
+int launch_fwd_bf16(const FwdParams& p_in, int d, void* stream) {
+  FwdParams p = p_in;
   const bool split = p.n_split > 1;
   const bool packed = split && p.pack > 1;
   const bool varlen = p.cu_q != nullptr;
@@ -61,6 +62,11 @@ int launch_fwd_bf16(const FwdParams& p, int d, void* stream) {
     const int64_t groups = (int64_t)p.B * p.H;
     tm.per_xcd = (int)((groups + 7) / 8 * tm.n_qtiles);
   }
+  // d = 64 biased kernels stage each wave's 32 bias rows in LDS by DMA when
+  // every row start is 16-byte aligned, whole 4-key chunks cover the keys,
+  // rows belong to one head (no packing) and 32 rows fit 32-bit offsets
+  p.bias_dma = (p.bias != nullptr && d == 64 && p.bias_vec && p.Nk >= 4 && p.Nk % 4 == 0 &&
+                !packed && 32 * p.bias_sn * 4 + 256 < ((int64_t)1 << 31)) ? 1 : 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (varlen) return (int)launch_bf16_varlen(p, tm, d, waves, s);
   if (p.local) return (int)launch_bf16_local(p, tm, d, waves, s);

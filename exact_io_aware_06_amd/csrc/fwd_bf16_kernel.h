@@ -93,6 +93,10 @@ struct Geo {
   static constexpr int kSmem = 2 * (kKBytes + kVBytes);
   static constexpr int kDma = kKBytes / 1024;         // 1 KB DMA instructions per tile (K or V)
   static constexpr int kDmaPerWave = kDma / W;
+  // Bias tiles staged in LDS (d = 64 biased kernels): each wave copies the
+  // 32 x 64 fp32 bias block of its own rows, 8 KB.
+  static constexpr int kBiasWave = 32 * kBc * 4;
+  static constexpr int kBiasBytes = W * kBiasWave;
   static constexpr int kNkk = D / 16;                 // k-steps of QK^T
   static constexpr int kNcb = D / 32;                 // 32-wide output column blocks
 };
@@ -142,6 +146,25 @@ __device__ __forceinline__ float lane_pair_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
                                             false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// A copy of a lane-constant value that the compiler must recompute where it
+// is used: at 256 registers, values derived from the lane index that are
+// hoisted out of a loop get spilled and reloaded every iteration, while
+// recomputing them costs one or two vector instructions.
+__device__ __forceinline__ int fresh(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// A pointer that every lane holds, moved to scalar registers (the copy
+// instructions take their base address from an SGPR pair; the compiler may
+// keep a value derived from per-lane data in VGPRs even when it is uniform).
+__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
+  const uint64_t x = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
+  return reinterpret_cast<const uint8_t*>(((uint64_t)hi << 32) | lo);
 }
 
 // Two LDS transpose reads (4 keys each) concatenated into one MFMA operand.
@@ -449,13 +472,88 @@ __global__ __launch_bounds__(64 * W, 2) void fwd_bf16_kernel(FwdParams p, TileMa
     brow = p.bias + b * p.bias_sb + row_h * p.bias_sh + (int64_t)qrow * p.bias_sn + kbeg + 8 * hi;
   }
 
+  // ---- bias tiles through LDS (d = 64, host-checked layout, p.bias_dma):
+  // each wave copies the bias block of its own 32 rows into its own 8 KB of
+  // LDS (no other wave reads it, so no barrier is involved). The block of
+  // tile t+1 is copied right after the wave has read that of tile t (in
+  // iteration t-1, after that iteration's K/V copies). Vector memory
+  // operations complete in issue order, so that iteration ends with
+  // vmcnt(8) (the block may still be in flight; every K/V copy has landed),
+  // and iteration t waits vmcnt(kNdma) before reading it (its own K/V
+  // copies, issued later, may still be in flight): each block has about a
+  // full iteration to arrive instead of being loaded where it is used.
+  // LDS layout of a wave's block: 16-byte chunk kc (keys 4kc..4kc+3) of
+  // row r at slot 16 r + (kc ^ (r % 16)), so the 16 lanes of one row copy
+  // 256 contiguous bytes and the reads of 16 rows hit 16 different banks.
+  constexpr bool kBiasLds = HAS_BIAS && D == 64;
+  const bool bias_dma = kBiasLds && p.bias_dma;
+  uint8_t* const bias_lds = smem + G::kSmem + wave * G::kBiasWave;
+  const uint8_t* bias_wave = nullptr;  // row min(qw0, Nq-1) of the bias, key kbeg
+  int bias_rmax = 0;                   // rows of this wave that exist, minus 1
+  uint32_t boff[kBiasLds ? 8 : 1];     // lane's source offsets for a full tile
+  if constexpr (kBiasLds) {
+    if (bias_dma) {
+      const int rbase = min(qw0, Nq - 1);
+      bias_rmax = Nq - 1 - rbase;
+      bias_wave = reinterpret_cast<const uint8_t*>(p.bias + b * p.bias_sb + row_h * p.bias_sh +
+                                                   (int64_t)rbase * p.bias_sn + kbeg);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = 4 * i + (lane >> 4);
+        const int kc = (lane & 15) ^ (r & 15);
+        boff[i] = (uint32_t)(min(r, bias_rmax) * (int)(p.bias_sn * 4) + 16 * kc);
+      }
+    }
+  }
+  // copy the block of tile j (the last tile's chunks past the last key read
+  // the row's last four keys instead: finite, and masked)
+  auto dma_bias = [&](int j) {
+    if constexpr (kBiasLds) {
+      const int kv0 = j * kBc;
+      const uint8_t* t = uniform_ptr(bias_wave + 4 * kv0);
+      if (kv0 + kBc <= Nk) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) dma16(t, boff[i], bias_lds + 1024 * i);
+      } else {
+        const int ln = fresh(lane);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int r = 4 * i + (ln >> 4);
+          const int kc = (ln & 15) ^ (r & 15);
+          const int key = min(4 * kc, Nk - 4 - kv0);
+          dma16(t, (uint32_t)(min(r, bias_rmax) * (int)(p.bias_sn * 4) + 4 * key),
+                bias_lds + 1024 * i);
+        }
+      }
+    }
+  };
+
   // Bias and masks of tile j. Register r of block bb holds key
-  // kv0 + 32bb + 16(r/8) + 8hi + (r%8).
+  // kv0 + 32bb + 16(r/8) + 8hi + (r%8). With a bias the scores become
+  // scale * qk + bias in natural units (one FMA); the exponent's FMA turns
+  // them into base 2 (without one, the raw qk goes there with scale * log2 e).
   auto mask_bias = [&](int j, f32x16 (&s)[2]) {
     const int kv0 = j * kBc;
     if (HAS_BIAS) {
       f32x16 bia[2];
       const bool fullb = p.bias_vec && kv0 + kBc <= Nk;
+      if (bias_dma) {
+        // this wave's block of tile j, from LDS (see dma_bias): chunk
+        // 8bb + 4s2 + 2hi + half of row l32
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * G::kDmaPerWave) : "memory");
+        const uint8_t* rowp = bias_lds + 256 * l32;
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+              const int kc = 8 * bb + 4 * s2 + 2 * hi + half;
+              const f32x4 x = *reinterpret_cast<const f32x4*>(rowp + 16 * (kc ^ (l32 & 15)));
+#pragma unroll
+              for (int e = 0; e < 4; ++e) bia[bb][8 * s2 + 4 * half + e] = x[e];
+            }
+      } else {
 #pragma unroll
       for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
@@ -475,10 +573,16 @@ __global__ __launch_bounds__(64 * W, 2) void fwd_bf16_kernel(FwdParams p, TileMa
             for (int e = 0; e < 8; ++e) bia[bb][8 * s2 + e] = (k0 + e < Nk) ? src[e] : 0.f;
           }
         }
+      }
 #pragma unroll
       for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[bb][r] = __builtin_fmaf(s[bb][r], c2, bia[bb][r] * kLog2e);
+        for (int r = 0; r < 16; ++r) s[bb][r] = __builtin_fmaf(s[bb][r], p.scale, bia[bb][r]);
+      if (bias_dma && j + 1 < nt) {
+        // the block of tile j+1 replaces it once this wave's reads are done
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        dma_bias(j + 1);
+      }
     }
     const bool need_mask = (kv0 + kBc > kend) || (CAUSAL && kv0 + kBc - 1 > qmin_w + off) ||
                            (LOCAL && kv0 < qmax_w + off_l);
@@ -511,7 +615,7 @@ __global__ __launch_bounds__(64 * W, 2) void fwd_bf16_kernel(FwdParams p, TileMa
 #pragma unroll
       for (int r = 0; r < 16; ++r) m = fmaxf(m, s[bb][r]);
     m = lane_pair_max(m);
-    return HAS_BIAS ? m : m * c2;
+    return m * (HAS_BIAS ? kLog2e : c2);
   };
   // Exponential slice: scores 2i and 2i+1 of the tile (block i/8, registers
   // 2(i%8), 2(i%8)+1) -> probabilities, their sum, and one packed bf16 pair
@@ -522,7 +626,7 @@ __global__ __launch_bounds__(64 * W, 2) void fwd_bf16_kernel(FwdParams p, TileMa
     float x[2];
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      const float t = HAS_BIAS ? (s[bb][r + e] - m_use) : __builtin_fmaf(s[bb][r + e], c2, -m_use);
+      const float t = __builtin_fmaf(s[bb][r + e], HAS_BIAS ? kLog2e : c2, -m_use);
       x[e] = __builtin_amdgcn_exp2f(t);
       rs += x[e];
     }
@@ -699,7 +803,11 @@ __global__ __launch_bounds__(64 * W, 2) void fwd_bf16_kernel(FwdParams p, TileMa
     if constexpr (kNext) mask_bias(j + 1, sn);
     phase_b(has_next, vlane + cur * G::kVBytes, pb, sn, m_run == -INFINITY ? 0.f : m_run, rs_half);
     if constexpr (kNext) {
-      wait_tiles();
+      // a bias block copied above (tile j+2 exists) may stay in flight
+      if (bias_dma && j + 2 < nt)
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      else
+        wait_tiles();
       __syncthreads();
     }
   };
@@ -711,6 +819,7 @@ __global__ __launch_bounds__(64 * W, 2) void fwd_bf16_kernel(FwdParams p, TileMa
     load_k(0);
     load_v(0);
     if (nt > 1) load_k(1);
+    if (bias_dma) dma_bias(0);
     wait_tiles();
     __syncthreads();
     qk_plain(klane, sa);
@@ -783,16 +892,18 @@ __global__ __launch_bounds__(64 * W, 2) void fwd_bf16_kernel(FwdParams p, TileMa
 template <int D, int W, bool CAUSAL, bool HAS_BIAS, bool SPLIT, bool LOCAL, bool VARLEN>
 hipError_t launch_one(const FwdParams& p, const TileMap& tm, hipStream_t stream) {
   using G = Geo<D, W>;
+  // d = 64 biased kernels also hold the staged bias blocks
+  constexpr int kSmemAll = G::kSmem + ((HAS_BIAS && D == 64) ? G::kBiasBytes : 0);
   static bool attr_set = false;  // benign race: every caller sets the same value
   auto kern = fwd_bf16_kernel<D, W, CAUSAL, HAS_BIAS, SPLIT, LOCAL, VARLEN>;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, G::kSmem);
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kSmemAll);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const int grid = 8 * tm.per_xcd;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(G::kThreads), G::kSmem, stream, p, tm);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(G::kThreads), kSmemAll, stream, p, tm);
   return hipGetLastError();
 }
 

@@ -27,7 +27,11 @@ struct FwdParams {
   int32_t head_group;        // H / Hk
   int32_t causal;
   int32_t bias_vec;          // 1: every bias row start is 16-byte aligned
+  int32_t bias_dma;          // 1: d = 64 kernels stage bias tiles in LDS (set
+                             // by the launcher: bias_vec, Nk % 4 == 0, no
+                             // packed heads, 32 rows and a row within 2 GiB)
   float scale_log2;          // scale * log2(e): scores go to base-2 units
+  float scale;               // the softmax scale itself (biased kernels)
 
   // Split over keys (flash-decoding). n_split == 1: each workgroup covers all
   // keys of its query tile and writes o / lse. n_split > 1: a workgroup
