@@ -39,7 +39,7 @@ int launch_fwd_bf16(const FwdParams& p_in, int d, void* stream) {
   const int64_t nrows = varlen ? p.max_q : packed ? (int64_t)p.pack * p.Nq : p.Nq;
   const int br = fwd_bf16_rows(d, nrows, p.causal != 0, p.bias != nullptr, split);
   const int waves = br / 32;
-  TileMap tm;
+  TileMap tm{};
   tm.n_qtiles = (int)((nrows + br - 1) / br);
   const int64_t total = (int64_t)p.B * (packed ? p.Hk : p.H) * tm.n_qtiles;
   tm.total = (int)total;
@@ -53,6 +53,17 @@ int launch_fwd_bf16(const FwdParams& p_in, int d, void* stream) {
   if (p.n_split > 1) {
     tm.n_split = p.n_split;
     const int64_t all = total * p.n_split;
+    tm.total = (int)all;
+    tm.per_xcd = (int)((all + 7) / 8);
+    tm.batch_inner = 0;
+  }
+  // Paired batches for d = 64 with a batch-broadcast bias and key lengths
+  // (the kernel ranks the batches by key length on the device; B <= 64 so
+  // that one wavefront holds them)
+  if (d == 64 && !split && !varlen && !p.causal && !p.local && p.bias != nullptr &&
+      p.bias_sb == 0 && p.kv_len != nullptr && p.B >= 2 && p.B <= 64) {
+    tm.pairs = (p.B + 1) / 2;
+    const int64_t all = (int64_t)p.H * tm.n_qtiles * tm.pairs;
     tm.total = (int)all;
     tm.per_xcd = (int)((all + 7) / 8);
     tm.batch_inner = 0;

@@ -278,8 +278,51 @@ __global__ __launch_bounds__(64 * W, 2) void fwd_bf16_kernel(FwdParams p, TileMa
   // packed: the query heads of one key/value head share the workgroup's rows
   const bool packed = SPLIT && p.pack > 1;
   int b, h, qt, split;
-  if (!decode_tile<SPLIT, VARLEN>(tm, p.B, packed ? p.Hk : p.H, b, h, qt, split)) return;
+  // Paired batches (d = 64 with a batch-broadcast bias and key lengths,
+  // tm.pairs > 0): the batches are ranked by key length (longest first) and
+  // the workgroup of pair r runs two items of one (head, query tile): the
+  // batch of rank r, then that of rank B-1-r, so every workgroup does about
+  // the same work whatever the lengths (a long batch with a short one), and
+  // the batches of one bias tile run together. Without pairing, items of
+  // very different lengths share the CUs and the last CUs to finish hold the
+  // whole launch (list-scheduling model of the padded-bias workload: 1.5x
+  // the balanced time).
+  constexpr bool kPairable = D == 64 && HAS_BIAS && !CAUSAL && !SPLIT && !VARLEN;
+  int b_next = -1;
+  if (kPairable && tm.pairs > 0) {
+    const int w = blockIdx.x;
+    const int logical = (w & 7) * tm.per_xcd + (w >> 3);
+    if (logical >= tm.total) return;
+    const int pr = logical % tm.pairs;
+    const int rest = logical / tm.pairs;
+    qt = rest % tm.n_qtiles;
+    h = rest / tm.n_qtiles;
+    split = 0;
+    // rank of batch `lane` (B <= 64): longer key lengths first, ties by index
+    const int ln = threadIdx.x & 63;
+    const int kl = ln < p.B ? min(max(p.kv_len[ln], 0), p.Nk) : -1;
+    int rank = 0;
+    for (int j = 0; j < p.B; ++j) {
+      const int kj = __builtin_amdgcn_readlane(kl, j);
+      rank += (kj > kl || (kj == kl && j < ln)) ? 1 : 0;
+    }
+    auto batch_of = [&](int r) {
+      return (int)__builtin_ctzll(__builtin_amdgcn_ballot_w64(ln < p.B && rank == r));
+    };
+    b = batch_of(pr);
+    if (p.B - 1 - pr != pr) b_next = batch_of(p.B - 1 - pr);
+  } else if (!decode_tile<SPLIT, VARLEN>(tm, p.B, packed ? p.Hk : p.H, b, h, qt, split)) {
+    return;
+  }
 
+  for (int item = 0; item < (kPairable ? 2 : 1); ++item) {
+  if (item == 1) {
+    if (b_next < 0) break;
+    b = b_next;
+    // the first item's last reads of the K/V and bias buffers are done
+    // before the second item's prologue copies into them
+    __syncthreads();
+  }
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: kept in SGPRs
@@ -887,6 +930,7 @@ __global__ __launch_bounds__(64 * W, 2) void fwd_bf16_kernel(FwdParams p, TileMa
       lrow[my_q] = (l_tot > 0.f) ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
     }
   }
+  }  // items
 }
 
 template <int D, int W, bool CAUSAL, bool HAS_BIAS, bool SPLIT, bool LOCAL, bool VARLEN>

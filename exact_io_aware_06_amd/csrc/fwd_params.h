@@ -118,6 +118,10 @@ struct TileMap {
   int32_t n_split;       // key splits per query tile (1: no split)
   int32_t group;         // > 1: flat (batch, head) indices dealt in groups of
                          // this many, tile index slow within a group
+  int32_t pairs;         // > 0: paired batches (d = 64, broadcast bias, key
+                         // lengths): pairs per (head, query tile), the
+                         // workgroup of pair r runs the batches of key-length
+                         // rank r and B-1-r; total = H * n_qtiles * pairs
 };
 
 // Number of flat heads to deal together so that one XCD's resident

@@ -181,6 +181,30 @@ def test_key_lengths_without_bias(d, dtype, causal):
     assert np.all(o[1] == 0.0) and np.all(np.isneginf(lse[1]))
 
 
+@pytest.mark.parametrize("B,lens", [
+    (7, [300, 64, 300, 0, 1, 129, 64]),        # odd count (the middle rank runs alone), ties
+    (64, None),                                # the most batches ranked on the device
+    (65, None),                                # one more: the unpaired order
+])
+def test_bias_key_lengths_paired_batches(B, lens):
+    # d = 64 with a bias shared by the batch and key lengths: workgroups run
+    # two batches each, paired by key-length rank (longest with shortest)
+    g = torch.Generator().manual_seed(19)
+    H, Nq, Nk, d = 2, 130, 300, 64
+    q = torch.randn(B, H, Nq, d, generator=g).to(torch.bfloat16)
+    k = torch.randn(B, H, Nk, d, generator=g).to(torch.bfloat16)
+    v = torch.randn(B, H, Nk, d, generator=g).to(torch.bfloat16)
+    if lens is None:
+        lens = torch.randint(0, Nk + 40, (B,), generator=g).tolist()  # some past Nk
+    kv_len = torch.tensor(lens, dtype=torch.int32)
+    bias = torch.randn(1, H, Nq, Nk, generator=g) * 0.5
+    inp = {"q": q, "k": k, "v": v, "bias": bias, "kv_len": kv_len, "causal": False,
+           "scale": 0.125}
+    o, lse = run_gpu(inp)
+    ro, rl = run_oracle(inp)
+    compare(o, lse, ro, rl, "bf16", f"paired batches B={B}")
+
+
 def test_no_keys_at_all():
     q = torch.randn(2, 2, 40, 64).to(torch.bfloat16)
     k = torch.zeros(2, 2, 0, 64, dtype=torch.bfloat16)
