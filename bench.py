@@ -302,6 +302,9 @@ def main(argv=None):
                     help="time the backward (attn_bwd) of the workload instead of the forward")
     ap.add_argument("--splits", type=int, default=None,
                     help="split count for a decoding workload (default: the library's choice)")
+    ap.add_argument("--cold", action="store_true",
+                    help="cold caches: write a 512 MiB buffer before every timed call and "
+                         "report the median call (each call timed on its own)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -386,14 +389,38 @@ def main(argv=None):
         step()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(args.steps):
-        step()
-    stop.record(stream)
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(stop) / args.steps
+
+    def per_call(n, flush=None):
+        # each call between its own pair of events (after the main timing, so
+        # the recorded events do not sit between the timed launches)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n)]
+        for a, b in evs:
+            if flush is not None:
+                flush.fill_(1.0)
+            a.record(stream)
+            step()
+            b.record(stream)
+        torch.cuda.synchronize()
+        t = sorted(a.elapsed_time(b) for a, b in evs)
+        return {"median": round(t[len(t) // 2], 4), "min": round(t[0], 4), "calls": n}
+
+    if args.cold:
+        # the L2s and the MALL hold far less than 512 MiB: writing it evicts the
+        # inputs, so each call reads them from HBM again
+        flush = torch.empty(512 << 18, dtype=torch.float32, device=dev)
+        calls = per_call(max(args.steps, 1), flush)
+        ms = calls["median"]
+    else:
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for _ in range(args.steps):
+            step()
+        stop.record(stream)
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(stop) / args.steps
+        calls = per_call(min(max(args.steps, 1), 50))
 
     flops = w.flops() if w.window is None else window_flops(w)
     tflops = flops / (ms * 1e-3) / 1e12
@@ -429,8 +456,11 @@ def main(argv=None):
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": w.dtype, "data": "synthetic",
-        "config": {**w.describe(), "flops_per_step": flops, **extra, "parallelism": "single GPU"},
+        "config": {**w.describe(), "flops_per_step": flops, **extra, "parallelism": "single GPU",
+                   "caches": "cold (512 MiB written before each call; value from the median call)"
+                   if args.cold else "warm (inputs resident)"},
         "roofline": roofline, "cpu_baseline": cpu,
+        "per_call_ms": calls,
     }
     print(json.dumps(out), flush=True)
     return 0
