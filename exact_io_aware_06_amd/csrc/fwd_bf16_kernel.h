@@ -823,6 +823,15 @@ __global__ __launch_bounds__(64 * W, 2) void fwd_bf16_kernel(FwdParams p, TileMa
     };
     // a row with no reference yet exponentiates against 0 and takes the
     // rare path below
+    // Causal or window edge: the O^T product of a tile whose every key lies
+    // outside the visible range of all 32 rows of this wave is skipped (its
+    // scores are all masked to -inf, so its probabilities are exactly 0 and
+    // the product would add nothing); the workgroup still copies the tile
+    // for its other waves.
+    auto seen = [&](int t) {
+      const int kv0 = t * kBc;
+      return kv0 <= qmax_w + off && (!LOCAL || kv0 + kBc - 1 >= qmin_w + off_l);
+    };
     float rs = rs_half + phase_a(has_next, klane + (cur ^ 1) * G::kKBytes, sc, sn, pb,
                                  m_run == -INFINITY ? 0.f : m_run, dma);
     if (__builtin_amdgcn_ballot_w64(!(rs <= kBig) || m_run == -INFINITY) != 0) {
@@ -844,7 +853,8 @@ __global__ __launch_bounds__(64 * W, 2) void fwd_bf16_kernel(FwdParams p, TileMa
     l_run += rs;
     rs_half = 0.f;
     if constexpr (kNext) mask_bias(j + 1, sn);
-    phase_b(has_next, vlane + cur * G::kVBytes, pb, sn, m_run == -INFINITY ? 0.f : m_run, rs_half);
+    if (!CAUSAL || seen(j))
+      phase_b(has_next, vlane + cur * G::kVBytes, pb, sn, m_run == -INFINITY ? 0.f : m_run, rs_half);
     if constexpr (kNext) {
       // a bias block copied above (tile j+2 exists) may stay in flight
       if (bias_dma && j + 2 < nt)
