@@ -828,6 +828,7 @@ __global__ __launch_bounds__(64 * W, 2) void fwd_bf16_kernel(FwdParams p, TileMa
     // scores are all masked to -inf, so its probabilities are exactly 0 and
     // the product would add nothing); the workgroup still copies the tile
     // for its other waves.
+    static_assert(!CAUSAL || kPre == 0, "a skipped phase B would drop the next tile's slices");
     auto seen = [&](int t) {
       const int kv0 = t * kBc;
       return kv0 <= qmax_w + off && (!LOCAL || kv0 + kBc - 1 >= qmin_w + off_l);
