@@ -181,6 +181,30 @@ def test_key_lengths_without_bias(d, dtype, causal):
     assert np.all(o[1] == 0.0) and np.all(np.isneginf(lse[1]))
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("aligned", [True, False])
+def test_bias_tiles_staged_and_direct(causal, aligned):
+    # d = 64 with a bias whose rows start 16-byte aligned and a key count
+    # divisible by 4: bias tiles go through LDS (the last, ragged tile with
+    # clamped chunks); a bias view shifted by one element takes the direct
+    # loads instead. Same inputs, same oracle, both within the bars.
+    g = torch.Generator().manual_seed(20)
+    B, H, Nq, Nk, d = 3, 2, 200, 324, 64
+    q = torch.randn(B, H, Nq, d, generator=g).to(torch.bfloat16)
+    k = torch.randn(B, H, Nk, d, generator=g).to(torch.bfloat16)
+    v = torch.randn(B, H, Nk, d, generator=g).to(torch.bfloat16)
+    # rows 4 floats apart from one another (16-byte multiples), the view on
+    # the device so that its strides and offset reach the library as they are
+    store = (torch.randn(B, H, Nq, Nk + 4, generator=g) * 0.7).cuda()
+    bias = store[..., :Nk] if aligned else store[..., 1:Nk + 1]
+    kv_len = torch.tensor([Nk, 5, 130], dtype=torch.int32)
+    inp = {"q": q, "k": k, "v": v, "bias": bias, "kv_len": kv_len, "causal": causal,
+           "scale": 0.125}
+    o, lse = run_gpu(inp)
+    ro, rl = run_oracle({**inp, "bias": bias.cpu()})
+    compare(o, lse, ro, rl, "bf16", f"bias tiles aligned={aligned} causal={causal}")
+
+
 @pytest.mark.parametrize("B,lens", [
     (7, [300, 64, 300, 0, 1, 129, 64]),        # odd count (the middle rank runs alone), ties
     (64, None),                                # the most batches ranked on the device
