@@ -8,13 +8,16 @@
 // the only departures from exact arithmetic are fp32 roundings. This path is
 // for small problems and accuracy checks; it is latency-bound, not tuned.
 //
-//   * One workgroup = 4 wavefronts x 16 query rows; tiles of 32 keys.
+//   * One workgroup = 4 wavefronts x 16 query rows; tiles of 64 keys.
 //   * Scores transposed, S^T = K Q^T: in the 16x16 accumulator lane l holds
 //     query l%16 and keys 4(l/16)..4(l/16)+3 of each 16-key block, so a row
 //     reduction is in-lane plus two cross-lane steps (lanes l^16, l^32).
 //   * O^T += V^T P^T: for the k = 4 contraction, lane group g supplies key
 //     4g + i from accumulator register i; V is read as V[key][c] directly.
-//   * Single-buffered LDS (load, barrier, compute, barrier).
+//   * Single-buffered LDS; the next tile is loaded into registers while the
+//     current one is computed (load latency, not arithmetic, bounds the
+//     small problems this path serves), then stored to LDS between two
+//     barriers.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -29,7 +32,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBr = 16 * kWaves;
-constexpr int kBc = 32;
+constexpr int kBc = 64;
+constexpr int kKb = kBc / 16;   // 16-key blocks of a tile
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kLog2e = 1.44269504088896341f;
 
@@ -139,36 +143,56 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdParams p, TileMap 
   if (HAS_BIAS)
     brow = p.bias + b * p.bias_sb + h * p.bias_sh + (int64_t)min(my_q, Nq - 1) * p.bias_sn;
 
+  // chunk c of a tile (c = tid + kThreads * n): key c / (D/4), columns
+  // 4 (c % (D/4)) .. +3; keys past Nk read as zeros
+  constexpr int kChunks = kBc * D / 4 / kThreads;
+  f32x4 kx[kChunks], vx[kChunks];
+  auto fetch = [&](int j) {
+    const int kv0 = j * kBc;
+#pragma unroll
+    for (int n = 0; n < kChunks; ++n) {
+      const int c = tid + kThreads * n;
+      const int key = c / (D / 4);
+      const int col = (c % (D / 4)) * 4;
+      kx[n] = f32x4{};
+      vx[n] = f32x4{};
+      if (kv0 + key < Nk) {
+        kx[n] = *reinterpret_cast<const f32x4*>(kgp + (int64_t)(kv0 + key) * p.k_sn + col);
+        vx[n] = *reinterpret_cast<const f32x4*>(vgp + (int64_t)(kv0 + key) * p.v_sn + col);
+      }
+    }
+  };
+  if (j0 < nt) fetch(j0);
   for (int j = j0; j < nt; ++j) {
     const int kv0 = j * kBc;
     __syncthreads();
-    for (int c = tid; c < kBc * D / 4; c += kThreads) {
+#pragma unroll
+    for (int n = 0; n < kChunks; ++n) {
+      const int c = tid + kThreads * n;
       const int key = c / (D / 4);
       const int col = (c % (D / 4)) * 4;
-      f32x4 kx{}, vx{};
-      if (kv0 + key < Nk) {
-        kx = *reinterpret_cast<const f32x4*>(kgp + (int64_t)(kv0 + key) * p.k_sn + col);
-        vx = *reinterpret_cast<const f32x4*>(vgp + (int64_t)(kv0 + key) * p.v_sn + col);
-      }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) ks[key * KP + col + e] = kx[e];
-      *reinterpret_cast<f32x4*>(&vs[key * D + col]) = vx;
+      for (int e = 0; e < 4; ++e) ks[key * KP + col + e] = kx[n][e];
+      *reinterpret_cast<f32x4*>(&vs[key * D + col]) = vx[n];
     }
+    if (j + 1 < nt) fetch(j + 1);
     __syncthreads();
     if (kv0 >= wave_keys || (p.local && kv0 + kBc <= qw0 + off_l)) continue;
 
     // S^T blocks: register i of block kb holds key kv0 + 16kb + 4g + i
-    f32x4 sacc[2] = {f32x4{}, f32x4{}};
+    f32x4 sacc[kKb];
+#pragma unroll
+    for (int kb = 0; kb < kKb; ++kb) sacc[kb] = f32x4{};
 #pragma unroll
     for (int s = 0; s < NS; ++s)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < kKb; ++kb) {
         const float a = ks[(16 * kb + l16) * KP + 4 * s + g];
         sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, qf[s], sacc[kb], 0, 0, 0);
       }
 
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < kKb; ++kb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int key = kv0 + 16 * kb + 4 * g + i;
@@ -186,9 +210,9 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdParams p, TileMap 
 
     float mx = sacc[0][0];
 #pragma unroll
-    for (int i = 1; i < 4; ++i) mx = fmaxf(mx, sacc[0][i]);
+    for (int kb = 0; kb < kKb; ++kb)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[1][i]);
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sacc[kb][i]);
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = xor32_max(mx);
     const float m_new = fmaxf(m_run, mx);
@@ -196,7 +220,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdParams p, TileMap 
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
     float rs = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < kKb; ++kb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float e = __builtin_amdgcn_exp2f(sacc[kb][i] - m_use);
@@ -212,7 +236,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(FwdParams p, TileMap 
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < kKb; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float a = vs[(16 * kb + 4 * g + i) * D + 16 * cb + l16];
