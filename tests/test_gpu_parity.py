@@ -205,6 +205,30 @@ def test_bias_tiles_staged_and_direct(causal, aligned):
     compare(o, lse, ro, rl, "bf16", f"bias tiles aligned={aligned} causal={causal}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("aligned", [True, False])
+def test_f32_bias_vector_and_scalar_loads(d, causal, aligned):
+    # fp32: with 16-byte aligned bias rows a lane's four bias values arrive
+    # as one vector load, except where the four keys run past Nk (Nk = 301:
+    # the last group falls back to single loads); a view shifted by one
+    # element takes single loads throughout. Several 16-row workgroups, key
+    # tiles spread over the waves of each, a ragged last tile.
+    g = torch.Generator().manual_seed(21)
+    B, H, Nq, Nk = 2, 2, 70, 301
+    q = torch.randn(B, H, Nq, d, generator=g)
+    k = torch.randn(B, H, Nk, d, generator=g)
+    v = torch.randn(B, H, Nk, d, generator=g)
+    store = (torch.randn(B, H, Nq, Nk + 3, generator=g) * 0.7).cuda()
+    bias = store[..., :Nk] if aligned else store[..., 1:Nk + 1]
+    kv_len = torch.tensor([Nk, 150], dtype=torch.int32)
+    inp = {"q": q, "k": k, "v": v, "bias": bias, "kv_len": kv_len, "causal": causal,
+           "scale": d ** -0.5}
+    o, lse = run_gpu(inp)
+    ro, rl = run_oracle({**inp, "bias": bias.cpu()})
+    compare(o, lse, ro, rl, "f32", f"f32 bias d={d} aligned={aligned} causal={causal}")
+
+
 @pytest.mark.parametrize("B,lens", [
     (7, [300, 64, 300, 0, 1, 129, 64]),        # odd count (the middle rank runs alone), ties
     (64, None),                                # the most batches ranked on the device
