@@ -154,9 +154,7 @@ def bench_varlen(args, w):
     step_p, _, _ = ea.prepare_call(qp, kp, vp, kv_len=kv_len, causal=w.causal, scale=inp["scale"])
 
     def timed(fn):
-        for _ in range(args.warmup):
-            fn()
-        torch.cuda.synchronize()
+        warm_up(fn, args)
         start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         start.record()
         for _ in range(args.steps):
@@ -212,9 +210,7 @@ def bench_backward(args, w):
                          window=w.window)
     step, _, _, _ = ea.prepare_bwd_call(q, k, v, o, lse, do, bias=bias, kv_len=kv_len,
                                         causal=w.causal, scale=inp["scale"], window=w.window)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_up(step, args)
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
     for _ in range(args.steps):
@@ -292,11 +288,39 @@ def cpu_baseline_varlen(inp, w, budget_s=15.0):
                       f"materialising S and P, {dt:.1f} s"}
 
 
+def warm_up(fn, args):
+    """Untimed warm-up before a timed region. With --warmup W: W calls.
+    Without: 30 calls, then as many more as fill about 100 ms, so that calls
+    of a fraction of a millisecond are timed at the clocks a sustained load
+    reaches (a d = 64 call of 80 us measured 15% slower after 30 warm-up
+    calls than after 300). args.warmup becomes the number of calls made,
+    which the JSON line reports."""
+    import torch
+    n = args.warmup if args.warmup is not None else 30
+    for _ in range(n):
+        fn()
+    torch.cuda.synchronize()
+    if args.warmup is None:
+        t0 = time.perf_counter()
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+        per = max((time.perf_counter() - t0) / 10, 1e-6)
+        extra = min(int(0.1 / per), 5000)
+        for _ in range(extra):
+            fn()
+        torch.cuda.synchronize()
+        n += 10 + extra
+    args.warmup = n
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed calls before the timed ones (default: at least 30 and "
+                         "at least about 100 ms of calls)")
     ap.add_argument("--workload", default=None)
     ap.add_argument("--backward", action="store_true",
                     help="time the backward (attn_bwd) of the workload instead of the forward")
@@ -347,7 +371,7 @@ def main(argv=None):
         n = args.gemm_calibration
         a = torch.randn(n, n, dtype=torch.bfloat16, device="cuda")
         b = torch.randn(n, n, dtype=torch.bfloat16, device="cuda")
-        for _ in range(max(args.warmup, 1)):
+        for _ in range(max(args.warmup or 30, 1)):
             c = a @ b
         torch.cuda.synchronize()
         start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -385,9 +409,7 @@ def main(argv=None):
                                  scale=inp["scale"], out=o, lse=lse, split=split,
                                  num_splits=n_split, window=w.window)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_up(step, args)
     stream = torch.cuda.current_stream(dev)
 
     def per_call(n, flush=None):
