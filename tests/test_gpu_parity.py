@@ -207,6 +207,26 @@ def test_bias_tiles_staged_and_direct(causal, aligned):
 
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
+def test_f32_many_tiles_per_wave(d, causal):
+    # fp32 with 1000 keys: every wave of a workgroup runs several key tiles
+    # before the merge (and, causal, the waves of early rows run fewer or
+    # none); key lengths cut some batches short, one to nothing.
+    g = torch.Generator().manual_seed(22)
+    B, H, Nq, Nk = 3, 2, 90, 1000
+    q = torch.randn(B, H, Nq, d, generator=g) * 1.5
+    k = torch.randn(B, H, Nk, d, generator=g)
+    v = torch.randn(B, H, Nk, d, generator=g)
+    kv_len = torch.tensor([Nk, 617, 0], dtype=torch.int32)
+    inp = {"q": q, "k": k, "v": v, "bias": None, "kv_len": kv_len, "causal": causal,
+           "scale": d ** -0.5}
+    o, lse = run_gpu(inp)
+    ro, rl = run_oracle(inp)
+    compare(o, lse, ro, rl, "f32", f"f32 many tiles d={d} causal={causal}")
+    assert np.all(o[2] == 0.0) and np.all(np.isneginf(lse[2]))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("aligned", [True, False])
 def test_f32_bias_vector_and_scalar_loads(d, causal, aligned):
     # fp32: with 16-byte aligned bias rows a lane's four bias values arrive
