@@ -6,7 +6,7 @@
 // Notes", sections 2.4 and 3.1), kept in full single precision: both
 // contractions use v_mfma_f32_16x16x4_f32 and the probabilities stay fp32, so
 // the only departures from exact arithmetic are fp32 roundings. This path is
-// for small problems and accuracy checks; it is latency-bound, not tuned.
+// for small problems and accuracy checks, and laid out for latency.
 //
 //   * One workgroup = 16 query rows; its W = 8 wavefronts split the key
 //     tiles among themselves (wave w takes tiles w, w+W, ...), each keeping its own running maximum, denominator and
