@@ -78,18 +78,69 @@ def window_flops(w):
     return 4.0 * w.B * w.H * w.d * pairs
 
 
-def _blas_threads():
+def _threadpools():
+    """The host thread pools the oracle runs on (BLAS, OpenMP), as numpy and
+    torch loaded them."""
     try:
         from threadpoolctl import threadpool_info
-        n = [d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"]
-        return max(n) if n else 1
+        return [(d.get("user_api"), d.get("internal_api"), d.get("num_threads", 1))
+                for d in threadpool_info()]
     except Exception:
-        return 1
+        return []
+
+
+def _blas_threads():
+    n = [t for api, _, t in _threadpools() if api == "blas"]
+    return max(n) if n else 1
+
+
+def _host():
+    """What the CPU baseline ran on: model, the cores this process may use
+    (sched_getaffinity), and the thread pools."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"cpu_model": model, "affinity_cores": len(os.sched_getaffinity(0)),
+            "os_cpu_count": os.cpu_count(),
+            "omp_num_threads_env": os.environ.get("OMP_NUM_THREADS"),
+            "threadpools": [{"api": a, "impl": i, "threads": t} for a, i, t in _threadpools()]}
+
+
+def _oracle_single_thread():
+    """Single-thread oracle times on the two small configured shapes: the
+    whole fp32 single-head workload and one (b, h) head of the d = 64
+    workload, each the best of three runs with every thread pool held to
+    one thread."""
+    import oracle
+    import workloads
+    from threadpoolctl import threadpool_limits
+    out = {}
+    for name, one_head in (("c1_f32_single_head", False), ("c2_bf16_d64", True)):
+        w = workloads.CONFIGS[name]
+        inp = workloads.make_inputs(w)
+        sl = (lambda t: t[0:1, 0:1]) if one_head else (lambda t: t)
+        q, k, v = (sl(inp[x]).double().numpy() for x in ("q", "k", "v"))
+        best = math.inf
+        with threadpool_limits(limits=1):
+            for _ in range(3):
+                t0 = time.perf_counter()
+                oracle.attention_forward(q, k, v, scale=inp["scale"], causal=w.causal)
+                best = min(best, time.perf_counter() - t0)
+        flops = w.flops() / (w.B * w.H if one_head else 1)
+        out[name + (" (one head)" if one_head else "")] = {
+            "seconds": round(best, 4), "gflops": round(flops / best / 1e9, 3)}
+    return out
 
 
 def cpu_baseline(inp, w, budget_s=15.0):
     """Time the fp64 oracle, as it stands, on whole (b, h) heads of the same
-    inputs until the time budget is spent; report the rate in TFLOP/s."""
+    inputs until the time budget is spent; report the rate in TFLOP/s, the
+    host it ran on, and single-thread times on the two small shapes."""
     import oracle
     q, k, v = inp["q"], inp["k"], inp["v"]
     heads = [(b, h) for b in range(w.B) for h in range(w.H)]
@@ -111,7 +162,11 @@ def cpu_baseline(inp, w, budget_s=15.0):
         "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": _blas_threads(),
         "kind": "oracle",
         "sample": (f"{done} of {len(heads)} (b,h) heads of {w.name} at full "
-                   f"Nq={w.Nq}, Nk={w.Nk}, fp64 materialising S and P, {dt:.1f} s"),
+                   f"Nq={w.Nq}, Nk={w.Nk}, fp64 materialising S and P, {dt:.1f} s; "
+                   "the matrix products run on the BLAS pool (cores = its threads), "
+                   "the exponentials and masks on one thread"),
+        "host": _host(),
+        "single_thread": _oracle_single_thread(),
     }
 
 
@@ -184,7 +239,7 @@ def bench_varlen(args, w):
                    "speedup_vs_padded": round(ms_padded / ms, 3), "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": None},
-        "cpu_baseline": cpu,
+        "cpu_baseline": cpu, "clock_settle": args.clock_settle,
     }
     print(json.dumps(out), flush=True)
     return 0
@@ -253,7 +308,7 @@ def bench_backward(args, w):
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": None, "timed": "preprocess + dK/dV + dQ (whole step)"},
-        "cpu_baseline": cpu,
+        "cpu_baseline": cpu, "clock_settle": args.clock_settle,
     }
     print(json.dumps(out), flush=True)
     return 0
@@ -289,29 +344,29 @@ def cpu_baseline_varlen(inp, w, budget_s=15.0):
 
 
 def warm_up(fn, args):
-    """Untimed warm-up before a timed region. With --warmup W: W calls.
-    Without: 30 calls, then as many more as fill about 100 ms, so that calls
-    of a fraction of a millisecond are timed at the clocks a sustained load
-    reaches (a d = 64 call of 80 us measured 15% slower after 30 warm-up
-    calls than after 300). args.warmup becomes the number of calls made,
-    which the JSON line reports."""
+    """Untimed calls before a timed region, in two parts.
+
+    Clock settling: the GPU's clocks ramp over the first ~20 launches and
+    keep rising for about 100 ms of sustained load (a d = 64 call of 80 us
+    measured 15% slower after 30 calls than after 300), so first the step
+    runs for about 150 ms (at least 10 calls, at most 5000). Then exactly
+    args.warmup warm-up steps (default 30). The JSON line reports both:
+    `warmup` is the warm-up steps, `clock_settle` the settling calls."""
     import torch
-    n = args.warmup if args.warmup is not None else 30
-    for _ in range(n):
+    t0 = time.perf_counter()
+    calls = 0
+    while calls < 10 or (time.perf_counter() - t0 < 0.15 and calls < 5000):
+        fn()
+        calls += 1
+        if calls % 10 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    args.clock_settle = {"calls": calls, "ms": round((time.perf_counter() - t0) * 1e3, 1)}
+    if args.warmup is None:
+        args.warmup = 30
+    for _ in range(args.warmup):
         fn()
     torch.cuda.synchronize()
-    if args.warmup is None:
-        t0 = time.perf_counter()
-        for _ in range(10):
-            fn()
-        torch.cuda.synchronize()
-        per = max((time.perf_counter() - t0) / 10, 1e-6)
-        extra = min(int(0.1 / per), 5000)
-        for _ in range(extra):
-            fn()
-        torch.cuda.synchronize()
-        n += 10 + extra
-    args.warmup = n
 
 
 def main(argv=None):
@@ -319,8 +374,8 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=None,
-                    help="untimed calls before the timed ones (default: at least 30 and "
-                         "at least about 100 ms of calls)")
+                    help="untimed warm-up steps before the timed ones (default 30); they "
+                         "follow about 150 ms of clock-settling calls, reported apart")
     ap.add_argument("--workload", default=None)
     ap.add_argument("--backward", action="store_true",
                     help="time the backward (attn_bwd) of the workload instead of the forward")
@@ -457,6 +512,22 @@ def main(argv=None):
     roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
                 "traffic": _traffic(name, w.dtype)}
+    if inp["bias"] is not None:
+        # A dense fp32 bias of H x Nq x Nk makes the forward HBM-bound: its
+        # algorithmic bytes are Q, K, V read and O written once per head, the
+        # LSE written, the bias read once (it is shared by the batch) and the
+        # key lengths; at 2.5 PFLOP/s and 8 TB/s the matrix work would take
+        # less time than these bytes.
+        eb = 2 if w.dtype == "bf16" else 4
+        algo = (w.B * w.H * w.Nq * (2 * w.d * eb + 4) + 2 * w.B * w.kv_heads * w.Nk * w.d * eb
+                + 4 * inp["bias"].numel()
+                + (0 if inp["kv_len"] is None else 4 * w.B))
+        gbps = algo / (ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS,
+                    "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4),
+                    "traffic": _traffic(name, w.dtype), "bytes_per_step": algo,
+                    "mfma_context": {"achieved_tflops": round(tflops, 2), "peak": peak,
+                                     "frac": round(tflops / peak, 4)}}
     if split:
         eb = 2 if w.dtype == "bf16" else 4
         algo = w.kv_bytes() + w.B * w.H * w.Nq * (2 * w.d * eb + 4)  # K, V; Q, O; LSE
@@ -482,7 +553,7 @@ def main(argv=None):
                    "caches": "cold (512 MiB written before each call; value from the median call)"
                    if args.cold else "warm (inputs resident)"},
         "roofline": roofline, "cpu_baseline": cpu,
-        "per_call_ms": calls,
+        "per_call_ms": calls, "clock_settle": args.clock_settle,
     }
     print(json.dumps(out), flush=True)
     return 0

@@ -110,8 +110,13 @@ attn_status_t prepare(const attn_tensor_t* q, const attn_tensor_t* k, const attn
   if (H > 0 && (Hk < 1 || H % Hk != 0))
     return fail(ATTN_ERR_INVALID, "key/value heads (%lld) must divide query heads (%lld)",
                 (long long)Hk, (long long)H);
-  if (!(std::isfinite(scale) && scale > 0.f))
-    return fail(ATTN_ERR_INVALID, "scale must be finite and > 0 (got %g)", (double)scale);
+  // A NaN or infinite scale is malformed; a finite scale <= 0 is well formed
+  // but outside what the kernels handle (they take the row maximum of the
+  // raw dot products and scale it afterwards, which needs scale > 0).
+  if (!std::isfinite(scale))
+    return fail(ATTN_ERR_INVALID, "scale must be finite (got %g)", (double)scale);
+  if (!(scale > 0.f))
+    return fail(ATTN_ERR_UNSUPPORTED, "scale must be > 0 (got %g)", (double)scale);
   if (B > kMaxExtent || H > kMaxExtent || Nq > kMaxExtent || Nk > kMaxExtent)
     return fail(ATTN_ERR_UNSUPPORTED, "extents above 2^30 are not supported");
   if (d != 64 && d != 128)
@@ -386,7 +391,20 @@ attn_status_t attn_bwd(const attn_tensor_t* q, const attn_tensor_t* k, const att
       if (t->shape[i] != ref->shape[i])
         return fail(ATTN_ERR_INVALID, "%s must have the shape of %s", name, ref == q ? "q" : "k / v");
   }
-  if (empty) return ATTN_OK;  // B, H or Nq is 0: dk, dv need Nq > 0 to be non-zero
+  if (empty) {
+    // B, H or Nq is 0: no query sees any key, so dK = dV = 0 wherever there
+    // are keys (H = 0 with Hk > 0, or Nq = 0 with Nk > 0)
+    const int64_t B = k->shape[0], Hk = k->shape[1], Nk = k->shape[2], d = k->shape[3];
+    if (B == 0 || Hk == 0 || Nk == 0) return ATTN_OK;
+    for (auto [name, t] : {std::pair{"dk", dk}, std::pair{"dv", dv}})
+      if ((s = check_rows(name, t)) != ATTN_OK) return s;
+    for (const attn_tensor_t* t : {dk, dv}) {
+      const int rc = attn::launch_zero_bf16(t->data, B, Hk, Nk, (int)d, st(t, 0), st(t, 1),
+                                            st(t, 2), stream);
+      if (rc != 0) return fail(ATTN_ERR_HIP, "kernel launch failed: %s", attn::hip_error_text(rc));
+    }
+    return ATTN_OK;
+  }
   for (auto [name, t] : {std::pair{"dout", dout}, std::pair{"dq", dq}})
     if ((s = check_rows(name, t)) != ATTN_OK) return s;
   // the dK/dV kernel streams 64-row tiles of q and dout, addressing their

@@ -39,7 +39,33 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
   }
 }
 
+// Zero fill of a strided [B, H, N, d] bf16 tensor: d / 8 lanes per row, one
+// 16-byte store each, grid-stride over all rows.
+__global__ __launch_bounds__(256) void zero_rows_kernel(__bf16* data, int64_t rows, int H, int N,
+                                                        int d8, int64_t sb, int64_t sh, int64_t sn) {
+  const int64_t total = rows * d8;
+  for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < total; t += (int64_t)gridDim.x * 256) {
+    const int64_t r = t / d8;
+    const int c = (int)(t % d8);
+    const int n = (int)(r % N);
+    const int h = (int)((r / N) % H);
+    const int64_t b = r / ((int64_t)N * H);
+    *reinterpret_cast<uint4*>(data + b * sb + h * sh + n * sn + 8 * c) = uint4{0, 0, 0, 0};
+  }
+}
+
 }  // namespace
+
+int launch_zero_bf16(void* data, int64_t B, int64_t H, int64_t N, int d, int64_t sb, int64_t sh,
+                     int64_t sn, void* stream) {
+  const int64_t rows = B * H * N;
+  if (rows == 0) return (int)hipSuccess;
+  const int64_t want = (rows * (d / 8) + 255) / 256;
+  const unsigned grid = (unsigned)(want < 65536 ? want : 65536);
+  hipLaunchKernelGGL(zero_rows_kernel, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<__bf16*>(data), rows, (int)H, (int)N, d / 8, sb, sh, sn);
+  return (int)hipGetLastError();
+}
 
 hipError_t launch_bwd_unmasked(const BwdParams& p, int d, hipStream_t s) {
   const bool bias = p.bias != nullptr;

@@ -296,9 +296,9 @@ __global__ __launch_bounds__(64 * f32_waves<D>()) void fwd_f32_kernel(FwdParams 
     wave_sync();  // the tile is read before the next one overwrites it
   }
 
-  // ---- merge of the four waves' partial results, through LDS: wave w
+  // ---- merge of the kWaves waves' partial results, through LDS: wave w
   // leaves O_w (unnormalised, 16 x D), m_w and l_w of each row in its own
-  // tile space; then wave w finishes the column blocks cb = w, w + 4, ...:
+  // tile space; then wave w finishes the column blocks cb = w, w + kWaves, ...:
   // with m = max_w m_w and s_w = 2^(m_w - m), O = sum_w s_w O_w / sum_w s_w l_w
   float l_w = l_run + __shfl_xor(l_run, 16);
   l_w = xor32_sum(l_w);

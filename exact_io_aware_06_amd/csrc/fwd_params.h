@@ -107,6 +107,9 @@ struct BwdParams {
 };
 
 int launch_bwd_bf16(const BwdParams& p, int d, void* stream);
+// Zero fill of a strided bf16 [B, H, N, d] tensor (rows 16-byte aligned).
+int launch_zero_bf16(void* data, int64_t B, int64_t H, int64_t N, int d, int64_t sb,
+                     int64_t sh, int64_t sn, void* stream);
 
 // How the flat workgroup index maps onto (batch, head, query tile).
 struct TileMap {

@@ -53,8 +53,8 @@ extern "C" {
 
 typedef enum {
   ATTN_OK = 0,
-  ATTN_ERR_INVALID = 1,     /* malformed arguments: null pointer, shape mismatch, bad scale */
-  ATTN_ERR_UNSUPPORTED = 2, /* well-formed but outside what the kernels handle (head dim, dtype, stride, alignment) */
+  ATTN_ERR_INVALID = 1,     /* malformed arguments: null pointer, shape mismatch, NaN or infinite scale */
+  ATTN_ERR_UNSUPPORTED = 2, /* well-formed but outside what the kernels handle (head dim, dtype, stride, alignment, scale <= 0) */
   ATTN_ERR_HIP = 3          /* the HIP runtime refused the launch; see attn_last_error() */
 } attn_status_t;
 
@@ -109,8 +109,10 @@ typedef struct {
  *   causal               non-zero: key j is hidden from query i when
  *                        j > i + (Nk - Nq) (aligned to the bottom-right
  *                        corner, so the last query sees every key)
- *   scale                multiplies QK^T; must be finite and > 0 (callers
- *                        usually pass 1/sqrt(d))
+ *   scale                multiplies QK^T (callers usually pass 1/sqrt(d)); a
+ *                        NaN or infinite scale is ATTN_ERR_INVALID, a finite
+ *                        scale <= 0 ATTN_ERR_UNSUPPORTED (the kernels scale
+ *                        the row maximum of the raw dot products)
  *   o    [B, H,  Nq, d]  output, same dtype as q
  *   lse  [B, H,  Nq, 1]  output, float32; stride[2] must be 1
  *   stream               a hipStream_t, or NULL for the default stream
@@ -282,7 +284,10 @@ int64_t attn_bwd_workspace_size(int64_t B, int64_t H, int64_t Nq);
  * the row stride of q and dout times 64 rows must also span less than
  * 2 GiB (ATTN_ERR_UNSUPPORTED otherwise); the outputs must not overlap the
  * inputs or each other. Keys no query sees get
- * dK = dV = 0 and a query row that sees no key gets dQ = 0.
+ * dK = dV = 0 and a query row that sees no key gets dQ = 0. With B, H or Nq
+ * equal to 0 no query sees any key: the call writes dK = dV = 0 (one small
+ * kernel per tensor, when it has elements; their layout is checked as
+ * above) and needs no workspace.
  */
 attn_status_t attn_bwd(const attn_tensor_t* q, const attn_tensor_t* k, const attn_tensor_t* v,
                        const attn_tensor_t* o, const attn_tensor_t* lse,

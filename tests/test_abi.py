@@ -108,9 +108,17 @@ def test_null_descriptor():
     assert "non-NULL" in ea.last_error()
 
 
-@pytest.mark.parametrize("scale", [0.0, -0.1, math.inf, math.nan])
-def test_bad_scale(scale):
+@pytest.mark.parametrize("scale", [math.inf, -math.inf, math.nan])
+def test_non_finite_scale_is_invalid(scale):
     assert _call(scale=scale) == ea.ATTN_ERR_INVALID
+    assert "scale" in ea.last_error()
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.0, -0.1, -8.0])
+def test_non_positive_scale_is_unsupported(scale):
+    # well formed, but the kernels scale the row maximum of the raw dot
+    # products and need scale > 0
+    assert _call(scale=scale) == ea.ATTN_ERR_UNSUPPORTED
     assert "scale" in ea.last_error()
 
 
@@ -357,3 +365,34 @@ def test_bwd_rejections():
         # as the (too small) workspace, which is checked after the strides
         assert _bwd_call(ws_bytes=8, **{kw: [64 * big, 64 * big, big - 8, 1]}) == ea.ATTN_ERR_INVALID
         assert "too small" in ea.last_error()
+
+
+def _bwd_empty_call(q_shape, kv_shape, dk_data=0x80000):
+    q = _desc(q_shape)
+    k = _desc(kv_shape, data=0x20000)
+    v = _desc(kv_shape, data=0x30000)
+    o = _desc(q_shape, data=0x40000)
+    B, H, N, _ = q_shape
+    lse = _desc((B, H, N, 1), ea.ATTN_F32, data=0x50000, stride=[H * N, N, 1, 1])
+    do = _desc(q_shape, data=0x60000)
+    dq = _desc(q_shape, data=0x70000)
+    dk = _desc(kv_shape, data=dk_data)
+    dv = _desc(kv_shape, data=0x90000)
+    lib = _lib()
+    return lib.attn_bwd(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), ctypes.byref(o),
+                        ctypes.byref(lse), ctypes.byref(do), None, 0, 0.125, None, 0,
+                        ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), None)
+
+
+def test_bwd_empty_query_side():
+    # no query rows, or no query heads, with keys present: dK and dV must be
+    # zeroed, so their layout is checked on the host first (a misaligned dk
+    # is refused before any launch); with no keys either there is nothing to
+    # write and the call returns OK without touching the device
+    assert _bwd_empty_call((2, 4, 0, 64), (2, 2, 300, 64), dk_data=0x80002) == \
+        ea.ATTN_ERR_UNSUPPORTED
+    assert "dk" in ea.last_error()
+    assert _bwd_empty_call((2, 0, 10, 64), (2, 2, 300, 64), dk_data=0x80002) == \
+        ea.ATTN_ERR_UNSUPPORTED
+    assert _bwd_empty_call((2, 4, 0, 64), (2, 2, 0, 64)) == ea.ATTN_OK
+    assert _bwd_empty_call((0, 4, 10, 64), (0, 2, 300, 64)) == ea.ATTN_OK

@@ -104,6 +104,26 @@ def test_bwd_rows_without_keys_and_unseen_keys():
     assert torch.all(got[1][1, :, 100:].cpu() == 0) and torch.all(got[2][1, :, 100:].cpu() == 0)
 
 
+@pytest.mark.parametrize("q_shape,kv_shape", [((2, 4, 0, 128), (2, 2, 300, 128)),
+                                               ((2, 0, 10, 64), (2, 2, 77, 64))])
+def test_bwd_empty_query_side_zeroes_dk_dv(q_shape, kv_shape):
+    # no query rows (or no query heads) but keys present: no query sees any
+    # key, so dK = dV = 0; the outputs start as NaN and dv is a strided view
+    _banner(f"bwd empty query side q={q_shape} kv={kv_shape}")
+    q = torch.zeros(q_shape, dtype=torch.bfloat16, device="cuda")
+    k = torch.randn(kv_shape, device="cuda").to(torch.bfloat16)
+    v = torch.randn(kv_shape, device="cuda").to(torch.bfloat16)
+    o = torch.zeros_like(q)
+    lse = torch.zeros(q_shape[:3], dtype=torch.float32, device="cuda")
+    dk = torch.full(kv_shape, float("nan"), dtype=torch.bfloat16, device="cuda")
+    B, Hk, Nk, d = kv_shape
+    dv_store = torch.full((B, Nk, Hk, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    dv = dv_store.transpose(1, 2)
+    _, dk2, dv2 = ea.attn_bwd(q, k, v, o, lse, torch.zeros_like(q), dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    assert torch.all(dk.cpu() == 0) and torch.all(dv_store.cpu() == 0)
+
+
 @pytest.mark.parametrize("hk", [1, 2])
 def test_bwd_grouped_heads(hk):
     _check(2, 4, hk, 260, 260, 128, seed=83, causal=True)

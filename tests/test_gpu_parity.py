@@ -7,8 +7,9 @@ for the oracle). Bars, written here and nowhere else:
   * no NaN anywhere; a -inf LSE (fully masked row) must match exactly and
     its O row must be exactly zero.
 Small cases are compared element by element; the five full-size workloads
-are run in the launch configuration the benchmark times and checked on
-sampled rows plus properties that hold at any size.
+are run in the launch configuration the benchmark times, into outputs
+pre-filled with NaN, and checked on one row of every query tile, on every
+row of the first and last head, and on properties that hold at any size.
 """
 
 import math
@@ -405,49 +406,120 @@ def test_error_status_raises():
     with pytest.raises(ea.AttnError, match="UNSUPPORTED"):
         ea.attn_fwd(q, q, q)
     q = torch.randn(1, 1, 16, 64, device="cuda").to(torch.bfloat16)
-    with pytest.raises(ea.AttnError, match="INVALID"):
+    with pytest.raises(ea.AttnError, match="UNSUPPORTED"):
         ea.attn_fwd(q, q, q, scale=-1.0)
+    with pytest.raises(ea.AttnError, match="INVALID"):
+        ea.attn_fwd(q, q, q, scale=float("nan"))
 
 
 # --------------------------------------------------------------- full-size workloads
+#
+# The full-size workloads run in the launch configuration the benchmark
+# times. The outputs are pre-filled with NaN, so a row that no workgroup
+# wrote cannot pass as a stale value of an earlier call; every row must come
+# back finite. Then one row of every (batch, head, 128-row query tile) -- a
+# different offset inside each tile, so the rows fall on every wavefront and
+# lane position -- and every row of the first and the last head are compared
+# with the oracle element by element. 128 rows is the smallest workgroup any
+# launch uses, so every workgroup of every launch has at least one row
+# checked. [flash-attention (stanleyjacob.dev), Part XII, testing against a
+# slow reference.]
 
-def _sample_rows(w, n_rows, seed):
+TILE_ROWS = 128
+
+
+def nan_outputs(B, H, Nq, d, dtype):
+    st = torch.bfloat16 if dtype == "bf16" else torch.float32
+    o = torch.full((B, H, Nq, d), float("nan"), dtype=st, device="cuda")
+    lse = torch.full((B, H, Nq), float("nan"), dtype=torch.float32, device="cuda")
+    return o, lse
+
+
+def tile_rows(B, H, Nq, seed, tile=TILE_ROWS):
+    """One row per (b, h, query tile), at a seeded offset inside the tile."""
     r = np.random.default_rng(seed)
     rows = []
-    for _ in range(n_rows):
-        rows.append((int(r.integers(w.B)), int(r.integers(w.H)), int(r.integers(w.Nq))))
-    # first and last rows of the first and last heads, and tile edges
-    for b, h in ((0, 0), (w.B - 1, w.H - 1)):
-        for i in (0, 1, 127, 128, w.Nq - 129, w.Nq - 1):
-            rows.append((b, h, max(0, min(i, w.Nq - 1))))
+    for b in range(B):
+        for h in range(H):
+            for t0 in range(0, Nq, tile):
+                rows.append((b, h, t0 + int(r.integers(min(tile, Nq - t0)))))
     return rows
 
 
+def head_rows(b, h, Nq):
+    return [(b, h, i) for i in range(Nq)]
+
+
+def assert_all_written(o_c, lse_c, what):
+    """Every row was written: no NaN left of the pre-fill anywhere."""
+    assert not torch.isnan(o_c.float()).any(), f"{what}: O rows left unwritten (NaN)"
+    assert not torch.isnan(lse_c).any(), f"{what}: LSE rows left unwritten (NaN)"
+
+
+def compare_rows(o_c, lse_c, rows, oracle_rows, dtype, what, chunk=2048):
+    """Compare the listed rows of a full-size output with the oracle, in
+    chunks of rows so that one head of 16K keys stays within memory.
+    oracle_rows(rows) returns (O [n, d], LSE [n]) in fp64."""
+    for c0 in range(0, len(rows), chunk):
+        part = rows[c0:c0 + chunk]
+        ro, rl = oracle_rows(part)
+        go = np.stack([o_c[b, h, i].double().numpy() for b, h, i in part])
+        gl = np.array([float(lse_c[b, h, i]) for b, h, i in part])
+        compare(go, gl, ro, rl, dtype, f"{what} rows {c0}..{c0 + len(part) - 1}")
+
+
+def full_size_rows(w):
+    """One row of every query tile, then all rows of the first and last head."""
+    return (tile_rows(w.B, w.H, w.Nq, w.seed) + head_rows(0, 0, w.Nq)
+            + head_rows(w.B - 1, w.H - 1, w.Nq))
+
+
 @pytest.mark.parametrize("name", sorted(workloads.CONFIGS))
-def test_full_size_sampled(name):
+def test_full_size_every_tile(name):
     w = workloads.CONFIGS[name]
     _banner(f"full {name}")
     inp = workloads.make_inputs(w)
     q, k, v = (inp[x].cuda() for x in ("q", "k", "v"))
     bias = _to_gpu(inp["bias"])
     kv_len = _to_gpu(inp["kv_len"])
-    o, lse = ea.attn_fwd(q, k, v, bias=bias, kv_len=kv_len, causal=w.causal,
-                         scale=inp["scale"])
+    o, lse = nan_outputs(w.B, w.H, w.Nq, w.d, w.dtype)
+    ea.attn_fwd(q, k, v, bias=bias, kv_len=kv_len, causal=w.causal, scale=inp["scale"],
+                out=o, lse=lse)
     torch.cuda.synchronize()
     o_c = o.cpu()
     lse_c = lse.cpu()
-    # properties at any size: finite, and each O row inside the range of V
-    assert not torch.isnan(o_c.float()).any() and torch.isfinite(lse_c).all()
+    assert_all_written(o_c, lse_c, name)
+    # every configured row sees at least one key
+    assert torch.isfinite(lse_c).all()
+    # each O row inside the range of V (any size)
     vmin = inp["v"].float().amin(dim=2, keepdim=True)
     vmax = inp["v"].float().amax(dim=2, keepdim=True)
     slack = 1e-2 * (vmax - vmin) + 1e-6
     assert bool(((o_c.float() >= vmin - slack) & (o_c.float() <= vmax + slack)).all())
-    rows = _sample_rows(w, 48, seed=w.seed)
     f = lambda t: None if t is None else t.double().numpy()
     kv = None if inp["kv_len"] is None else inp["kv_len"].numpy()
-    ro, rl = oracle.attention_rows(f(inp["q"]), f(inp["k"]), f(inp["v"]), rows,
-                                   scale=inp["scale"], bias=f(inp["bias"]), kv_len=kv,
-                                   causal=w.causal)
-    go = np.stack([o_c[b, h, i].double().numpy() for b, h, i in rows])
-    gl = np.array([float(lse_c[b, h, i]) for b, h, i in rows])
-    compare(go, gl, ro, rl, w.dtype, f"full {name} sampled")
+    qd, kd, vd, bd = f(inp["q"]), f(inp["k"]), f(inp["v"]), f(inp["bias"])
+
+    def oracle_rows(part):
+        return oracle.attention_rows(qd, kd, vd, part, scale=inp["scale"], bias=bd,
+                                     kv_len=kv, causal=w.causal)
+
+    compare_rows(o_c, lse_c, full_size_rows(w), oracle_rows, w.dtype, f"full {name}")
+
+
+# Causal launches deal the flat heads in groups (longest query tiles of a
+# whole group first). Shapes with several groups and a smaller last group,
+# compared in full: d = 128 (256-row tiles, 4 per head, groups of 8 heads:
+# 8 + 7) and d = 64 (128-row tiles, 8 per head, groups of 8: 8 + 8 + 5).
+@pytest.mark.parametrize("d,B,H", [(128, 3, 5), (64, 3, 7)])
+def test_causal_grouped_dispatch_ragged_last_group(d, B, H):
+    w = workloads.Workload("grouped", B, H, 1000, 1000, d, causal=True, seed=31 + d)
+    inp = workloads.make_inputs(w)
+    o, lse = nan_outputs(B, H, 1000, d, "bf16")
+    _banner(f"causal grouped dispatch d={d} B={B} H={H}")
+    ea.attn_fwd(inp["q"].cuda(), inp["k"].cuda(), inp["v"].cuda(), causal=True,
+                scale=inp["scale"], out=o, lse=lse)
+    torch.cuda.synchronize()
+    ro, rl = run_oracle(inp)
+    compare(o.double().cpu().numpy(), lse.double().cpu().numpy(), ro, rl, "bf16",
+            f"causal grouped d={d} B={B} H={H}")

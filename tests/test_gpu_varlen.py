@@ -8,7 +8,8 @@ and not, both head dimensions and dtypes, grouped K/V heads, different query
 and key offsets per sequence (bottom-right causal alignment per sequence),
 a window, rows past the last sequence left untouched, a generous
 max_seqlen_q, offsets outside the tensors (clamped: no access leaves them),
-and the packed workload at full size on sampled rows. [flash-attention
+and the packed workload at full size (one row of every query tile and
+whole sequences, into NaN-filled outputs). [flash-attention
 (stanleyjacob.dev), Part II "Variable-length batches: stop padding", Lab 5.]
 """
 
@@ -127,30 +128,45 @@ def test_varlen_offsets_outside_tensors_are_clamped():
 
 
 @pytest.mark.parametrize("name", sorted(workloads.VARLEN))
-def test_varlen_full_size_sampled(name):
+def test_varlen_full_size_every_tile(name):
+    # NaN-filled outputs (the sequences cover every packed row, so every row
+    # must come back written); one row of every (sequence, head, 128-row
+    # query tile) and every row of the first and last sequence at the first
+    # and last head against the oracle
     w = workloads.VARLEN[name]
     _banner(f"varlen full {name}")
     inp = workloads.make_varlen_inputs(w)
     cu = inp["cu"]
+    T = inp["q"].shape[0]
+    st = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    out = torch.full((T, w.H, w.d), float("nan"), dtype=st, device="cuda")
+    lse = torch.full((w.H, T), float("nan"), dtype=torch.float32, device="cuda")
     o, lse = _run(inp["q"], inp["k"], inp["v"], cu, cu, inp["max_len"], w.causal,
-                  scale=inp["scale"])
+                  scale=inp["scale"], out=out, lse=lse)
     oc, lc = o.cpu(), lse.cpu()
-    assert not torch.isnan(oc.float()).any() and torch.isfinite(lc).all()
+    assert not torch.isnan(oc.float()).any() and not torch.isnan(lc).any()
+    assert torch.isfinite(lc).all()
     r = np.random.default_rng(w.seed)
     c = cu.tolist()
-    go, gl, ro, rl = [], [], [], []
-    for s in list(range(w.B)):
+    rep = w.H // w.kv_heads
+    picks = []   # (sequence, head, rows inside the sequence)
+    for s in range(w.B):
         n = c[s + 1] - c[s]
-        idx = sorted(set([0, n - 1] + [int(x) for x in r.integers(0, n, 2)]))
-        h = int(r.integers(w.H))
-        f = lambda t: t[c[s]:c[s + 1], h].double().numpy()[None, None]
-        oo, ll = oracle.attention_rows(f(inp["q"]), f(inp["k"]), f(inp["v"]),
+        for h in range(w.H):
+            picks.append((s, h, [t0 + int(r.integers(min(128, n - t0))) for t0 in range(0, n, 128)]))
+    for s in (0, w.B - 1):
+        n = c[s + 1] - c[s]
+        for h in (0, w.H - 1):
+            picks.append((s, h, list(range(n))))
+    go, gl, ro, rl = [], [], [], []
+    for s, h, idx in picks:
+        f = lambda t, hh: t[c[s]:c[s + 1], hh].double().numpy()[None, None]
+        oo, ll = oracle.attention_rows(f(inp["q"], h), f(inp["k"], h // rep), f(inp["v"], h // rep),
                                        [(0, 0, i) for i in idx], scale=inp["scale"],
                                        causal=w.causal)
-        for j, i in enumerate(idx):
-            go.append(oc[c[s] + i, h].double().numpy())
-            gl.append(float(lc[h, c[s] + i]))
-            ro.append(oo[j])
-            rl.append(ll[j])
-    compare(np.stack(go), np.array(gl), np.stack(ro), np.array(rl), w.dtype,
-            f"varlen full {name} sampled")
+        go.append(oc[[c[s] + i for i in idx], h].double().numpy())
+        gl.append(lc[h, [c[s] + i for i in idx]].double().numpy())
+        ro.append(oo)
+        rl.append(ll)
+    compare(np.concatenate(go), np.concatenate(gl), np.concatenate(ro), np.concatenate(rl),
+            w.dtype, f"varlen full {name} every tile")
