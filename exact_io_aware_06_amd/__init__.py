@@ -23,6 +23,7 @@ import os
 from typing import Optional
 
 __all__ = ["attn_fwd", "attn_fwd_raw", "attn_fwd_splitkv", "attn_fwd_splitkv_raw",
+           "attn_fwd_splitkv_noalloc", "NOALLOC_SCRATCH_BYTES",
            "attn_fwd_varlen", "prepare_varlen_call", "attn_bwd", "prepare_bwd_call",
            "bwd_workspace_size",
            "splitkv_num_splits", "splitkv_workspace_size", "prepare_call", "AttnError", "load_library", "library_path",
@@ -33,6 +34,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 
 ATTN_OK, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, 1, 2, 3
 ATTN_BF16, ATTN_F32 = 0, 1
+NOALLOC_SCRATCH_BYTES = 8 * 1024 * 1024   # ATTN_NOALLOC_SCRATCH_BYTES of include/attn.h
 _STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_INVALID", 2: "ATTN_ERR_UNSUPPORTED", 3: "ATTN_ERR_HIP"}
 
 
@@ -79,6 +81,10 @@ def load_library():
                                      ctypes.c_float, ctypes.c_int32, ctypes.c_void_p,
                                      ctypes.c_int64, P, P, ctypes.c_void_p]
     lib.attn_fwd_splitkv.restype = ctypes.c_int
+    lib.attn_fwd_splitkv_noalloc.argtypes = [P, P, P, ctypes.POINTER(AttnMask), ctypes.c_int,
+                                             ctypes.c_float, ctypes.c_int32, P, P,
+                                             ctypes.c_void_p]
+    lib.attn_fwd_splitkv_noalloc.restype = ctypes.c_int
     lib.attn_fwd_splitkv_workspace_size.argtypes = [ctypes.c_int64] * 4 + [ctypes.c_int32]
     lib.attn_fwd_splitkv_workspace_size.restype = ctypes.c_int64
     lib.attn_fwd_splitkv_num_splits.argtypes = [ctypes.c_int64] * 6 + [ctypes.c_int] * 2
@@ -234,6 +240,33 @@ def attn_fwd_splitkv(q, k, v, bias=None, kv_len=None, causal: bool = False,
         stream = torch.cuda.current_stream(q.device).cuda_stream
         rc = attn_fwd_splitkv_raw(qd, kd, vd, mask, causal, scale, num_splits,
                                   workspace.data_ptr(), ws_bytes, od, ld, stream)
+    if rc != ATTN_OK:
+        raise AttnError(rc, last_error())
+    return out, lse
+
+
+def attn_fwd_splitkv_noalloc(q, k, v, bias=None, kv_len=None, causal: bool = False,
+                             scale: Optional[float] = None, num_splits: Optional[int] = None,
+                             out=None, lse=None, window=None):
+    """``attn_fwd_splitkv`` without a workspace: the library keeps the split
+    partials in its own per-device scratch array (NOALLOC_SCRATCH_BYTES), so
+    the C call allocates nothing. Outputs are allocated here when not given.
+    Calls that overlap on one device race on the array (use one stream)."""
+    import torch
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if num_splits is None:
+        num_splits = splitkv_num_splits(B, H, Nq, Nk, d, causal, bias is not None, k.shape[1])
+    scale, out, lse, (qd, kd, vd, od, ld, mask, _keep) = _prepare(q, k, v, bias, kv_len, scale,
+                                                                    out, lse, window)
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        rc = lib.attn_fwd_splitkv_noalloc(ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(vd),
+                                          ctypes.byref(mask) if mask is not None else None,
+                                          1 if causal else 0, float(scale), int(num_splits),
+                                          ctypes.byref(od), ctypes.byref(ld),
+                                          ctypes.c_void_p(stream))
     if rc != ATTN_OK:
         raise AttnError(rc, last_error())
     return out, lse

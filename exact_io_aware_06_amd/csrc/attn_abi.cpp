@@ -283,11 +283,17 @@ int32_t attn_fwd_splitkv_num_splits(int64_t B, int64_t H, int64_t Hk, int64_t Nq
   return (int32_t)std::max<int64_t>(n, 1);
 }
 
-attn_status_t attn_fwd_splitkv(const attn_tensor_t* q, const attn_tensor_t* k,
-                               const attn_tensor_t* v, const attn_mask_t* bias_or_mask,
-                               int causal, float scale, int32_t num_splits, void* workspace,
-                               int64_t workspace_bytes, const attn_tensor_t* o,
-                               const attn_tensor_t* lse, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The split-key forward with its partials in `workspace` (the caller's, or,
+// noalloc, this device's scratch array, fetched only once every argument
+// has been checked and a split is needed).
+attn_status_t splitkv(const attn_tensor_t* q, const attn_tensor_t* k, const attn_tensor_t* v,
+                      const attn_mask_t* bias_or_mask, int causal, float scale,
+                      int32_t num_splits, void* workspace, int64_t workspace_bytes, bool noalloc,
+                      const attn_tensor_t* o, const attn_tensor_t* lse, void* stream) {
   g_last_error.clear();
   if (num_splits < 1 || num_splits > kMaxSplits)
     return fail(ATTN_ERR_INVALID, "num_splits must be in [1, %d] (got %d)", kMaxSplits, (int)num_splits);
@@ -305,17 +311,31 @@ attn_status_t attn_fwd_splitkv(const attn_tensor_t* q, const attn_tensor_t* k,
 
   const int64_t need = attn_fwd_splitkv_workspace_size(p.B, p.H, p.Nq, d, (int32_t)n_split);
   if (need < 0) return fail(ATTN_ERR_UNSUPPORTED, "workspace size overflows");
-  if (workspace == nullptr || !aligned16(workspace))
-    return fail(ATTN_ERR_INVALID, "workspace is NULL or not 16-byte aligned");
-  if (workspace_bytes < need)
-    return fail(ATTN_ERR_INVALID, "workspace of %lld bytes is too small (%lld needed for %lld splits)",
-                (long long)workspace_bytes, (long long)need, (long long)n_split);
+  if (noalloc) {
+    if (need > attn::kNoallocScratchBytes)
+      return fail(ATTN_ERR_UNSUPPORTED,
+                  "%lld splits of this shape need %lld bytes of partials, more than the %lld-byte "
+                  "device scratch of the no-allocation entry point (use fewer splits, or "
+                  "attn_fwd_splitkv with a workspace)",
+                  (long long)n_split, (long long)need, (long long)attn::kNoallocScratchBytes);
+  } else {
+    if (workspace == nullptr || !aligned16(workspace))
+      return fail(ATTN_ERR_INVALID, "workspace is NULL or not 16-byte aligned");
+    if (workspace_bytes < need)
+      return fail(ATTN_ERR_INVALID, "workspace of %lld bytes is too small (%lld needed for %lld splits)",
+                  (long long)workspace_bytes, (long long)need, (long long)n_split);
+  }
   const int pack = attn::fwd_bf16_pack(p.head_group, p.Nq);
   const int64_t nrows = (int64_t)pack * p.Nq;
   const int rows = attn::fwd_bf16_rows(d, nrows, p.causal != 0, p.bias != nullptr, true);
   const int64_t wgs = (int64_t)p.B * (p.H / pack) * ((nrows + rows - 1) / rows) * n_split;
   if (wgs > ((int64_t)1 << 31) - 64 || (int64_t)p.B * p.H * p.Nq > ((int64_t)1 << 32))
     return fail(ATTN_ERR_UNSUPPORTED, "problem needs more than 2^31 workgroups");
+  if (noalloc) {
+    const int rc = attn::noalloc_scratch(&workspace);
+    if (rc != 0)
+      return fail(ATTN_ERR_HIP, "device scratch address unavailable: %s", attn::hip_error_text(rc));
+  }
 
   p.kv_split = (int32_t)kv_split;
   p.n_split = (int32_t)n_split;
@@ -326,6 +346,28 @@ attn_status_t attn_fwd_splitkv(const attn_tensor_t* q, const attn_tensor_t* k,
   if (rc == 0) rc = attn::launch_combine_bf16(p, d, stream);
   if (rc != 0) return fail(ATTN_ERR_HIP, "kernel launch failed: %s", attn::hip_error_text(rc));
   return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status_t attn_fwd_splitkv(const attn_tensor_t* q, const attn_tensor_t* k,
+                               const attn_tensor_t* v, const attn_mask_t* bias_or_mask,
+                               int causal, float scale, int32_t num_splits, void* workspace,
+                               int64_t workspace_bytes, const attn_tensor_t* o,
+                               const attn_tensor_t* lse, void* stream) {
+  return splitkv(q, k, v, bias_or_mask, causal, scale, num_splits, workspace, workspace_bytes,
+                 false, o, lse, stream);
+}
+
+attn_status_t attn_fwd_splitkv_noalloc(const attn_tensor_t* q, const attn_tensor_t* k,
+                                       const attn_tensor_t* v, const attn_mask_t* bias_or_mask,
+                                       int causal, float scale, int32_t num_splits,
+                                       const attn_tensor_t* o, const attn_tensor_t* lse,
+                                       void* stream) {
+  return splitkv(q, k, v, bias_or_mask, causal, scale, num_splits, nullptr, 0, true, o, lse,
+                 stream);
 }
 
 attn_status_t attn_fwd_varlen(const attn_tensor_t* q, const attn_tensor_t* k,

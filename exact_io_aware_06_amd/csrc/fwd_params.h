@@ -5,7 +5,15 @@
 
 #include <stdint.h>
 
+#include "attn.h"
+
 namespace attn {
+
+// Size of the per-device scratch array behind attn_fwd_splitkv_noalloc.
+constexpr int64_t kNoallocScratchBytes = ATTN_NOALLOC_SCRATCH_BYTES;
+// The calling thread's current device's address of that array (fetched with
+// hipGetSymbolAddress on the first call on the device). Returns a hipError_t.
+int noalloc_scratch(void** ptr);
 
 struct FwdParams {
   const void* q;

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define ATTN_ABI_VERSION 5
+#define ATTN_ABI_VERSION 6
 
 typedef enum {
   ATTN_OK = 0,
@@ -199,6 +199,37 @@ attn_status_t attn_fwd_splitkv(const attn_tensor_t* q, const attn_tensor_t* k,
                                int causal, float scale, int32_t num_splits, void* workspace,
                                int64_t workspace_bytes, const attn_tensor_t* o,
                                const attn_tensor_t* lse, void* stream);
+
+/*
+ * attn_fwd_splitkv_noalloc - attn_fwd_splitkv for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).
+ *
+ * Same arguments, function, checks and results as attn_fwd_splitkv, without
+ * the workspace: the split partials go to a file-scope device array of
+ * ATTN_NOALLOC_SCRATCH_BYTES bytes inside the library. This call allocates
+ * nothing (no hipMalloc, hipFree or allocating library routine); on its
+ * first call on a device (the calling thread's current device, which must
+ * hold the tensors and own `stream`) it looks up that device's copy of the
+ * array once. Each device keeps its copy until the process ends.
+ *
+ *   - A split count whose partials need more than ATTN_NOALLOC_SCRATCH_BYTES
+ *     (num_splits * B * H * Nq * (d + 1) * 4 for the splits used) returns
+ *     ATTN_ERR_UNSUPPORTED before anything is enqueued.
+ *   - Every call on one device shares that device's array, and nothing in
+ *     it has to start at zero (each call writes every partial it reads).
+ *     Calls whose kernels can overlap on one device - on different streams,
+ *     or from several host threads - race on it: serialise them (one
+ *     stream), or use attn_fwd_splitkv with distinct workspaces.
+ *   - With one split the call is exactly attn_fwd and the array is not used.
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES (8 * 1024 * 1024)
+
+attn_status_t attn_fwd_splitkv_noalloc(const attn_tensor_t* q, const attn_tensor_t* k,
+                                       const attn_tensor_t* v, const attn_mask_t* bias_or_mask,
+                                       int causal, float scale, int32_t num_splits,
+                                       const attn_tensor_t* o, const attn_tensor_t* lse,
+                                       void* stream);
 
 /*
  * attn_fwd_varlen - the forward over packed variable-length sequences.

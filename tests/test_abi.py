@@ -34,7 +34,7 @@ def test_exports_every_declared_function():
     lib = _lib()
     names = _declared_functions()
     assert names == ["attn_abi_version", "attn_bwd", "attn_bwd_workspace_size", "attn_fwd",
-                     "attn_fwd_splitkv",
+                     "attn_fwd_splitkv", "attn_fwd_splitkv_noalloc",
                      "attn_fwd_splitkv_num_splits", "attn_fwd_splitkv_workspace_size",
                      "attn_fwd_varlen", "attn_last_error"]
     for n in names:
@@ -396,3 +396,32 @@ def test_bwd_empty_query_side():
         ea.ATTN_ERR_UNSUPPORTED
     assert _bwd_empty_call((2, 4, 0, 64), (2, 2, 0, 64)) == ea.ATTN_OK
     assert _bwd_empty_call((0, 4, 10, 64), (0, 2, 300, 64)) == ea.ATTN_OK
+
+
+def _noalloc_call(shape_q, Nk, num_splits, dtype=ea.ATTN_BF16):
+    B, H, Nq, d = shape_q
+    q = _desc(shape_q, dtype)
+    k = _desc((B, H, Nk, d), dtype, data=0x20000)
+    v = _desc((B, H, Nk, d), dtype, data=0x30000)
+    o = _desc(shape_q, dtype, data=0x40000)
+    lse = _desc((B, H, Nq, 1), ea.ATTN_F32, data=0x50000, stride=[H * Nq, Nq, 1, 1])
+    lib = _lib()
+    return lib.attn_fwd_splitkv_noalloc(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), None,
+                                        0, 0.125, num_splits, ctypes.byref(o), ctypes.byref(lse),
+                                        None)
+
+
+def test_noalloc_rejections():
+    # refused on the host before the scratch array is looked up or anything
+    # is enqueued: partials beyond the scratch size, f32, bad split counts;
+    # an empty problem is a no-op
+    assert ea.NOALLOC_SCRATCH_BYTES == int(re.search(
+        r"#define ATTN_NOALLOC_SCRATCH_BYTES \((\d+) \* 1024 \* 1024\)",
+        open(HEADER).read()).group(1)) << 20
+    # 2 splits x 8 x 32 x 64 rows x 129 x 4 bytes = 16.9 MB > 8 MiB
+    assert _noalloc_call((8, 32, 64, 128), 4096, 2) == ea.ATTN_ERR_UNSUPPORTED
+    assert "scratch" in ea.last_error()
+    assert _noalloc_call((1, 2, 1, 128), 4096, 4, dtype=ea.ATTN_F32) == ea.ATTN_ERR_UNSUPPORTED
+    assert _noalloc_call((1, 2, 1, 128), 4096, 0) == ea.ATTN_ERR_INVALID
+    assert _noalloc_call((1, 2, 1, 128), 4096, 1025) == ea.ATTN_ERR_INVALID
+    assert _noalloc_call((0, 2, 1, 128), 4096, 4) == ea.ATTN_OK
