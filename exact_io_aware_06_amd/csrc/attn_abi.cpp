@@ -8,7 +8,7 @@
 // "flash-attention" (stanleyjacob.dev), Part IV, stage 3, except that here the
 // caller allocates the outputs.
 
-#include "../../include/attn.h"
+#include "attn.h"
 
 #include <algorithm>
 #include <cmath>

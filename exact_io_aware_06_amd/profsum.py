@@ -1,7 +1,7 @@
 """Turn rocprofv3 CSV output into the short text summaries kept under profiles/.
 
     python -m exact_io_aware_06_amd.profsum stats  <kernel_stats.csv> <out.txt> <command...>
-    python -m exact_io_aware_06_amd.profsum counters [--kernel SUBSTR] <workload> <out.txt> <pmc_dir>... -- <command...>
+    python -m exact_io_aware_06_amd.profsum counters [--kernel SUBSTR] [--last N] <workload> <out.txt> <pmc_dir>... -- <command...>
     python -m exact_io_aware_06_amd.profsum traffic <workload> <fetch_dir> <write_dir> \
         <copy_fetch_dir> <copy_write_dir> <copy_mib> <kernel_src[,src...]> <out.txt> <command...>
 
@@ -49,40 +49,85 @@ def stats(src, out, cmd):
                     f"{float(r['Percentage']):.2f}\n")
 
 
-def counters(workload, out, dirs, cmd, kernel="fwd_bf16"):
+def _durations_ns(d, kernel):
+    """Per-dispatch kernel durations (ns) from the kernel trace written next
+    to the counters (rocprofv3 --pmc ... --kernel-trace), keyed by dispatch."""
+    path = os.path.join(d, "kernel_trace.csv")
+    if not os.path.exists(path):
+        return {}
+    out = {}
+    for r in csv.DictReader(open(path)):
+        if kernel in r["Kernel_Name"]:
+            out[int(r["Dispatch_Id"])] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+    return out
+
+
+def counters(workload, out, dirs, cmd, kernel="fwd_bf16", last=0):
+    """Mean of each counter over the dispatches of `kernel` (the last `last`
+    of them when last > 0: the calls after the clocks have settled)."""
     acc = {}
+    durs = []
+    full_name = ""
     for d in dirs:
         path = os.path.join(d, "pmc_counter_collection.csv")
         per = {}
         for r in csv.DictReader(open(path)):
             if kernel not in r["Kernel_Name"]:
                 continue
+            full_name = r["Kernel_Name"]
             key = (r["Counter_Name"], int(r["Dispatch_Id"]))
             per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+        disp = sorted({k[1] for k in per})
+        if last > 0:
+            disp = disp[-last:]
+        keep = set(disp)
         names = {}
-        for (n, _), v in per.items():
-            names.setdefault(n, []).append(v)
+        for (n, di), v in per.items():
+            if di in keep:
+                names.setdefault(n, []).append(v)
         for n, vs in names.items():
             acc.setdefault(n, []).append(sum(vs) / len(vs))
+        dd = _durations_ns(d, kernel)
+        durs += [dd[x] for x in disp if x in dd]
     c = {n: sum(v) / len(v) for n, v in acc.items()}
     if not acc:
         raise SystemExit(f"no counter rows for kernels matching {kernel!r}")
+    which = f"the last {last} dispatches of each run" if last > 0 else "every dispatch"
     lines = [f"# rocprofv3 --pmc counters of the kernels matching {kernel!r}, workload {workload}",
+             f"# averaged over {which}",
              f"# command (one run per counter group): {cmd}",
              "counter | mean per dispatch"]
     lines += [f"{n} | {c[n]:.1f}" for n in sorted(c)]
-    if "SQ_INSTS_MFMA" in c and "GRBM_GUI_ACTIVE" in c:
-        mf = c["SQ_INSTS_MFMA"]
-        gui = c["GRBM_GUI_ACTIVE"] / 8.0
-        lines.append("# derived")
-        lines.append(f"mfma_busy_fraction_per_simd | {c['SQ_VALU_MFMA_BUSY_CYCLES'] / 1024 / gui:.3f}")
+    if durs:
+        dur = sum(durs) / len(durs)
+        lines.append(f"kernel_duration_us_under_pmc | {dur / 1e3:.1f}")
+        if "GRBM_GUI_ACTIVE" in c:
+            lines.append(f"gui_active_cycles_per_xcd_over_duration_GHz | {c['GRBM_GUI_ACTIVE'] / 8.0 / dur:.3f}")
+    lines.append("# derived")
+    gui = c.get("GRBM_GUI_ACTIVE", 0.0) / 8.0   # GUI-active cycles of one XCD
+    if gui > 0:
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+            lines.append(f"mfma_busy_fraction_per_simd | {c['SQ_VALU_MFMA_BUSY_CYCLES'] / 1024 / gui:.3f}")
+        for n in ("SQ_LDS_DATA_FIFO_FULL", "SQ_LDS_CMD_FIFO_FULL", "SQ_LDS_IDX_ACTIVE",
+                  "SQ_LDS_BANK_CONFLICT"):
+            if n in c:
+                lines.append(f"{n.lower()}_per_cu_over_gui | {c[n] / 256 / gui:.3f}")
+    if "SQ_VALU_MFMA_COEXEC_CYCLES" in c and "SQ_VALU_MFMA_BUSY_CYCLES" in c:
         lines.append(f"mfma_coexec_over_busy | {c['SQ_VALU_MFMA_COEXEC_CYCLES'] / c['SQ_VALU_MFMA_BUSY_CYCLES']:.3f}")
+    if "SQ_LDS_BANK_CONFLICT" in c and "SQ_LDS_IDX_ACTIVE" in c:
         lines.append(f"lds_bank_conflict_over_idx_active | {c['SQ_LDS_BANK_CONFLICT'] / max(c['SQ_LDS_IDX_ACTIVE'], 1):.4f}")
-        if "SQ_INSTS_VALU" in c and kernel.startswith("fwd_"):
-            wt = mf / 32.0   # 32 MFMA instructions per wave per 64-key tile at d=128
-            lines.append(f"valu_non_mfma_per_wave_tile | {(c['SQ_INSTS_VALU'] - mf) / wt:.1f}")
-            lines.append(f"lds_insts_per_wave_tile | {c['SQ_INSTS_LDS'] / wt:.1f}")
-            lines.append(f"transcendental_per_wave_tile | {c['SQ_INSTS_VALU_TRANS_F32'] / wt:.1f}")
+    mf = c.get("SQ_INSTS_MFMA", 0.0)
+    if mf > 0 and kernel.startswith("fwd_"):
+        # MFMAs per wave per 64-key tile: 32 at head dimension 128, 16 at 64
+        per_tile = 32 if "kernel<128," in full_name else 16 if "kernel<64," in full_name else None
+        if per_tile:
+            wt = mf / per_tile   # MFMA instructions per wave per 64-key tile
+            if "SQ_INSTS_VALU" in c:
+                lines.append(f"valu_non_mfma_per_wave_tile | {(c['SQ_INSTS_VALU'] - mf) / wt:.1f}")
+            if "SQ_INSTS_LDS" in c:
+                lines.append(f"lds_insts_per_wave_tile | {c['SQ_INSTS_LDS'] / wt:.1f}")
+            if "SQ_INSTS_VALU_TRANS_F32" in c:
+                lines.append(f"transcendental_per_wave_tile | {c['SQ_INSTS_VALU_TRANS_F32'] / wt:.1f}")
     open(out, "w").write("\n".join(lines) + "\n")
 
 
@@ -128,10 +173,15 @@ if __name__ == "__main__":
     elif mode == "counters":
         args = sys.argv[2:]
         kernel = "fwd_bf16"
-        if args[0] == "--kernel":
-            kernel, args = args[1], args[2:]
+        last = 0
+        while args[0] in ("--kernel", "--last"):
+            if args[0] == "--kernel":
+                kernel = args[1]
+            else:
+                last = int(args[1])
+            args = args[2:]
         cut = args.index("--")
-        counters(args[0], args[1], args[2:cut], " ".join(args[cut + 1:]), kernel)
+        counters(args[0], args[1], args[2:cut], " ".join(args[cut + 1:]), kernel, last)
     elif mode == "traffic":
         traffic(*sys.argv[2:10], " ".join(sys.argv[10:]))
     else:
