@@ -19,6 +19,7 @@ LIB = os.path.join(HERE, "libattn.so")
 
 SOURCES = ["attn_abi.cpp", "runtime.hip", "fwd_bf16.hip", "fwd_bf16_split.hip",
            "fwd_bf16_local.hip", "fwd_bf16_local_split.hip", "fwd_bf16_varlen.hip",
+           "fwd_bf16_stream.hip",
            "fwd_f32.hip", "combine.hip", "bwd_bf16.hip", "bwd_bf16_masked.hip",
            "scratch.hip"]
 

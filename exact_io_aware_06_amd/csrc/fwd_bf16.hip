@@ -30,6 +30,36 @@ int fwd_bf16_rows(int d, int64_t nrows, bool causal, bool bias, bool split) {
   return 256;
 }
 
+// Compute units of the current device (cached per device; 256 on MI355X).
+static int device_cus() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// The persistent form (fwd_bf16_stream.hip) applies to dense problems whose
+// key tiles are all full and come in pairs (Nk a multiple of 128), with
+// enough of them for its schedule (the next Q rows are copied during the
+// first tiles of the current query tile), rows that 32-bit copy offsets
+// reach, and at least two query tiles per compute unit to walk.
+static int stream_grid(const FwdParams& p, int d, int64_t total) {
+  if (p.n_split > 1 || p.cu_q != nullptr || p.local || p.causal || p.bias != nullptr ||
+      p.kv_len != nullptr)
+    return 0;
+  if (p.Nk % 128 != 0 || p.Nk / 64 < (d == 128 ? 14 : 8)) return 0;
+  if (64 * p.q_sn * 2 >= ((int64_t)1 << 31)) return 0;
+  const int cus = device_cus();
+  if (cus % 8 != 0 || total < 2 * (int64_t)cus) return 0;
+  return cus;   // one workgroup per compute unit, cus / 8 per XCD
+}
+
 int launch_fwd_bf16(const FwdParams& p_in, int d, void* stream) {
   FwdParams p = p_in;
   const bool split = p.n_split > 1;
@@ -79,6 +109,8 @@ int launch_fwd_bf16(const FwdParams& p_in, int d, void* stream) {
   p.bias_dma = (p.bias != nullptr && d == 64 && p.bias_vec && p.Nk >= 4 && p.Nk % 4 == 0 &&
                 !packed && 32 * p.bias_sn * 4 + 256 < ((int64_t)1 << 31)) ? 1 : 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (const int grid = stream_grid(p, d, total); grid > 0 && br == 256)
+    return (int)launch_bf16_stream(p, tm, d, grid, s);
   if (varlen) return (int)launch_bf16_varlen(p, tm, d, waves, s);
   if (p.local) return (int)launch_bf16_local(p, tm, d, waves, s);
   return split ? (int)launch_bf16_split(p, tm, d, waves, s) : (int)launch_bf16_plain(p, tm, d, waves, s);

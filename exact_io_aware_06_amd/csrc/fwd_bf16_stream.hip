@@ -1,0 +1,458 @@
+// bf16 forward, persistent ("stream") form for dense problems: no mask, no
+// bias, no key split, every key tile full (Nk a multiple of 128).
+//
+// Same arithmetic as fwd_bf16_kernel.h (transposed scores S^T = K Q^T with
+// v_mfma_f32_32x32x16_bf16, base-2 exponentials against an overflow-checked
+// reference, O^T += V^T P^T from LDS transpose reads; "Understanding
+// FlashAttention Pt 1", sections 2.3-2.4 and 3.1), with the query tiles of
+// a workgroup processed back to back as one stream of key tiles.
+//
+// Why: with one workgroup per query tile, every round of workgroups starts
+// with all compute units loading their Q rows and first key/value tiles at
+// once and ends with all of them writing O at once; measured on the
+// B=2 H=32 N=4096 d=128 workload, those two bursts took about 11k and 7k of
+// a workgroup's 209k cycles, in every round. Here one workgroup per compute
+// unit walks its query tiles in turn (the tiles of one XCD stay on it, as in
+// the per-tile launch) and the boundary between two tiles costs about one
+// ordinary iteration:
+//   * the next tile's Q rows are copied into LDS by LDS DMA, one 1 KB copy
+//     per wavefront per iteration, early in the current tile;
+//   * the key/value stream runs across the boundary: the last iteration of
+//     a tile already copies the next tile's first key/value tiles and
+//     computes the next tile's first S^T (with the next Q, read from LDS);
+//   * the finished tile's O is normalised and written to LDS (each
+//     wavefront into its own 32 rows, where its Q rows were), then copied
+//     out in whole 16-byte row pieces during the next tile's first
+//     iterations, two copies per wavefront per iteration, so full 256-byte
+//     rows leave each instruction and the writes are spread over time.
+// Rows of Q/O in LDS: row r at r * 2d bytes, 16-byte chunk c at slot
+// c ^ (r mod d/8), so that the 16 lanes of a transposing read or of a row
+// copy hit 16 different bank groups.
+
+#include "fwd_bf16_kernel.h"
+
+namespace attn {
+namespace {
+
+template <int D>
+__global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, TileMap tm) {
+  constexpr int W = 8;
+  using G = Geo<D, W>;
+  constexpr int kBr = G::kBr;                   // 256 query rows per tile
+  constexpr int kC = D / 8;                     // 16-byte chunks per row
+  constexpr int kRowBytes = 2 * D;
+  constexpr int kQWave = 32 * kRowBytes;        // a wavefront's Q / O rows in LDS
+  constexpr int kQCopies = kQWave / 1024;       // 1 KB copies for them (D / 16)
+  constexpr int kRowsPerKB = 1024 / kRowBytes;  // rows per 1 KB (4 or 8)
+  constexpr int kDrainIters = (kQCopies + 1) / 2;  // O copied out, 2 per iteration
+  constexpr int kQ0 = kDrainIters;              // first iteration copying the next Q
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+
+  // Tiles of this workgroup: the logical tiles slot, slot + wpx, ... of its
+  // XCD's range (workgroup w runs on XCD w % 8).
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, wpx = gridDim.x >> 3;
+  const int base_logical = xcd * tm.per_xcd + slot;
+  const int n_items = max(0, min((tm.per_xcd - slot + wpx - 1) / wpx,
+                                 (tm.total - base_logical + wpx - 1) / wpx));
+  if (n_items == 0) return;
+
+  const int Nq = p.Nq, Nk = p.Nk, nt = Nk / kBc;
+  const int64_t ksn = p.k_sn * 2, vsn = p.v_sn * 2;  // row strides in bytes
+  struct Item {
+    const uint8_t* q;   // row q0 + 32 * wave (clamped to the last row) of Q
+    const uint8_t* k;   // key 0 of K
+    const uint8_t* v;   // key 0 of V
+    __bf16* o;          // row 0 of O
+    float* lse;         // row 0 of LSE
+    int q0;             // first query row of the tile
+  };
+  auto item = [&](int it) {
+    const int logical = base_logical + it * wpx;
+    const int qt = logical % tm.n_qtiles;
+    const int hb = logical / tm.n_qtiles;
+    const int h = hb % p.H, b = hb / p.H;
+    const int hk = h / p.head_group;
+    Item r;
+    r.q0 = qt * kBr;
+    const int wrow = min(r.q0 + 32 * wave, Nq - 1);
+    r.q = uniform_ptr(reinterpret_cast<const uint8_t*>(static_cast<const __bf16*>(p.q) + b * p.q_sb +
+                                                       h * p.q_sh + (int64_t)wrow * p.q_sn));
+    r.k = uniform_ptr(reinterpret_cast<const uint8_t*>(static_cast<const __bf16*>(p.k) + b * p.k_sb +
+                                                       hk * p.k_sh));
+    r.v = uniform_ptr(reinterpret_cast<const uint8_t*>(static_cast<const __bf16*>(p.v) + b * p.v_sb +
+                                                       hk * p.v_sh));
+    r.o = static_cast<__bf16*>(p.o) + b * p.o_sb + h * p.o_sh;
+    r.lse = p.lse + b * p.l_sb + h * p.l_sh;
+    return r;
+  };
+
+  uint8_t* const kbuf = smem;                    // K tile t in buffer t % 2
+  uint8_t* const vbuf = smem + 2 * G::kKBytes;   // V tile t in buffer t % 2
+  uint8_t* const qw = smem + G::kSmem + wave * kQWave;  // this wavefront's Q / O rows
+
+  // ---- LDS DMA lane offsets of a full K / V tile (every tile is full here)
+  uint32_t koff[G::kDmaPerWave], voff[G::kDmaPerWave];
+#pragma unroll
+  for (int i = 0; i < G::kDmaPerWave; ++i) {
+    koff[i] = (uint32_t)(k_dma_key<D, W>(wave, lane, i) * (int)ksn + k_dma_col<D, W>(wave, lane, i));
+    voff[i] = (uint32_t)(v_dma_key<D, W>(wave, lane, i) * (int)vsn + v_dma_col<D, W>(wave, lane, i));
+  }
+  auto dma_k = [&](const uint8_t* tile, uint8_t* dst, int i) {
+    dma16(tile, koff[i], dst + 1024 * (wave + W * i));
+  };
+  auto dma_v = [&](const uint8_t* tile, uint8_t* dst, int i) {
+    dma16(tile, voff[i], dst + 1024 * (wave + W * i));
+  };
+  auto wait_tiles = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+
+  // ---- Q rows of this wavefront into its LDS rows: copy i holds rows
+  // i * kRowsPerKB + lane / kC; the lane fetches chunk (lane % kC) ^ (row % kC)
+  // of that row (rows past the last query re-read the last one).
+  auto q_copy = [&](const Item& it, int i) {
+    const int ln = fresh(lane);
+    const int r = i * kRowsPerKB + ln / kC;
+    const int wrow0 = it.q0 + 32 * wave;
+    const int rel = max(min(wrow0 + r, Nq - 1) - min(wrow0, Nq - 1), 0);
+    const int chunk = (ln % kC) ^ (r % kC);
+    dma16(it.q, (uint32_t)(rel * (int)(p.q_sn * 2) + 16 * chunk), qw + 1024 * i);
+  };
+  // Q as the MFMA B operand: lane holds row l32, elements [16kk + 8hi, +8)
+  bf16x8 qf[G::kNkk];
+  // (addresses recomputed at each use: kept across the loop they would take
+  // registers the loop needs)
+  auto q_from_lds = [&]() {
+    const int ln = fresh(lane);
+    const uint8_t* const row = qw + (ln & 31) * kRowBytes;
+    const int sw = (ln & 31) % kC, h = ln >> 5;
+#pragma unroll
+    for (int kk = 0; kk < G::kNkk; ++kk)
+      qf[kk] = *reinterpret_cast<const bf16x8*>(row + 16 * ((2 * kk + h) ^ sw));
+  };
+
+  // ---- MFMA operand addressing (as in the per-tile kernel)
+  const uint8_t* const klane = kbuf + (l32 >> 4) * G::kKBlock + hi * 256 + (l32 & 15) * 16;
+  const int gi = l32 & 15;
+  const uint8_t* const vlane = vbuf + 2 * hi * G::kVBlock + 128 * (l32 >> 4) +
+                               64 * ((gi >> 1) & 1) + 16 * (gi >> 2) + 8 * (gi & 1);
+  constexpr int kNq = 2 * G::kNkk;
+  constexpr int kNv = 4 * G::kNcb;
+  auto kfrag = [&](const uint8_t* kb, int i) {
+    return *reinterpret_cast<const bf16x8*>(kb + (i & 1) * 2 * G::kKBlock + (i >> 1) * 512);
+  };
+  auto vfrag = [&](const uint8_t* vb, int i) {
+    const uint8_t* p0 = vb + 4 * (i / G::kNcb) * G::kVBlock + 256 * (i % G::kNcb);
+    return lds_read_tr_pair(p0, p0 + G::kVBlock);
+  };
+
+  f32x16 oacc[G::kNcb];
+  float m_run = -INFINITY;  // reference R of this lane's row (base 2)
+  float l_run = 0.f;
+  const float c2 = p.scale_log2;
+
+  auto tile_max = [&](const f32x16 (&s)[2]) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) m = fmaxf(m, s[bb][r]);
+    return lane_pair_max(m) * c2;
+  };
+  auto exp_slice = [&](const f32x16 (&s)[2], u32x4 (&pw)[2][2], float m_use, float& rs, int i) {
+    const int bb = i >> 3, r = 2 * (i & 7);
+    float x[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      x[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[bb][r + e], c2, -m_use));
+      rs += x[e];
+    }
+    const bf16x2 v = {(__bf16)x[0], (__bf16)x[1]};
+    uint32_t w = __builtin_bit_cast(uint32_t, v);
+    asm volatile("" : "+v"(w), "+v"(rs));
+    pw[bb][r >> 3][(r & 7) >> 1] = w;
+  };
+
+  // Software pipeline of one tile (see fwd_bf16_kernel.h): phase A = S_{j+1}
+  // on the matrix pipe beside the second half of tile j's exponentials and
+  // the tile copies; the overflow check; phase B = O += V_j P_j beside the
+  // first half of tile j+1's exponentials.
+  constexpr int kSlices = 16;
+  constexpr int kPre = kSlices / 2;
+  constexpr int kSlicesA = kSlices - kPre;
+  constexpr int kNdma = 2 * G::kDmaPerWave;
+  auto phase_a = [&](auto with_qk, const uint8_t* kb, const f32x16 (&sc)[2], f32x16 (&sn)[2],
+                     u32x4 (&pb)[2][2], float m_use, auto&& dma) {
+    float rs = 0.f;
+    __builtin_amdgcn_s_setprio(1);
+    if constexpr (decltype(with_qk)::value) {
+      sn[0] = f32x16{};
+      sn[1] = f32x16{};
+      bf16x8 kf[kPf];
+#pragma unroll
+      for (int i = 0; i < kPf; ++i) kf[i] = kfrag(kb, i);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < kNq; ++i) {
+        sn[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % kPf], qf[i >> 1], sn[i & 1], 0, 0, 0);
+        if (i + kPf < kNq) kf[i % kPf] = kfrag(kb, i + kPf);
+        dma(i);
+#pragma unroll
+        for (int k = (kSlicesA * i) / kNq; k < (kSlicesA * (i + 1)) / kNq; ++k)
+          exp_slice(sc, pb, m_use, rs, kPre + k);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+#pragma unroll
+      for (int k = kPre; k < kSlices; ++k) exp_slice(sc, pb, m_use, rs, k);
+    }
+    return rs;
+  };
+  auto phase_b = [&](auto with_next, const uint8_t* vb, u32x4 (&pb)[2][2], const f32x16 (&sn)[2],
+                     float m_use, float& rs_next) {
+    __builtin_amdgcn_s_setprio(0);
+    bf16x8 vf[kPf];
+#pragma unroll
+    for (int i = 0; i < kPf; ++i) vf[i] = vfrag(vb, i);
+    __builtin_amdgcn_sched_barrier(0);
+    constexpr int kPer = kSlices / kNv;
+    constexpr int kB0 = kNv - kPre / kPer;
+    static_assert(kPre % kPer == 0 && kPre <= 12, "slices must follow the MFMAs that read their P");
+#pragma unroll
+    for (int i = 0; i < kNv; ++i) {
+      const int u = i / G::kNcb;
+      oacc[i % G::kNcb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          vf[i % kPf], __builtin_bit_cast(bf16x8, pb[u >> 1][u & 1]), oacc[i % G::kNcb], 0, 0, 0);
+      if (i + kPf < kNv) vf[i % kPf] = vfrag(vb, i + kPf);
+      if constexpr (decltype(with_next)::value) {
+        if (i == kB0) __builtin_amdgcn_s_setprio(1);
+        if (i >= kB0) {
+#pragma unroll
+          for (int k = kPer * (i - kB0); k < kPer * (i + 1 - kB0); ++k)
+            exp_slice(sn, pb, m_use, rs_next, k);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto qk_plain = [&](const uint8_t* kb, f32x16 (&s)[2]) {
+    s[0] = f32x16{};
+    s[1] = f32x16{};
+    bf16x8 kf[kPf];
+#pragma unroll
+    for (int i = 0; i < kPf; ++i) kf[i] = kfrag(kb, i);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < kNq; ++i) {
+      s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % kPf], qf[i >> 1], s[i & 1], 0, 0, 0);
+      if (i + kPf < kNq) kf[i % kPf] = kfrag(kb, i + kPf);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  u32x4 pb[2][2];
+  float rs_half = 0.f;
+
+  // Two kinds of iteration: ordinary (tile j+1 of the same query tile
+  // follows) and the last of a query tile (its phase A computes the first
+  // S^T of the tile `nxt`, with nxt's Q read from LDS, and its phase B
+  // computes no exponentials ahead). The workgroup's very last query tile
+  // ends the same way with nxt = itself (sixteen MFMAs and two tile copies
+  // for nothing, once per workgroup: one code path fewer to fit in 256
+  // registers).
+  using Yes = std::integral_constant<bool, true>;
+  using No = std::integral_constant<bool, false>;
+  auto iteration = [&](auto last, int j, const Item& cur, const Item& prv, const Item& nxt,
+                       bool has_next, bool has_prev, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+    constexpr bool kLast = decltype(last)::value;
+    const int par = j & 1;
+    if constexpr (!kLast) {
+      // the previous query tile's O, from this wavefront's LDS rows to HBM
+      // (two 1 KB row copies per iteration), then the next tile's Q rows
+      // into the same LDS rows (one copy per iteration)
+      if (has_prev && j < kDrainIters) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const int i = 2 * j + c;
+          if (i < kQCopies) {
+            const int ln = fresh(lane);
+            const int r = i * kRowsPerKB + ln / kC;
+            const u32x4 x = *reinterpret_cast<const u32x4*>(qw + 1024 * i + 16 * ln);
+            const int row = prv.q0 + 32 * wave + r;
+            if (row < Nq) {
+              const int chunk = (ln % kC) ^ (r % kC);
+              *reinterpret_cast<u32x4*>(reinterpret_cast<uint8_t*>(prv.o + (int64_t)row * p.o_sn) +
+                                        16 * chunk) = x;
+            }
+          }
+        }
+      }
+      if (has_next && j >= kQ0 && j < kQ0 + kQCopies) q_copy(nxt, j - kQ0);
+    } else {
+      q_from_lds();   // nxt's Q (copied during this tile; own rows of Q)
+    }
+    // K_{j+2} and V_{j+1} of the stream into the buffers of K_j and V_{j-1};
+    // past this query tile's keys they are nxt's first ones
+    auto ktile = [&](int t) { return t < nt ? cur.k + t * kBc * ksn : nxt.k + (t - nt) * kBc * ksn; };
+    auto vtile = [&](int t) { return t < nt ? cur.v + t * kBc * vsn : nxt.v + (t - nt) * kBc * vsn; };
+    const uint8_t* const kt = uniform_ptr(ktile(j + 2));
+    const uint8_t* const vt = uniform_ptr(vtile(j + 1));
+    uint8_t* const kd = kbuf + par * G::kKBytes;
+    uint8_t* const vd = vbuf + (par ^ 1) * G::kVBytes;
+    auto dma = [&](int s) {
+#pragma unroll
+      for (int n = 0; n < kNdma; ++n) {
+        if ((n * kNq) / kNdma != s) continue;
+        if (n < G::kDmaPerWave) dma_k(kt, kd, n);
+        else dma_v(vt, vd, n - G::kDmaPerWave);
+      }
+    };
+    float rs = rs_half + phase_a(Yes{}, klane + (par ^ 1) * G::kKBytes, sc, sn, pb,
+                                 m_run == -INFINITY ? 0.f : m_run, dma);
+    if (__builtin_amdgcn_ballot_w64(!(rs <= kBig) || m_run == -INFINITY) != 0) {
+      // rare: move the reference to the tile maximum and redo the tile
+      const float r_new = fmaxf(m_run, tile_max(sc));
+      const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - r_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int cb = 0; cb < G::kNcb; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[cb][r] *= alpha;
+      m_run = r_new;
+      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+      rs = 0.f;
+#pragma unroll
+      for (int k = 0; k < kSlices; ++k) exp_slice(sc, pb, m_use, rs, k);
+    }
+    l_run += rs;
+    rs_half = 0.f;
+    using Next = std::integral_constant<bool, !kLast>;
+    phase_b(Next{}, vlane + par * G::kVBytes, pb, sn, m_run == -INFINITY ? 0.f : m_run, rs_half);
+    wait_tiles();
+    __syncthreads();
+  };
+
+  // This wavefront's rows of the finished tile: O / l as bf16 into its LDS
+  // rows, LSE straight to HBM.
+  auto stage_o = [&](const Item& it) {
+    const float l_tot = lane_pair_sum(l_run);
+    const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+    const int ln = fresh(lane);
+    uint8_t* const row = qw + (ln & 31) * kRowBytes + 8 * (ln >> 5);
+    const int sw = (ln & 31) % kC;
+#pragma unroll
+    for (int cb = 0; cb < G::kNcb; ++cb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = (__bf16)(oacc[cb][4 * g + e] * inv);
+        *reinterpret_cast<bf16x4*>(row + 16 * ((4 * cb + g) ^ sw)) = w;
+      }
+    const int my_q = it.q0 + 32 * wave + (ln & 31);
+    if ((ln >> 5) == 0 && my_q < Nq)
+      it.lse[my_q] = (l_tot > 0.f) ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
+  };
+  // the new query tile's first score tile: its reference and the
+  // exponentials computed ahead of iteration 0
+  auto start_tile = [&](const f32x16 (&s)[2]) {
+#pragma unroll
+    for (int cb = 0; cb < G::kNcb; ++cb) oacc[cb] = f32x16{};
+    l_run = 0.f;
+    m_run = tile_max(s);
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
+    rs_half = 0.f;
+#pragma unroll
+    for (int k = 0; k < kPre; ++k) exp_slice(s, pb, m_use, rs_half, k);
+  };
+
+  f32x16 sa[2], sb[2];
+
+  // ---- prologue of the first query tile
+  {
+    const Item c0 = item(0);
+#pragma unroll
+    for (int i = 0; i < kQCopies; ++i) q_copy(c0, i);
+    const uint8_t* k0 = c0.k;
+    const uint8_t* v0 = c0.v;
+#pragma unroll
+    for (int i = 0; i < G::kDmaPerWave; ++i) dma_k(k0, kbuf, i);
+#pragma unroll
+    for (int i = 0; i < G::kDmaPerWave; ++i) dma_v(v0, vbuf, i);
+    const uint8_t* k1 = uniform_ptr(c0.k + kBc * ksn);
+#pragma unroll
+    for (int i = 0; i < G::kDmaPerWave; ++i) dma_k(k1, kbuf + G::kKBytes, i);
+    wait_tiles();
+    __syncthreads();
+    q_from_lds();
+    qk_plain(klane, sa);
+    // iteration 0 overwrites K buffer 0: every wavefront must be done with K_0
+    __syncthreads();
+    start_tile(sa);
+  }
+
+  for (int it = 0; it < n_items; ++it) {
+    const bool has_next = it + 1 < n_items;
+    const bool has_prev = it > 0;
+    const Item cur = item(it);
+    const Item prv = has_prev ? item(it - 1) : cur;
+    const Item nxt = has_next ? item(it + 1) : cur;
+    for (int j = 0; j + 2 < nt; j += 2) {
+      iteration(No{}, j, cur, prv, nxt, has_next, has_prev, sa, sb);
+      iteration(No{}, j + 1, cur, prv, nxt, has_next, has_prev, sb, sa);
+    }
+    iteration(No{}, nt - 2, cur, prv, nxt, has_next, has_prev, sa, sb);
+    // without a next query tile, nxt is this one: its Q rows are still in
+    // LDS (nothing was copied over them) and its first S^T is computed again
+    iteration(Yes{}, nt - 1, cur, prv, nxt, has_next, has_prev, sb, sa);
+    // sa holds nxt's first S^T
+    stage_o(cur);
+    if (has_next) {
+      start_tile(sa);
+    } else {
+      // no tile follows: copy O out at once (this wavefront's rows only)
+#pragma unroll
+      for (int i = 0; i < kQCopies; ++i) {
+        const int ln = fresh(lane);
+        const int r = i * kRowsPerKB + ln / kC;
+        const u32x4 x = *reinterpret_cast<const u32x4*>(qw + 1024 * i + 16 * ln);
+        const int row = cur.q0 + 32 * wave + r;
+        if (row < Nq) {
+          const int chunk = (ln % kC) ^ (r % kC);
+          *reinterpret_cast<u32x4*>(reinterpret_cast<uint8_t*>(cur.o + (int64_t)row * p.o_sn) +
+                                    16 * chunk) = x;
+        }
+      }
+    }
+  }
+}
+
+template <int D>
+hipError_t launch_stream_d(const FwdParams& p, const TileMap& tm, int grid, hipStream_t stream) {
+  using G = Geo<D, 8>;
+  constexpr int kSmemAll = G::kSmem + 8 * 32 * 2 * D;  // K/V double buffers + Q/O rows
+  static bool attr_set = false;  // benign race: every caller sets the same value
+  auto kern = fwd_bf16_stream_kernel<D>;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kSmemAll);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(512), kSmemAll, stream, p, tm);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bf16_stream(const FwdParams& p, const TileMap& tm, int d, int grid, hipStream_t s) {
+  if (d == 128) return launch_stream_d<128>(p, tm, grid, s);
+  if (d == 64) return launch_stream_d<64>(p, tm, grid, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace attn

@@ -1,0 +1,102 @@
+"""Parity of the persistent ("stream") forward with the fp64 oracle.
+
+Dense bf16 problems (no mask, no bias, no key lengths) whose key count is a
+multiple of 128 and which have at least two 256-row query tiles per compute
+unit run on one workgroup per compute unit that walks its query tiles back
+to back: the next tile's Q rows are copied into LDS during the current tile,
+the key/value stream runs across the boundary and the finished O leaves
+through LDS during the next tile. The cases below all take that path (the
+launcher picks it for these shapes) with several tiles per workgroup, an
+uneven number of tiles per workgroup, ragged last query tiles, unequal query
+and key counts, grouped key/value heads and strided views. Outputs start as
+NaN; one row of every 128-row query tile and every row of the first and last
+head are compared with the oracle at the parity bars. [Understanding
+FlashAttention Pt 1, sections 2.4 and 3.1; FlashAttention: Mathematical
+Foundations..., section 5.]
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+import exact_io_aware_06_amd as ea
+
+from tests.test_gpu_parity import (_banner, assert_all_written, compare_rows, head_rows,
+                                   nan_outputs, tile_rows)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("these tests need a GPU")
+    ea.load_library()
+    yield
+
+
+CASES = [
+    # (B, H, Hk, Nq, Nk, d): tiles per head x heads >= 2 x 256
+    (2, 96, 96, 1000, 1024, 128),    # 768 tiles: 3 per workgroup, ragged last tile
+    (3, 68, 17, 700, 512, 64),       # grouped heads (4 per K/V head), 612 tiles
+    (2, 101, 101, 1024, 896, 128),   # 808 tiles: 3 or 4 per workgroup, Nk = 14 tiles
+    (1, 128, 128, 1300, 2048, 64),   # Nq > multiple of 256, long keys
+]
+
+
+@pytest.mark.parametrize("B,H,Hk,Nq,Nk,d", CASES)
+def test_stream_matches_oracle(B, H, Hk, Nq, Nk, d):
+    _banner(f"stream B={B} H={H} Hk={Hk} Nq={Nq} Nk={Nk} d={d}")
+    w = workloads.Workload("stream", B, H, Nq, Nk, d, seed=B * H + Nq + Nk + d, Hk=Hk)
+    inp = workloads.make_inputs(w)
+    o, lse = nan_outputs(B, H, Nq, d, "bf16")
+    ea.attn_fwd(inp["q"].cuda(), inp["k"].cuda(), inp["v"].cuda(), scale=inp["scale"],
+                out=o, lse=lse)
+    torch.cuda.synchronize()
+    o_c, lse_c = o.cpu(), lse.cpu()
+    assert_all_written(o_c, lse_c, "stream")
+    rep = H // Hk
+    f = lambda t: t.double().numpy()
+    qd, kd, vd = f(inp["q"]), f(inp["k"]), f(inp["v"])
+
+    def oracle_rows(part):
+        out_o, out_l = [], []
+        for b, h, i in part:
+            oo, ll = oracle.attention_rows(qd[b:b + 1, h:h + 1], kd[b:b + 1, h // rep:h // rep + 1],
+                                           vd[b:b + 1, h // rep:h // rep + 1], [(0, 0, i)],
+                                           scale=inp["scale"])
+            out_o.append(oo[0])
+            out_l.append(ll[0])
+        return np.stack(out_o), np.array(out_l)
+
+    rows = tile_rows(B, H, Nq, w.seed) + head_rows(0, 0, Nq) + head_rows(B - 1, H - 1, Nq)
+    compare_rows(o_c, lse_c, rows, oracle_rows, "bf16", f"stream d={d} Nq={Nq} Nk={Nk}")
+
+
+def test_stream_strided_views_and_determinism():
+    # [B, N, H, d] storage seen as [B, H, N, d] for q, k, v and the output;
+    # two calls are bitwise equal
+    g = torch.Generator().manual_seed(71)
+    B, H, N, d = 2, 128, 1024, 128
+    base = torch.randn(3, B, N, H, d, generator=g).to(torch.bfloat16).cuda()
+    q, k, v = (base[i].transpose(1, 2) for i in range(3))
+    out_store = torch.full((B, N, H, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    out = out_store.transpose(1, 2)
+    lse = torch.full((B, H, N), float("nan"), dtype=torch.float32, device="cuda")
+    ea.attn_fwd(q, k, v, out=out, lse=lse)
+    o2, l2 = ea.attn_fwd(q, k, v)
+    torch.cuda.synchronize()
+    assert torch.equal(out, o2) and torch.equal(lse, l2)
+    o_c, lse_c = out.cpu(), lse.cpu()
+    assert_all_written(o_c, lse_c, "stream strided")
+    qd, kd, vd = (t.double().cpu().numpy() for t in (q, k, v))
+
+    def oracle_rows(part):
+        return oracle.attention_rows(qd, kd, vd, part, scale=d ** -0.5)
+
+    rows = tile_rows(B, H, N, 72) + head_rows(1, 77, N)
+    compare_rows(o_c, lse_c, rows, oracle_rows, "bf16", "stream strided")
