@@ -31,7 +31,8 @@ PEAK_F32_TFLOPS = 157.3     # MI355X dense fp32 matrix
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 # the sources a kernel's HBM traffic depends on (kernel body and its launch)
 KERNEL_SRC = {"bf16": ["exact_io_aware_06_amd/csrc/fwd_bf16_kernel.h",
-                       "exact_io_aware_06_amd/csrc/fwd_bf16.hip"],
+                       "exact_io_aware_06_amd/csrc/fwd_bf16.hip",
+                       "exact_io_aware_06_amd/csrc/fwd_bf16_stream.hip"],
               "f32": ["exact_io_aware_06_amd/csrc/fwd_f32.hip"]}
 
 

@@ -394,6 +394,24 @@ __global__ __launch_bounds__(64 * W, 2) void fwd_bf16_kernel(FwdParams p, TileMa
   if (CAUSAL) wg_keys = min(kend, qend + off);
   wg_keys = max(wg_keys, 0);
   const int nt = (wg_keys + kBc - 1) / kBc;
+  // Window without a key split: the key tiles are visited in a rotated
+  // order, step j taking the tile whose absolute index (counted from key 0)
+  // is congruent to j modulo nt, wrapping at the end of the range. Every
+  // workgroup with a whole window covers the same number of tiles, so the
+  // query tiles of one head that run side by side on an XCD read each key
+  // tile at the same step and all but the first copy come from L2 (in
+  // ascending order the band of 32 neighbouring query tiles spans more than
+  // an XCD's L2 between the first and the last read of a tile). Not done
+  // when a tile runs past the last key: such a tile's copy offsets are
+  // clamped in place and must not be followed by whole tiles.
+  int rot = 0;
+  if constexpr (LOCAL && !SPLIT) {
+    if (nt > 0 && nt * kBc <= Nk) rot = (nt - (kbeg / kBc) % nt) % nt;
+  }
+  auto ktile = [&](int j) {
+    const int x = j + rot;
+    return x >= nt ? x - nt : x;
+  };
 
   // ---- Q as the B operand, resident for the whole loop: lane holds query
   // row_i, elements [16kk + 8hi, 16kk + 8hi + 8).
@@ -438,7 +456,7 @@ __global__ __launch_bounds__(64 * W, 2) void fwd_bf16_kernel(FwdParams p, TileMa
   // is the last tile of its kind ever loaded (later loads only fetch it
   // again), so its clamped offsets simply replace the fixed ones.
   auto prep_k = [&](int j) {
-    const int kv0 = j * kBc;
+    const int kv0 = ktile(j) * kBc;
     if (kv0 + kBc > Nk) {
 #pragma unroll
       for (int i = 0; i < G::kDmaPerWave; ++i)
@@ -448,7 +466,7 @@ __global__ __launch_bounds__(64 * W, 2) void fwd_bf16_kernel(FwdParams p, TileMa
     return kbase + kv0 * ksn;
   };
   auto prep_v = [&](int j) {
-    const int kv0 = j * kBc;
+    const int kv0 = ktile(j) * kBc;
     if (kv0 + kBc > Nk) {
 #pragma unroll
       for (int i = 0; i < G::kDmaPerWave; ++i)
@@ -552,7 +570,7 @@ __global__ __launch_bounds__(64 * W, 2) void fwd_bf16_kernel(FwdParams p, TileMa
   // the row's last four keys instead: finite, and masked)
   auto dma_bias = [&](int j) {
     if constexpr (kBiasLds) {
-      const int kv0 = j * kBc;
+      const int kv0 = ktile(j) * kBc;
       const uint8_t* t = uniform_ptr(bias_wave + 4 * kv0);
       if (kv0 + kBc <= Nk) {
 #pragma unroll
@@ -576,7 +594,7 @@ __global__ __launch_bounds__(64 * W, 2) void fwd_bf16_kernel(FwdParams p, TileMa
   // scale * qk + bias in natural units (one FMA); the exponent's FMA turns
   // them into base 2 (without one, the raw qk goes there with scale * log2 e).
   auto mask_bias = [&](int j, f32x16 (&s)[2]) {
-    const int kv0 = j * kBc;
+    const int kv0 = ktile(j) * kBc;
     if (HAS_BIAS) {
       f32x16 bia[2];
       const bool fullb = p.bias_vec && kv0 + kBc <= Nk;
@@ -830,7 +848,7 @@ __global__ __launch_bounds__(64 * W, 2) void fwd_bf16_kernel(FwdParams p, TileMa
     // for its other waves.
     static_assert(!CAUSAL || kPre == 0, "a skipped phase B would drop the next tile's slices");
     auto seen = [&](int t) {
-      const int kv0 = t * kBc;
+      const int kv0 = ktile(t) * kBc;
       return kv0 <= qmax_w + off && (!LOCAL || kv0 + kBc - 1 >= qmin_w + off_l);
     };
     float rs = rs_half + phase_a(has_next, klane + (cur ^ 1) * G::kKBytes, sc, sn, pb,

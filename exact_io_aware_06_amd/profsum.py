@@ -21,6 +21,7 @@ unchanged.
 import csv
 import hashlib
 import os
+import re
 import sys
 
 
@@ -52,8 +53,9 @@ def stats(src, out, cmd):
 def _durations_ns(d, kernel):
     """Per-dispatch kernel durations (ns) from the kernel trace written next
     to the counters (rocprofv3 --pmc ... --kernel-trace), keyed by dispatch."""
-    path = os.path.join(d, "kernel_trace.csv")
-    if not os.path.exists(path):
+    path = next((os.path.join(d, n) for n in ("kernel_trace.csv", "pmc_kernel_trace.csv")
+                 if os.path.exists(os.path.join(d, n))), None)
+    if path is None:
         return {}
     out = {}
     for r in csv.DictReader(open(path)):
@@ -119,7 +121,8 @@ def counters(workload, out, dirs, cmd, kernel="fwd_bf16", last=0):
     mf = c.get("SQ_INSTS_MFMA", 0.0)
     if mf > 0 and kernel.startswith("fwd_"):
         # MFMAs per wave per 64-key tile: 32 at head dimension 128, 16 at 64
-        per_tile = 32 if "kernel<128," in full_name else 16 if "kernel<64," in full_name else None
+        dm = re.search(r"kernel<(\d+)[,>]", full_name)
+        per_tile = {128: 32, 64: 16}.get(int(dm.group(1))) if dm else None
         if per_tile:
             wt = mf / per_tile   # MFMA instructions per wave per 64-key tile
             if "SQ_INSTS_VALU" in c:
