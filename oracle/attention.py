@@ -294,37 +294,53 @@ def online_softmax_scalar(scores, values):
 
 
 def online_softmax_blocked(scores, values, block):
-    """Blockwise merge recurrence for one query row.
+    """The blockwise merge recurrence over the keys, for one query row or a
+    block of query rows.
 
-    State (m, l, a). For a block of scores s with values V_b:
-        m_b = max(s), m' = max(m, m_b), alpha = exp(m - m'), p = exp(s - m')
-        l' = alpha l + sum(p),  a' = alpha a + p^T V_b
-    and finally o = a / l [Understanding FlashAttention Pt 1, §2.4 "The
-    Blockwise Merge Recurrence"; FlashAttention: Mathematical Foundations...,
-    §2]. A block whose scores are all -inf leaves the state unchanged.
-    Returns (o, lse, m, l).
+    scores: [n] (one row) or [r, n] (r rows sharing the values; masked
+    positions are -inf and contribute zero probability); values: [n, dv].
+    The state of each row is (m, l, a): the largest score so far, the sum of
+    exp(score - m) so far and the unnormalised value accumulator. Each block
+    of `block` consecutive keys, with scores s and values V_b, applies
+        m_b = max(s),  m' = max(m, m_b),  alpha = exp(m - m'),  p = exp(s - m'),
+        l' = alpha l + sum(p),  a' = alpha a + p^T V_b,  (m, l, a) <- (m', l', a')
+    row by row, and at the end o = a / l [Understanding FlashAttention Pt 1,
+    §2.4 "The Blockwise Merge Recurrence", including its closing remarks on
+    blocks of query rows (m and l row vectors, a a matrix) and on masks
+    applied before the exponentials]. A row whose maximum is still -inf after
+    a block (nothing visible yet) keeps its empty state. Returns
+    (o, lse, m, l); o = 0 and lse = -inf for a row that saw no key.
     """
-    scores = _f64(scores).ravel()
-    values = _f64(values).reshape(len(scores), -1)
-    block = int(block)
-    if block < 1:
+    sc = _f64(scores)
+    one_row = sc.ndim == 1
+    sc = sc.reshape(1, -1) if one_row else sc.reshape(-1, sc.shape[-1])
+    n_rows, n = sc.shape
+    vals = _f64(values).reshape(n, -1)
+    width = int(block)
+    if width < 1:
         raise ValueError("block must be >= 1")
-    m, l = -math.inf, 0.0
-    a = np.zeros(values.shape[1])
-    for j0 in range(0, len(scores), block):
-        s = scores[j0:j0 + block]
-        vb = values[j0:j0 + block]
-        m_new = max(m, float(s.max()))
-        if m_new == -math.inf:
-            continue
-        alpha = math.exp(m - m_new)
-        p = np.exp(s - m_new)
-        l = alpha * l + float(p.sum())
-        a = alpha * a + p @ vb
-        m = m_new
-    if l == 0.0:
-        return np.zeros_like(a), -math.inf, m, l
-    return a / l, m + math.log(l), m, l
+    m = np.full(n_rows, -np.inf)            # running maximum per row
+    ell = np.zeros(n_rows)                  # running denominator per row
+    acc = np.zeros((n_rows, vals.shape[1]))  # running accumulator per row
+    for lo in range(0, n, width):
+        s_blk = sc[:, lo:lo + width]
+        v_blk = vals[lo:lo + width]
+        m_blk = s_blk.max(axis=1)
+        m_next = np.maximum(m, m_blk)
+        live = np.isfinite(m_next)           # rows that have seen a key
+        ref = np.where(live, m_next, 0.0)    # any finite stand-in for dead rows
+        alpha = np.where(np.isfinite(m), np.exp(m - ref), 0.0)
+        p = np.where(live[:, None], np.exp(s_blk - ref[:, None]), 0.0)
+        ell = np.where(live, alpha * ell + p.sum(axis=1), ell)
+        acc = np.where(live[:, None], alpha[:, None] * acc + p @ v_blk, acc)
+        m = np.where(live, m_next, m)
+    seen = ell > 0.0
+    safe = np.where(seen, ell, 1.0)
+    o = np.where(seen[:, None], acc / safe[:, None], 0.0)
+    lse = np.where(seen, m + np.log(safe), -np.inf)
+    if one_row:
+        return o[0], float(lse[0]), float(m[0]), float(ell[0])
+    return o, lse, m, ell
 
 
 def merge_partials(parts):

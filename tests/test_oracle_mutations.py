@@ -113,24 +113,34 @@ def _head(variant):
 
 def _blocked(variant):
     def online_softmax_blocked(scores, values, block):
-        scores = np.asarray(scores, dtype=np.float64).ravel()
-        values = np.asarray(values, dtype=np.float64).reshape(len(scores), -1)
-        m, l = -math.inf, 0.0
-        a = np.zeros(values.shape[1])
-        for j0 in range(0, len(scores), int(block)):
-            s = scores[j0:j0 + int(block)]
-            vb = values[j0:j0 + int(block)]
-            m_new = max(m, float(s.max()))
-            if m_new == -math.inf:
-                continue
-            alpha = math.exp(m - m_new)
-            p = np.exp(s - m_new)
-            l = (l if variant == "blocked_no_rescale_l" else alpha * l) + float(p.sum())
-            a = (a if variant == "blocked_no_rescale_a" else alpha * a) + p @ vb
-            m = m_new
-        if l == 0.0:
-            return np.zeros_like(a), -math.inf, m, l
-        return a / l, m + math.log(l), m, l
+        sc = np.asarray(scores, dtype=np.float64)
+        one_row = sc.ndim == 1
+        sc = sc.reshape(1, -1) if one_row else sc.reshape(-1, sc.shape[-1])
+        n_rows, n = sc.shape
+        vals = np.asarray(values, dtype=np.float64).reshape(n, -1)
+        m = np.full(n_rows, -np.inf)
+        ell = np.zeros(n_rows)
+        acc = np.zeros((n_rows, vals.shape[1]))
+        for lo in range(0, n, int(block)):
+            s_blk = sc[:, lo:lo + int(block)]
+            v_blk = vals[lo:lo + int(block)]
+            m_next = np.maximum(m, s_blk.max(axis=1))
+            live = np.isfinite(m_next)
+            ref = np.where(live, m_next, 0.0)
+            alpha = np.where(np.isfinite(m), np.exp(m - ref), 0.0)
+            p = np.where(live[:, None], np.exp(s_blk - ref[:, None]), 0.0)
+            a_l = np.ones(n_rows) if variant == "blocked_no_rescale_l" else alpha
+            a_a = np.ones(n_rows) if variant == "blocked_no_rescale_a" else alpha
+            ell = np.where(live, a_l * ell + p.sum(axis=1), ell)
+            acc = np.where(live[:, None], a_a[:, None] * acc + p @ v_blk, acc)
+            m = np.where(live, m_next, m)
+        seen = ell > 0.0
+        safe = np.where(seen, ell, 1.0)
+        o = np.where(seen[:, None], acc / safe[:, None], 0.0)
+        lse = np.where(seen, m + np.log(safe), -np.inf)
+        if one_row:
+            return o[0], float(lse[0]), float(m[0]), float(ell[0])
+        return o, lse, m, ell
     return online_softmax_blocked
 
 

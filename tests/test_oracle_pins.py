@@ -165,23 +165,42 @@ def test_scalar_recurrence_matches_definition():
 
 
 def test_block_size_invariance():
-    # flash-attention, Lab 4: the blocked recurrence reproduces the direct
-    # result to ~1e-16 and does not depend on the block size.
-    r = _rng(0)
-    s = r.normal(size=64)
-    v = r.normal(size=(64, 8))
-    ref = np.exp(s - s.max())
-    ref /= ref.sum()
+    # "Understanding FlashAttention Pt 1", §2.4: the recurrence does not
+    # depend on where the tile boundaries fall, and for a block of query rows
+    # with masked (-inf) positions it is the direct masked softmax. Checked
+    # against scipy's softmax / logsumexp on a 6-row block of 37 keys with
+    # masked positions, one row with a single visible key and one row with
+    # none, for block widths that split it evenly, raggedly, or not at all.
+    from scipy.special import logsumexp, softmax
+    r = _rng(11)
+    s = 3.0 * r.normal(size=(6, 37))
+    v = r.normal(size=(37, 3))
+    s[1, ::3] = -np.inf           # every third key hidden
+    s[2, :] = -np.inf
+    s[2, 20] = 0.5                # a single visible key, in a middle block
+    s[3, :] = -np.inf             # no visible key at all
+    s[4, :30] = -np.inf           # only the last (ragged) block visible
+    live = np.isfinite(s).any(axis=1)
+    ref_o = np.zeros((6, 3))
+    ref_lse = np.full(6, -np.inf)
+    ref_o[live] = softmax(s[live], axis=1) @ v
+    ref_lse[live] = logsumexp(s[live], axis=1)
     outs = []
-    for blk in (1, 3, 4, 64, 1000):
-        o, lse, _, _ = oracle.online_softmax_blocked(s, v, blk)
-        assert np.abs(o - ref @ v).max() < 1e-13
-        outs.append((o, lse))
-    for o, lse in outs[1:]:
-        assert np.abs(o - outs[0][0]).max() < 1e-13
-        assert abs(lse - outs[0][1]) < 1e-13
-    o, lse = _row_attention(s, v)
-    assert np.abs(o - outs[0][0]).max() < 1e-13
+    for blk in (1, 2, 5, 8, 36, 37, 100):
+        o, lse, m, ell = oracle.online_softmax_blocked(s, v, blk)
+        assert np.abs(o - ref_o).max() < 1e-13
+        assert np.array_equal(np.isneginf(lse), ~live)
+        assert np.abs(lse[live] - ref_lse[live]).max() < 1e-13
+        assert np.array_equal(o[~live], np.zeros((int((~live).sum()), 3)))
+        # the state's maximum is the row maximum; its sum is l = exp(lse - m)
+        assert np.array_equal(m[live], s[live].max(axis=1))
+        assert np.abs(ell[live] - np.exp(ref_lse[live] - m[live])).max() < 1e-12
+        outs.append(o)
+    # one row at a time gives the same rows
+    for i in range(6):
+        oi, lsei, _, _ = oracle.online_softmax_blocked(s[i], v, 4)
+        assert np.abs(oi - ref_o[i]).max() < 1e-13
+        assert (lsei == -np.inf) if not live[i] else abs(lsei - ref_lse[i]) < 1e-13
 
 
 def test_merge_identity():
