@@ -4,6 +4,8 @@
 // compiled in fwd_bf16_split.hip, fwd_bf16_local.hip and
 // fwd_bf16_local_split.hip.
 
+#include <algorithm>
+
 #include "fwd_bf16_kernel.h"
 
 namespace attn {
@@ -44,20 +46,38 @@ static int device_cus() {
   return cached[dev];
 }
 
-// The persistent form (fwd_bf16_stream.hip) applies to dense problems whose
-// key tiles are all full and come in pairs (Nk a multiple of 128), with
-// enough of them for its schedule (the next Q rows are copied during the
-// first tiles of the current query tile), rows that 32-bit copy offsets
-// reach, and at least two query tiles per compute unit to walk.
-static int stream_grid(const FwdParams& p, int d, int64_t total) {
-  if (p.n_split > 1 || p.cu_q != nullptr || p.local || p.causal || p.bias != nullptr ||
-      p.kv_len != nullptr)
+// The persistent form (fwd_bf16_stream.hip), 256-row query tiles and one
+// workgroup per compute unit, applies with no bias, key lengths, key split,
+// window or packed sequences, when every key tile is full and they come in
+// pairs (Nk a multiple of 128), rows are in reach of 32-bit copy offsets and
+// there are at least two query tiles per compute unit. Every query tile that
+// is followed by another on its workgroup hosts that one's Q copy during
+// its first key tiles and needs enough of them: dense problems need at least
+// 14 key tiles at d = 128 (8 at d = 64). Causal problems also need the
+// diagonal on key-tile pairs (Nk >= Nq, Nk - Nq a multiple of 128), B*H a
+// multiple of 8 (whole heads per XCD), and the shortest tile of every round
+// but the last to be long enough. Returns the grid, or 0.
+static int stream_grid(const FwdParams& p, int d) {
+  if (p.n_split > 1 || p.cu_q != nullptr || p.local || p.bias != nullptr || p.kv_len != nullptr)
     return 0;
-  if (p.Nk % 128 != 0 || p.Nk / 64 < (d == 128 ? 14 : 8)) return 0;
-  if (64 * p.q_sn * 2 >= ((int64_t)1 << 31)) return 0;
+  if (p.Nk % 128 != 0 || 64 * p.q_sn * 2 >= ((int64_t)1 << 31)) return 0;
   const int cus = device_cus();
-  if (cus % 8 != 0 || total < 2 * (int64_t)cus) return 0;
-  return cus;   // one workgroup per compute unit, cus / 8 per XCD
+  if (cus % 8 != 0) return 0;
+  const int64_t n_qtiles = (p.Nq + 255) / 256;
+  const int64_t total = (int64_t)p.B * p.H * n_qtiles;
+  if (total < 2 * (int64_t)cus) return 0;
+  const int64_t min_host = d == 128 ? 14 : 8;
+  if (!p.causal) return p.Nk / 64 >= min_host ? cus : 0;
+  const int64_t off = p.Nk - p.Nq;
+  if (off < 0 || off % 128 != 0 || ((int64_t)p.B * p.H) % 8 != 0) return 0;
+  const int64_t hpx = (int64_t)p.B * p.H / 8, wpx = cus / 8;
+  const int64_t rounds = (hpx * n_qtiles + wpx - 1) / wpx;
+  if (rounds >= 2) {
+    const int64_t i = (rounds - 1) * wpx - 1;   // last tile of the last round but one
+    const int64_t qt = n_qtiles - 1 - i / hpx;
+    if (std::min<int64_t>(p.Nk, 256 * qt + 256 + off) / 64 < min_host) return 0;
+  }
+  return cus;
 }
 
 int launch_fwd_bf16(const FwdParams& p_in, int d, void* stream) {
@@ -109,8 +129,13 @@ int launch_fwd_bf16(const FwdParams& p_in, int d, void* stream) {
   p.bias_dma = (p.bias != nullptr && d == 64 && p.bias_vec && p.Nk >= 4 && p.Nk % 4 == 0 &&
                 !packed && 32 * p.bias_sn * 4 + 256 < ((int64_t)1 << 31)) ? 1 : 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (const int grid = stream_grid(p, d, total); grid > 0 && br == 256)
-    return (int)launch_bf16_stream(p, tm, d, grid, s);
+  if (const int grid = stream_grid(p, d); grid > 0) {
+    TileMap ts{};
+    ts.n_qtiles = (int)((p.Nq + 255) / 256);
+    ts.total = (int)((int64_t)p.B * p.H * ts.n_qtiles);
+    ts.per_xcd = (ts.total + 7) / 8;
+    return (int)launch_bf16_stream(p, ts, d, grid, s);
+  }
   if (varlen) return (int)launch_bf16_varlen(p, tm, d, waves, s);
   if (p.local) return (int)launch_bf16_local(p, tm, d, waves, s);
   return split ? (int)launch_bf16_split(p, tm, d, waves, s) : (int)launch_bf16_plain(p, tm, d, waves, s);

@@ -1,5 +1,6 @@
-// bf16 forward, persistent ("stream") form for dense problems: no mask, no
-// bias, no key split, every key tile full (Nk a multiple of 128).
+// bf16 forward, persistent ("stream") form for problems with no bias, key
+// lengths, key split or window, every key tile full (Nk a multiple of 128):
+// dense, or causal with the diagonal on key-tile boundaries.
 //
 // Same arithmetic as fwd_bf16_kernel.h (transposed scores S^T = K Q^T with
 // v_mfma_f32_32x32x16_bf16, base-2 exponentials against an overflow-checked
@@ -28,13 +29,25 @@
 // Rows of Q/O in LDS: row r at r * 2d bytes, 16-byte chunk c at slot
 // c ^ (r mod d/8), so that the 16 lanes of a transposing read or of a row
 // copy hit 16 different bank groups.
+//
+// Causal (bottom-right aligned: key j hidden from query i when
+// j > i + Nk - Nq; "Understanding FlashAttention Pt 1", section 3.5): query
+// tile t sees the key tiles up to its diagonal, 4 (t + 1) + (Nk - Nq) / 64
+// of them, so the tiles differ in length and a workgroup's share has to be
+// balanced ahead of time. Each XCD takes B*H/8 whole heads; their query
+// tiles, longest first, are dealt to the XCD's workgroups in rounds, the
+// direction alternating from round to round, so that every workgroup's
+// total is about the same and its own tiles come longest first (only a
+// workgroup's last tile can be too short to host the next one's Q copy).
+// The score tiles that cross a wavefront's diagonal are masked to -inf
+// before their exponentials; every row sees key 0, so no row is empty.
 
 #include "fwd_bf16_kernel.h"
 
 namespace attn {
 namespace {
 
-template <int D>
+template <int D, bool CAUSAL>
 __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, TileMap tm) {
   constexpr int W = 8;
   using G = Geo<D, W>;
@@ -54,15 +67,26 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  // Tiles of this workgroup: the logical tiles slot, slot + wpx, ... of its
-  // XCD's range (workgroup w runs on XCD w % 8).
+  // Tiles of this workgroup (workgroup w runs on XCD w % 8). Dense: the
+  // logical tiles slot, slot + wpx, ... of its XCD's range. Causal: round r
+  // gives it the tile at position slot (r even) or wpx - 1 - slot (r odd)
+  // of the r-th group of wpx in its XCD's tiles sorted longest first.
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, wpx = gridDim.x >> 3;
   const int base_logical = xcd * tm.per_xcd + slot;
-  const int n_items = max(0, min((tm.per_xcd - slot + wpx - 1) / wpx,
-                                 (tm.total - base_logical + wpx - 1) / wpx));
+  const int hpx = (p.B * p.H) >> 3;   // causal: heads per XCD
+  int n_items;
+  if constexpr (CAUSAL) {
+    const int n_x = hpx * tm.n_qtiles;
+    const int rounds = n_x / wpx, rem = n_x % wpx;
+    n_items = rounds + (((rounds & 1) ? wpx - 1 - slot : slot) < rem ? 1 : 0);
+  } else {
+    n_items = max(0, min((tm.per_xcd - slot + wpx - 1) / wpx,
+                         (tm.total - base_logical + wpx - 1) / wpx));
+  }
   if (n_items == 0) return;
 
-  const int Nq = p.Nq, Nk = p.Nk, nt = Nk / kBc;
+  const int Nq = p.Nq, Nk = p.Nk;
+  const int off = Nk - Nq;   // causal: key j hidden from query i when j > i + off
   const int64_t ksn = p.k_sn * 2, vsn = p.v_sn * 2;  // row strides in bytes
   struct Item {
     const uint8_t* q;   // row q0 + 32 * wave (clamped to the last row) of Q
@@ -71,15 +95,24 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
     __bf16* o;          // row 0 of O
     float* lse;         // row 0 of LSE
     int q0;             // first query row of the tile
+    int nt;             // key tiles it sees
   };
   auto item = [&](int it) {
-    const int logical = base_logical + it * wpx;
-    const int qt = logical % tm.n_qtiles;
-    const int hb = logical / tm.n_qtiles;
+    int qt, hb;
+    if constexpr (CAUSAL) {
+      const int i = it * wpx + ((it & 1) ? wpx - 1 - slot : slot);
+      qt = tm.n_qtiles - 1 - i / hpx;
+      hb = xcd * hpx + i % hpx;
+    } else {
+      const int logical = base_logical + it * wpx;
+      qt = logical % tm.n_qtiles;
+      hb = logical / tm.n_qtiles;
+    }
     const int h = hb % p.H, b = hb / p.H;
     const int hk = h / p.head_group;
     Item r;
     r.q0 = qt * kBr;
+    r.nt = (CAUSAL ? min(Nk, r.q0 + kBr + off) : Nk) / kBc;
     const int wrow = min(r.q0 + 32 * wave, Nq - 1);
     r.q = uniform_ptr(reinterpret_cast<const uint8_t*>(static_cast<const __bf16*>(p.q) + b * p.q_sb +
                                                        h * p.q_sh + (int64_t)wrow * p.q_sn));
@@ -254,6 +287,36 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
     }
   };
 
+  // causal: the scores of key tile kv0.. of the tile at q0 hidden from this
+  // lane's row become -inf; only tiles crossing this wavefront's diagonal
+  // (register r of block bb holds key kv0 + 32 bb + 16 (r / 8) + 8 hi + r % 8)
+  auto mask_causal = [&](f32x16 (&s)[2], int q0, int kv0) {
+    const int qmin = q0 + 32 * wave;
+    if (kv0 + kBc - 1 > qmin + off) {
+      const int lim = qmin + l32 + off;   // last key this lane's row sees
+#pragma unroll
+      for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kv0 + 32 * bb + 16 * (r >> 3) + 8 * hi + (r & 7);
+          if (key > lim) s[bb][r] = -INFINITY;
+        }
+    }
+  };
+
+  // 1 KB piece i of the previous query tile's O, from this wavefront's LDS
+  // rows to HBM (rows i * kRowsPerKB + lane / kC, whole 16-byte chunks)
+  auto drain = [&](const Item& prv, int i) {
+    const int ln = fresh(lane);
+    const int r = i * kRowsPerKB + ln / kC;
+    const u32x4 x = *reinterpret_cast<const u32x4*>(qw + 1024 * i + 16 * ln);
+    const int row = prv.q0 + 32 * wave + r;
+    if (row < Nq) {
+      const int chunk = (ln % kC) ^ (r % kC);
+      *reinterpret_cast<u32x4*>(reinterpret_cast<uint8_t*>(prv.o + (int64_t)row * p.o_sn) + 16 * chunk) = x;
+    }
+  };
+
   u32x4 pb[2][2];
   float rs_half = 0.f;
 
@@ -276,27 +339,26 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
       // into the same LDS rows (one copy per iteration)
       if (has_prev && j < kDrainIters) {
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const int i = 2 * j + c;
-          if (i < kQCopies) {
-            const int ln = fresh(lane);
-            const int r = i * kRowsPerKB + ln / kC;
-            const u32x4 x = *reinterpret_cast<const u32x4*>(qw + 1024 * i + 16 * ln);
-            const int row = prv.q0 + 32 * wave + r;
-            if (row < Nq) {
-              const int chunk = (ln % kC) ^ (r % kC);
-              *reinterpret_cast<u32x4*>(reinterpret_cast<uint8_t*>(prv.o + (int64_t)row * p.o_sn) +
-                                        16 * chunk) = x;
-            }
-          }
-        }
+        for (int c = 0; c < 2; ++c)
+          if (2 * j + c < kQCopies) drain(prv, 2 * j + c);
       }
       if (has_next && j >= kQ0 && j < kQ0 + kQCopies) q_copy(nxt, j - kQ0);
     } else {
+      // a query tile shorter than kDrainIters + 1 key tiles (only the last
+      // of a workgroup's causal tiles can be) drains the rest of the
+      // previous tile's O here
+      if constexpr (CAUSAL) {
+        if (has_prev && j < kDrainIters) {
+#pragma unroll
+          for (int i = 0; i < kQCopies; ++i)
+            if (i >= 2 * j) drain(prv, i);
+        }
+      }
       q_from_lds();   // nxt's Q (copied during this tile; own rows of Q)
     }
     // K_{j+2} and V_{j+1} of the stream into the buffers of K_j and V_{j-1};
     // past this query tile's keys they are nxt's first ones
+    const int nt = cur.nt;
     auto ktile = [&](int t) { return t < nt ? cur.k + t * kBc * ksn : nxt.k + (t - nt) * kBc * ksn; };
     auto vtile = [&](int t) { return t < nt ? cur.v + t * kBc * vsn : nxt.v + (t - nt) * kBc * vsn; };
     const uint8_t* const kt = uniform_ptr(ktile(j + 2));
@@ -330,6 +392,8 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
     }
     l_run += rs;
     rs_half = 0.f;
+    // S_{j+1}: key tile j + 1 of this query tile, or nxt's first
+    if constexpr (CAUSAL) mask_causal(sn, kLast ? nxt.q0 : cur.q0, kLast ? 0 : (j + 1) * kBc);
     using Next = std::integral_constant<bool, !kLast>;
     phase_b(Next{}, vlane + par * G::kVBytes, pb, sn, m_run == -INFINITY ? 0.f : m_run, rs_half);
     wait_tiles();
@@ -390,6 +454,7 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
     __syncthreads();
     q_from_lds();
     qk_plain(klane, sa);
+    if constexpr (CAUSAL) mask_causal(sa, c0.q0, 0);
     // iteration 0 overwrites K buffer 0: every wavefront must be done with K_0
     __syncthreads();
     start_tile(sa);
@@ -401,6 +466,7 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
     const Item cur = item(it);
     const Item prv = has_prev ? item(it - 1) : cur;
     const Item nxt = has_next ? item(it + 1) : cur;
+    const int nt = cur.nt;
     for (int j = 0; j + 2 < nt; j += 2) {
       iteration(No{}, j, cur, prv, nxt, has_next, has_prev, sa, sb);
       iteration(No{}, j + 1, cur, prv, nxt, has_next, has_prev, sb, sa);
@@ -416,27 +482,17 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
     } else {
       // no tile follows: copy O out at once (this wavefront's rows only)
 #pragma unroll
-      for (int i = 0; i < kQCopies; ++i) {
-        const int ln = fresh(lane);
-        const int r = i * kRowsPerKB + ln / kC;
-        const u32x4 x = *reinterpret_cast<const u32x4*>(qw + 1024 * i + 16 * ln);
-        const int row = cur.q0 + 32 * wave + r;
-        if (row < Nq) {
-          const int chunk = (ln % kC) ^ (r % kC);
-          *reinterpret_cast<u32x4*>(reinterpret_cast<uint8_t*>(cur.o + (int64_t)row * p.o_sn) +
-                                    16 * chunk) = x;
-        }
-      }
+      for (int i = 0; i < kQCopies; ++i) drain(cur, i);
     }
   }
 }
 
-template <int D>
+template <int D, bool CAUSAL>
 hipError_t launch_stream_d(const FwdParams& p, const TileMap& tm, int grid, hipStream_t stream) {
   using G = Geo<D, 8>;
   constexpr int kSmemAll = G::kSmem + 8 * 32 * 2 * D;  // K/V double buffers + Q/O rows
   static bool attr_set = false;  // benign race: every caller sets the same value
-  auto kern = fwd_bf16_stream_kernel<D>;
+  auto kern = fwd_bf16_stream_kernel<D, CAUSAL>;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kSmemAll);
@@ -450,8 +506,10 @@ hipError_t launch_stream_d(const FwdParams& p, const TileMap& tm, int grid, hipS
 }  // namespace
 
 hipError_t launch_bf16_stream(const FwdParams& p, const TileMap& tm, int d, int grid, hipStream_t s) {
-  if (d == 128) return launch_stream_d<128>(p, tm, grid, s);
-  if (d == 64) return launch_stream_d<64>(p, tm, grid, s);
+  if (d == 128) return p.causal ? launch_stream_d<128, true>(p, tm, grid, s)
+                                : launch_stream_d<128, false>(p, tm, grid, s);
+  if (d == 64) return p.causal ? launch_stream_d<64, true>(p, tm, grid, s)
+                               : launch_stream_d<64, false>(p, tm, grid, s);
   return hipErrorInvalidValue;
 }
 

@@ -1,9 +1,9 @@
 """Parity of the persistent ("stream") forward with the fp64 oracle.
 
-Dense bf16 problems (no mask, no bias, no key lengths) whose key count is a
-multiple of 128 and which have at least two 256-row query tiles per compute
-unit run on one workgroup per compute unit that walks its query tiles back
-to back: the next tile's Q rows are copied into LDS during the current tile,
+Dense and causal bf16 problems (no bias, no key lengths, no window) whose
+key count is a multiple of 128 and which have at least two 256-row query
+tiles per compute unit run on one workgroup per compute unit that walks its
+query tiles back to back: the next tile's Q rows are copied into LDS during the current tile,
 the key/value stream runs across the boundary and the finished O leaves
 through LDS during the next tile. The cases below all take that path (the
 launcher picks it for these shapes) with several tiles per workgroup, an
@@ -75,6 +75,54 @@ def test_stream_matches_oracle(B, H, Hk, Nq, Nk, d):
 
     rows = tile_rows(B, H, Nq, w.seed) + head_rows(0, 0, Nq) + head_rows(B - 1, H - 1, Nq)
     compare_rows(o_c, lse_c, rows, oracle_rows, "bf16", f"stream d={d} Nq={Nq} Nk={Nk}")
+
+
+CAUSAL_CASES = [
+    # (B, H, Hk, Nq, Nk, d): causal, Nk - Nq a multiple of 128, B*H a
+    # multiple of 8, 512 query tiles; two rounds of tiles per workgroup
+    (1, 64, 64, 1920, 2048, 128),   # diagonal offset 128, ragged last query tile
+    (2, 32, 8, 2048, 2048, 64),     # grouped heads (4 per K/V head), offset 0
+    (1, 64, 16, 2048, 2304, 64),    # offset 256, grouped heads
+    # offset 0 at d = 128: a workgroup's last tile can have 4 key tiles,
+    # fewer than the iterations that drain the previous tile's O
+    (2, 32, 32, 2048, 2048, 128),
+]
+
+
+@pytest.mark.parametrize("B,H,Hk,Nq,Nk,d", CAUSAL_CASES)
+def test_stream_causal_matches_oracle(B, H, Hk, Nq, Nk, d):
+    # Causal problems of these shapes take the persistent form with its
+    # longest-first rounds; every row of three whole heads (every position
+    # against the diagonal, in the first, a middle and the last head) and one
+    # row of every 128-row tile are compared. [Understanding FlashAttention
+    # Pt 1, section 3.5: causal tiles.]
+    _banner(f"stream causal B={B} H={H} Hk={Hk} Nq={Nq} Nk={Nk} d={d}")
+    w = workloads.Workload("stream_causal", B, H, Nq, Nk, d, causal=True,
+                           seed=3 * B * H + Nq + Nk + d, Hk=Hk)
+    inp = workloads.make_inputs(w)
+    o, lse = nan_outputs(B, H, Nq, d, "bf16")
+    ea.attn_fwd(inp["q"].cuda(), inp["k"].cuda(), inp["v"].cuda(), scale=inp["scale"],
+                causal=True, out=o, lse=lse)
+    torch.cuda.synchronize()
+    o_c, lse_c = o.cpu(), lse.cpu()
+    assert_all_written(o_c, lse_c, "stream causal")
+    rep = H // Hk
+    f = lambda t: t.double().numpy()
+    qd, kd, vd = f(inp["q"]), f(inp["k"]), f(inp["v"])
+
+    def oracle_rows(part):
+        out_o, out_l = [], []
+        for b, h, i in part:
+            oo, ll = oracle.attention_rows(qd[b:b + 1, h:h + 1], kd[b:b + 1, h // rep:h // rep + 1],
+                                           vd[b:b + 1, h // rep:h // rep + 1], [(0, 0, i)],
+                                           scale=inp["scale"], causal=True)
+            out_o.append(oo[0])
+            out_l.append(ll[0])
+        return np.stack(out_o), np.array(out_l)
+
+    rows = (tile_rows(B, H, Nq, w.seed) + head_rows(0, 0, Nq) + head_rows(B - 1, H // 2, Nq)
+            + head_rows(B - 1, H - 1, Nq))
+    compare_rows(o_c, lse_c, rows, oracle_rows, "bf16", f"stream causal d={d} Nq={Nq} Nk={Nk}")
 
 
 def test_stream_strided_views_and_determinism():
