@@ -888,16 +888,25 @@ __global__ __launch_bounds__(64 * W, 2) void fwd_bf16_kernel(FwdParams p, TileMa
 
   f32x16 sa[2], sb[2];
   if (nt > 0) {
+    // K_0 and the first bias block, then V_0 and K_1: the first two are
+    // waited for (copies complete in issue order) and the last two may land
+    // while S_0 is computed
     load_k(0);
-    load_v(0);
-    if (nt > 1) load_k(1);
     if (bias_dma) dma_bias(0);
-    wait_tiles();
+    load_v(0);
+    if (nt > 1) {
+      load_k(1);
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * G::kDmaPerWave) : "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(G::kDmaPerWave) : "memory");
+    }
     __syncthreads();
     qk_plain(klane, sa);
-    // iteration 0 overwrites K buffer 0 (with K_2, or with K_1 again when
-    // there are two tiles): every wave must be done reading K_0 first
-    if (nt > 1) __syncthreads();
+    // iteration 0 reads V_0 (and K_1) and overwrites K buffer 0 (with K_2,
+    // or with K_1 again when there are two tiles): every wave's copies have
+    // landed and every wave is done reading K_0
+    wait_tiles();
+    __syncthreads();
     mask_bias(0, sa);
     m_run = tile_max(sa);
     // the slices of tile 0 computed ahead (the later tiles' come from the

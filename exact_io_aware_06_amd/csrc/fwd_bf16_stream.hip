@@ -450,12 +450,16 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
     const uint8_t* k1 = uniform_ptr(c0.k + kBc * ksn);
 #pragma unroll
     for (int i = 0; i < G::kDmaPerWave; ++i) dma_k(k1, kbuf + G::kKBytes, i);
-    wait_tiles();
+    // the Q rows and K_0 (the oldest copies; they complete in issue order):
+    // V_0 and K_1 may land while S_0 is computed
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * G::kDmaPerWave) : "memory");
     __syncthreads();
     q_from_lds();
     qk_plain(klane, sa);
     if constexpr (CAUSAL) mask_causal(sa, c0.q0, 0);
-    // iteration 0 overwrites K buffer 0: every wavefront must be done with K_0
+    // iteration 0 reads V_0 and K_1 and overwrites K buffer 0: every
+    // wavefront's copies have landed and every one is done with K_0
+    wait_tiles();
     __syncthreads();
     start_tile(sa);
   }
