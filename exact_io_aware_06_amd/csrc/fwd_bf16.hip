@@ -4,8 +4,6 @@
 // compiled in fwd_bf16_split.hip, fwd_bf16_local.hip and
 // fwd_bf16_local_split.hip.
 
-#include <algorithm>
-
 #include "fwd_bf16_kernel.h"
 
 namespace attn {
@@ -50,13 +48,12 @@ static int device_cus() {
 // workgroup per compute unit, applies with no bias, key lengths, key split,
 // window or packed sequences, when every key tile is full and they come in
 // pairs (Nk a multiple of 128), rows are in reach of 32-bit copy offsets and
-// there are at least two query tiles per compute unit. Every query tile that
-// is followed by another on its workgroup hosts that one's Q copy during
-// its first key tiles and needs enough of them: dense problems need at least
-// 14 key tiles at d = 128 (8 at d = 64). Causal problems also need the
-// diagonal on key-tile pairs (Nk >= Nq, Nk - Nq a multiple of 128), B*H a
-// multiple of 8 (whole heads per XCD), and the shortest tile of every round
-// but the last to be long enough. Returns the grid, or 0.
+// there are at least two query tiles per compute unit. Dense query tiles
+// host the next one's Q copy during their first key tiles and need at least
+// 14 of them at d = 128 (8 at d = 64). Causal problems also need the
+// diagonal on key-tile pairs (Nk >= Nq, Nk - Nq a multiple of 128) and B*H a
+// multiple of 8 (whole heads per XCD); their short tiles copy at once.
+// Returns the grid, or 0.
 static int stream_grid(const FwdParams& p, int d) {
   if (p.n_split > 1 || p.cu_q != nullptr || p.local || p.bias != nullptr || p.kv_len != nullptr)
     return 0;
@@ -66,17 +63,9 @@ static int stream_grid(const FwdParams& p, int d) {
   const int64_t n_qtiles = (p.Nq + 255) / 256;
   const int64_t total = (int64_t)p.B * p.H * n_qtiles;
   if (total < 2 * (int64_t)cus) return 0;
-  const int64_t min_host = d == 128 ? 14 : 8;
-  if (!p.causal) return p.Nk / 64 >= min_host ? cus : 0;
+  if (!p.causal) return p.Nk / 64 >= (d == 128 ? 14 : 8) ? cus : 0;
   const int64_t off = p.Nk - p.Nq;
   if (off < 0 || off % 128 != 0 || ((int64_t)p.B * p.H) % 8 != 0) return 0;
-  const int64_t hpx = (int64_t)p.B * p.H / 8, wpx = cus / 8;
-  const int64_t rounds = (hpx * n_qtiles + wpx - 1) / wpx;
-  if (rounds >= 2) {
-    const int64_t i = (rounds - 1) * wpx - 1;   // last tile of the last round but one
-    const int64_t qt = n_qtiles - 1 - i / hpx;
-    if (std::min<int64_t>(p.Nk, 256 * qt + 256 + off) / 64 < min_host) return 0;
-  }
   return cus;
 }
 

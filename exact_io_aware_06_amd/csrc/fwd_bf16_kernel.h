@@ -1032,8 +1032,8 @@ hipError_t launch_bf16_plain(const FwdParams& p, const TileMap& tm, int d, int w
 hipError_t launch_bf16_split(const FwdParams& p, const TileMap& tm, int d, int waves, hipStream_t s);
 hipError_t launch_bf16_local(const FwdParams& p, const TileMap& tm, int d, int waves, hipStream_t s);
 hipError_t launch_bf16_varlen(const FwdParams& p, const TileMap& tm, int d, int waves, hipStream_t s);
-// Persistent form for dense problems (fwd_bf16_stream.hip): `grid`
-// workgroups, one per compute unit, each walking several query tiles.
+// Persistent form for dense and causal problems (fwd_bf16_stream.hip):
+// `grid` workgroups, one per compute unit, each walking several query tiles.
 hipError_t launch_bf16_stream(const FwdParams& p, const TileMap& tm, int d, int grid, hipStream_t s);
 
 }  // namespace attn

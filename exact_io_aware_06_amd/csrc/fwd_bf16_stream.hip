@@ -37,8 +37,9 @@
 // balanced ahead of time. Each XCD takes B*H/8 whole heads; their query
 // tiles, longest first, are dealt to the XCD's workgroups in rounds, the
 // direction alternating from round to round, so that every workgroup's
-// total is about the same and its own tiles come longest first (only a
-// workgroup's last tile can be too short to host the next one's Q copy).
+// total is about the same and its own tiles come longest first. A tile
+// too short to spread the previous O's drain and the next Q's copy over its
+// iterations does both at its start.
 // The score tiles that cross a wavefront's diagonal are masked to -inf
 // before their exponentials; every row sees key 0, so no row is empty.
 
@@ -344,16 +345,6 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
       }
       if (has_next && j >= kQ0 && j < kQ0 + kQCopies) q_copy(nxt, j - kQ0);
     } else {
-      // a query tile shorter than kDrainIters + 1 key tiles (only the last
-      // of a workgroup's causal tiles can be) drains the rest of the
-      // previous tile's O here
-      if constexpr (CAUSAL) {
-        if (has_prev && j < kDrainIters) {
-#pragma unroll
-          for (int i = 0; i < kQCopies; ++i)
-            if (i >= 2 * j) drain(prv, i);
-        }
-      }
       q_from_lds();   // nxt's Q (copied during this tile; own rows of Q)
     }
     // K_{j+2} and V_{j+1} of the stream into the buffers of K_j and V_{j-1};
@@ -471,14 +462,32 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
     const Item prv = has_prev ? item(it - 1) : cur;
     const Item nxt = has_next ? item(it + 1) : cur;
     const int nt = cur.nt;
-    for (int j = 0; j + 2 < nt; j += 2) {
-      iteration(No{}, j, cur, prv, nxt, has_next, has_prev, sa, sb);
-      iteration(No{}, j + 1, cur, prv, nxt, has_next, has_prev, sb, sa);
+    // A causal query tile with too few key tiles to spread the previous O's
+    // drain and the next Q's copy over its iterations does both here, at
+    // its start (each drain's LDS read is complete before the copy that
+    // overwrites its rows is issued: the store that uses it waits for it).
+    bool spread_prev = has_prev, spread_next = has_next;
+    if constexpr (CAUSAL) {
+      if (nt < kQ0 + kQCopies + 1) {
+        if (has_prev) {
+#pragma unroll
+          for (int i = 0; i < kQCopies; ++i) drain(prv, i);
+        }
+        if (has_next) {
+#pragma unroll
+          for (int i = 0; i < kQCopies; ++i) q_copy(nxt, i);
+        }
+        spread_prev = spread_next = false;
+      }
     }
-    iteration(No{}, nt - 2, cur, prv, nxt, has_next, has_prev, sa, sb);
+    for (int j = 0; j + 2 < nt; j += 2) {
+      iteration(No{}, j, cur, prv, nxt, spread_next, spread_prev, sa, sb);
+      iteration(No{}, j + 1, cur, prv, nxt, spread_next, spread_prev, sb, sa);
+    }
+    iteration(No{}, nt - 2, cur, prv, nxt, spread_next, spread_prev, sa, sb);
     // without a next query tile, nxt is this one: its Q rows are still in
     // LDS (nothing was copied over them) and its first S^T is computed again
-    iteration(Yes{}, nt - 1, cur, prv, nxt, has_next, has_prev, sb, sa);
+    iteration(Yes{}, nt - 1, cur, prv, nxt, spread_next, spread_prev, sb, sa);
     // sa holds nxt's first S^T
     stage_o(cur);
     if (has_next) {

@@ -67,7 +67,20 @@ def test_many_heads_forward_and_backward():
         ref = oracle.attention_backward(sl(q), sl(k), sl(v), sl(do), scale=scale)
         compare_grads([x[b:b + 1, h:h + 1].cpu() for x in (dq, dk, dv)], ref,
                       f"large bwd head ({b}, {h})")
-    del q, k, v, do, o, lse, dq, dk, dv
+    del dq, dk, dv
+    # the causal forward of the same tensors (the per-tile causal kernel:
+    # with 1040 heads per XCD the persistent deal would put short tiles
+    # back to back)
+    o.fill_(float("nan"))
+    lse.fill_(float("nan"))
+    ea.attn_fwd(q, k, v, causal=True, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert not torch.isnan(lse).any()
+    for b, h in ((0, 0), (1, 2077), (B - 1, H - 1)):
+        sl = lambda t: t[b:b + 1, h:h + 1].double().cpu().numpy()
+        ro, rl = oracle.attention_forward(sl(q), sl(k), sl(v), scale=scale, causal=True)
+        compare(sl(o), sl(lse), ro, rl, "bf16", f"large causal fwd head ({b}, {h})")
+    del q, k, v, do, o, lse
     torch.cuda.empty_cache()
 
 

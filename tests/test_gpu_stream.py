@@ -79,13 +79,17 @@ def test_stream_matches_oracle(B, H, Hk, Nq, Nk, d):
 
 CAUSAL_CASES = [
     # (B, H, Hk, Nq, Nk, d): causal, Nk - Nq a multiple of 128, B*H a
-    # multiple of 8, 512 query tiles; two rounds of tiles per workgroup
+    # multiple of 8, at least 512 query tiles
     (1, 64, 64, 1920, 2048, 128),   # diagonal offset 128, ragged last query tile
     (2, 32, 8, 2048, 2048, 64),     # grouped heads (4 per K/V head), offset 0
     (1, 64, 16, 2048, 2304, 64),    # offset 256, grouped heads
     # offset 0 at d = 128: a workgroup's last tile can have 4 key tiles,
     # fewer than the iterations that drain the previous tile's O
     (2, 32, 32, 2048, 2048, 128),
+    # many heads per XCD: eight rounds, short tiles (4, 8, 12 key tiles)
+    # back to back, each draining and copying at its start
+    (8, 64, 64, 1024, 1024, 128),
+    (4, 32, 8, 1024, 1152, 64),     # grouped heads, offset 128, short first tiles
 ]
 
 
