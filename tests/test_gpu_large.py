@@ -68,8 +68,8 @@ def test_many_heads_forward_and_backward():
         compare_grads([x[b:b + 1, h:h + 1].cpu() for x in (dq, dk, dv)], ref,
                       f"large bwd head ({b}, {h})")
     del dq, dk, dv
-    # the causal forward of the same tensors (the per-tile causal kernel:
-    # with 1040 heads per XCD the persistent deal would put short tiles
+    # the causal forward of the same tensors (the persistent causal form:
+    # 1040 heads per XCD, 260 rounds of tiles per workgroup, short tiles
     # back to back)
     o.fill_(float("nan"))
     lse.fill_(float("nan"))
