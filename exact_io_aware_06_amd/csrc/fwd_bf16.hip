@@ -45,18 +45,18 @@ static int device_cus() {
 }
 
 // The persistent form (fwd_bf16_stream.hip), 256-row query tiles and one
-// workgroup per compute unit, applies with no bias, key lengths, key split,
-// window or packed sequences, when every key tile is full and they come in
+// workgroup per compute unit, applies with no bias, key lengths, key split
+// or packed sequences, when every key tile is full and they come in
 // pairs (Nk a multiple of 128), rows are in reach of 32-bit copy offsets and
 // there are at least two query tiles per compute unit. Dense query tiles
 // host the next one's Q copy during their first key tiles and need at least
 // 14 of them at d = 128 (8 at d = 64). Causal problems also need the
 // diagonal on key-tile pairs (Nk >= Nq, Nk - Nq a multiple of 128) and B*H a
-// multiple of 8 (whole heads per XCD); their short tiles copy at once.
+// multiple of 8 (whole heads per XCD); windows need Nk >= Nq; short causal
+// and window tiles copy at once.
 // Returns the grid, or 0.
 static int stream_grid(const FwdParams& p, int d) {
-  if (p.n_split > 1 || p.cu_q != nullptr || p.local || p.bias != nullptr || p.kv_len != nullptr)
-    return 0;
+  if (p.n_split > 1 || p.cu_q != nullptr || p.bias != nullptr || p.kv_len != nullptr) return 0;
   if (p.Nk % 128 != 0 || 64 * p.q_sn * 2 >= ((int64_t)1 << 31)) return 0;
   const int cus = device_cus();
   if (cus % 8 != 0) return 0;
@@ -65,6 +65,7 @@ static int stream_grid(const FwdParams& p, int d) {
   if (total < 2 * (int64_t)cus) return 0;
   if (!p.causal) return p.Nk / 64 >= (d == 128 ? 14 : 8) ? cus : 0;
   const int64_t off = p.Nk - p.Nq;
+  if (p.local) return off >= 0 ? cus : 0;
   if (off < 0 || off % 128 != 0 || ((int64_t)p.B * p.H) % 8 != 0) return 0;
   return cus;
 }

@@ -42,14 +42,27 @@
 // iterations does both at its start.
 // The score tiles that cross a wavefront's diagonal are masked to -inf
 // before their exponentials; every row sees key 0, so no row is empty.
+//
+// Window (key j kept for query i iff i + Nk - Nq - left <= j <= i + Nk - Nq
+// + right; Nk >= Nq): the tiles are dealt as for dense problems, each
+// covering the key tiles from the left edge of its first row to the right
+// edge of its last (made even by one more masked tile), visited in a
+// rotated order: step t reads the tile whose absolute index is congruent
+// to t modulo their number, so neighbouring query tiles of a head, running
+// side by side on an XCD, read each key tile at the same step. Scores
+// outside either edge are masked; every row sees key i + Nk - Nq. A row's
+// first visited tile can be hidden from it: its reference stays unset
+// (-inf) and the overflow check's rare path sets it at the first tile it
+// sees.
 
 #include "fwd_bf16_kernel.h"
 
 namespace attn {
 namespace {
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool LOCAL>
 __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, TileMap tm) {
+  static_assert(CAUSAL || !LOCAL, "a window is a two-sided causal mask");
   constexpr int W = 8;
   using G = Geo<D, W>;
   constexpr int kBr = G::kBr;                   // 256 query rows per tile
@@ -76,7 +89,7 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
   const int base_logical = xcd * tm.per_xcd + slot;
   const int hpx = (p.B * p.H) >> 3;   // causal: heads per XCD
   int n_items;
-  if constexpr (CAUSAL) {
+  if constexpr (CAUSAL && !LOCAL) {
     const int n_x = hpx * tm.n_qtiles;
     const int rounds = n_x / wpx, rem = n_x % wpx;
     n_items = rounds + (((rounds & 1) ? wpx - 1 - slot : slot) < rem ? 1 : 0);
@@ -97,10 +110,12 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
     float* lse;         // row 0 of LSE
     int q0;             // first query row of the tile
     int nt;             // key tiles it sees
+    int kb;             // window: its first key tile
+    int rot;            // window: step 0 visits key tile kb + rot
   };
   auto item = [&](int it) {
     int qt, hb;
-    if constexpr (CAUSAL) {
+    if constexpr (CAUSAL && !LOCAL) {
       const int i = it * wpx + ((it & 1) ? wpx - 1 - slot : slot);
       qt = tm.n_qtiles - 1 - i / hpx;
       hb = xcd * hpx + i % hpx;
@@ -114,6 +129,24 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
     Item r;
     r.q0 = qt * kBr;
     r.nt = (CAUSAL ? min(Nk, r.q0 + kBr + off) : Nk) / kBc;
+    r.kb = 0;
+    r.rot = 0;
+    if constexpr (LOCAL) {
+      // key tiles from the left edge of its first row to the right edge of
+      // its last, made even (one more whole tile, masked, on either side)
+      int lo = max(r.q0 + off - p.win_left, 0) / kBc;
+      int hi_t = min((r.q0 + kBr - 1 + off + p.win_right) / kBc + 1, Nk / kBc);
+      if ((hi_t - lo) & 1) {
+        if (lo > 0) --lo;
+        else ++hi_t;   // hi_t odd < Nk / 64, which is even
+      }
+      r.kb = lo;
+      r.nt = hi_t - lo;
+      // step t visits the tile whose absolute index is = t (mod nt): the
+      // query tiles of one head on an XCD, all covering nt tiles, read the
+      // same key tile at the same step (its later copies come from L2)
+      r.rot = (r.nt - lo % r.nt) % r.nt;
+    }
     const int wrow = min(r.q0 + 32 * wave, Nq - 1);
     r.q = uniform_ptr(reinterpret_cast<const uint8_t*>(static_cast<const __bf16*>(p.q) + b * p.q_sb +
                                                        h * p.q_sh + (int64_t)wrow * p.q_sn));
@@ -124,6 +157,15 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
     r.o = static_cast<__bf16*>(p.o) + b * p.o_sb + h * p.o_sh;
     r.lse = p.lse + b * p.l_sb + h * p.l_sh;
     return r;
+  };
+  // key tile visited at step t of a query tile
+  auto tix = [&](const Item& it, int t) {
+    if constexpr (LOCAL) {
+      const int x = t + it.rot;
+      return it.kb + (x >= it.nt ? x - it.nt : x);
+    } else {
+      return t;
+    }
   };
 
   uint8_t* const kbuf = smem;                    // K tile t in buffer t % 2
@@ -288,19 +330,25 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
     }
   };
 
-  // causal: the scores of key tile kv0.. of the tile at q0 hidden from this
-  // lane's row become -inf; only tiles crossing this wavefront's diagonal
-  // (register r of block bb holds key kv0 + 32 bb + 16 (r / 8) + 8 hi + r % 8)
+  // causal / window: the scores of key tile kv0.. of the tile at q0 hidden
+  // from this lane's row become -inf (key > row + Nk - Nq + right, or, with a
+  // window, key < row + Nk - Nq - left); only tiles crossing an edge of this
+  // wavefront's rows (register r of block bb holds key kv0 + 32 bb +
+  // 16 (r / 8) + 8 hi + r % 8)
   auto mask_causal = [&](f32x16 (&s)[2], int q0, int kv0) {
     const int qmin = q0 + 32 * wave;
-    if (kv0 + kBc - 1 > qmin + off) {
-      const int lim = qmin + l32 + off;   // last key this lane's row sees
+    const int offr = LOCAL ? off + p.win_right : off;
+    const int offl = LOCAL ? off - p.win_left : 0;
+    const bool right = kv0 + kBc - 1 > qmin + offr;
+    const bool left = LOCAL && kv0 < qmin + 31 + offl;
+    if (right || left) {
+      const int row = qmin + l32;
 #pragma unroll
       for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kv0 + 32 * bb + 16 * (r >> 3) + 8 * hi + (r & 7);
-          if (key > lim) s[bb][r] = -INFINITY;
+          if (key > row + offr || (LOCAL && key < row + offl)) s[bb][r] = -INFINITY;
         }
     }
   };
@@ -350,8 +398,12 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
     // K_{j+2} and V_{j+1} of the stream into the buffers of K_j and V_{j-1};
     // past this query tile's keys they are nxt's first ones
     const int nt = cur.nt;
-    auto ktile = [&](int t) { return t < nt ? cur.k + t * kBc * ksn : nxt.k + (t - nt) * kBc * ksn; };
-    auto vtile = [&](int t) { return t < nt ? cur.v + t * kBc * vsn : nxt.v + (t - nt) * kBc * vsn; };
+    auto ktile = [&](int t) {
+      return t < nt ? cur.k + tix(cur, t) * kBc * ksn : nxt.k + tix(nxt, t - nt) * kBc * ksn;
+    };
+    auto vtile = [&](int t) {
+      return t < nt ? cur.v + tix(cur, t) * kBc * vsn : nxt.v + tix(nxt, t - nt) * kBc * vsn;
+    };
     const uint8_t* const kt = uniform_ptr(ktile(j + 2));
     const uint8_t* const vt = uniform_ptr(vtile(j + 1));
     uint8_t* const kd = kbuf + par * G::kKBytes;
@@ -384,7 +436,8 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
     l_run += rs;
     rs_half = 0.f;
     // S_{j+1}: key tile j + 1 of this query tile, or nxt's first
-    if constexpr (CAUSAL) mask_causal(sn, kLast ? nxt.q0 : cur.q0, kLast ? 0 : (j + 1) * kBc);
+    if constexpr (CAUSAL)
+      mask_causal(sn, kLast ? nxt.q0 : cur.q0, (kLast ? tix(nxt, 0) : tix(cur, j + 1)) * kBc);
     using Next = std::integral_constant<bool, !kLast>;
     phase_b(Next{}, vlane + par * G::kVBytes, pb, sn, m_run == -INFINITY ? 0.f : m_run, rs_half);
     wait_tiles();
@@ -432,13 +485,13 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
     const Item c0 = item(0);
 #pragma unroll
     for (int i = 0; i < kQCopies; ++i) q_copy(c0, i);
-    const uint8_t* k0 = c0.k;
-    const uint8_t* v0 = c0.v;
+    const uint8_t* k0 = uniform_ptr(c0.k + tix(c0, 0) * kBc * ksn);
+    const uint8_t* v0 = uniform_ptr(c0.v + tix(c0, 0) * kBc * vsn);
 #pragma unroll
     for (int i = 0; i < G::kDmaPerWave; ++i) dma_k(k0, kbuf, i);
 #pragma unroll
     for (int i = 0; i < G::kDmaPerWave; ++i) dma_v(v0, vbuf, i);
-    const uint8_t* k1 = uniform_ptr(c0.k + kBc * ksn);
+    const uint8_t* k1 = uniform_ptr(c0.k + tix(c0, 1) * kBc * ksn);
 #pragma unroll
     for (int i = 0; i < G::kDmaPerWave; ++i) dma_k(k1, kbuf + G::kKBytes, i);
     // the Q rows and K_0 (the oldest copies; they complete in issue order):
@@ -447,7 +500,7 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
     __syncthreads();
     q_from_lds();
     qk_plain(klane, sa);
-    if constexpr (CAUSAL) mask_causal(sa, c0.q0, 0);
+    if constexpr (CAUSAL) mask_causal(sa, c0.q0, tix(c0, 0) * kBc);
     // iteration 0 reads V_0 and K_1 and overwrites K buffer 0: every
     // wavefront's copies have landed and every one is done with K_0
     wait_tiles();
@@ -500,12 +553,12 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool LOCAL>
 hipError_t launch_stream_d(const FwdParams& p, const TileMap& tm, int grid, hipStream_t stream) {
   using G = Geo<D, 8>;
   constexpr int kSmemAll = G::kSmem + 8 * 32 * 2 * D;  // K/V double buffers + Q/O rows
   static bool attr_set = false;  // benign race: every caller sets the same value
-  auto kern = fwd_bf16_stream_kernel<D, CAUSAL>;
+  auto kern = fwd_bf16_stream_kernel<D, CAUSAL, LOCAL>;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kSmemAll);
@@ -519,10 +572,14 @@ hipError_t launch_stream_d(const FwdParams& p, const TileMap& tm, int grid, hipS
 }  // namespace
 
 hipError_t launch_bf16_stream(const FwdParams& p, const TileMap& tm, int d, int grid, hipStream_t s) {
-  if (d == 128) return p.causal ? launch_stream_d<128, true>(p, tm, grid, s)
-                                : launch_stream_d<128, false>(p, tm, grid, s);
-  if (d == 64) return p.causal ? launch_stream_d<64, true>(p, tm, grid, s)
-                               : launch_stream_d<64, false>(p, tm, grid, s);
+  if (d == 128)
+    return p.local ? launch_stream_d<128, true, true>(p, tm, grid, s)
+                   : p.causal ? launch_stream_d<128, true, false>(p, tm, grid, s)
+                              : launch_stream_d<128, false, false>(p, tm, grid, s);
+  if (d == 64)
+    return p.local ? launch_stream_d<64, true, true>(p, tm, grid, s)
+                   : p.causal ? launch_stream_d<64, true, false>(p, tm, grid, s)
+                              : launch_stream_d<64, false, false>(p, tm, grid, s);
   return hipErrorInvalidValue;
 }
 

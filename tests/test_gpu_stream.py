@@ -129,6 +129,52 @@ def test_stream_causal_matches_oracle(B, H, Hk, Nq, Nk, d):
     compare_rows(o_c, lse_c, rows, oracle_rows, "bf16", f"stream causal d={d} Nq={Nq} Nk={Nk}")
 
 
+WINDOW_CASES = [
+    # (B, H, Hk, Nq, Nk, d, causal, (left, right)): Nk >= Nq, at least 512
+    # query tiles; bands of whole and partial tiles, made even
+    (2, 64, 64, 1024, 1024, 128, True, (300, 0)),      # causal window, 6-7 key tiles
+    (2, 64, 16, 1024, 1280, 64, False, (200, 100)),    # two-sided, offset 256, grouped heads
+    (1, 128, 128, 1024, 1024, 128, False, (64, 37)),   # narrow band: short tiles copy at once
+    (1, 64, 64, 2048, 2048, 128, True, (1100, 0)),     # 22-key-tile bands, spread copies
+]
+
+
+@pytest.mark.parametrize("B,H,Hk,Nq,Nk,d,causal,window", WINDOW_CASES)
+def test_stream_window_matches_oracle(B, H, Hk, Nq, Nk, d, causal, window):
+    # Sliding windows on the persistent form with its rotated key order
+    # (reading 18: key j kept iff i + Nk - Nq - left <= j <= i + Nk - Nq +
+    # right); one row of every 128-row tile and three whole heads.
+    # [flash-attention, Part III, window_size; FlashAttention, Explained,
+    # section 14.]
+    _banner(f"stream window B={B} H={H} Hk={Hk} Nq={Nq} Nk={Nk} d={d} causal={causal} {window}")
+    w = workloads.Workload("stream_window", B, H, Nq, Nk, d, causal=causal, window=window,
+                           seed=5 * B * H + Nq + Nk + d + window[0], Hk=Hk)
+    inp = workloads.make_inputs(w)
+    o, lse = nan_outputs(B, H, Nq, d, "bf16")
+    ea.attn_fwd(inp["q"].cuda(), inp["k"].cuda(), inp["v"].cuda(), scale=inp["scale"],
+                causal=causal, window=window, out=o, lse=lse)
+    torch.cuda.synchronize()
+    o_c, lse_c = o.cpu(), lse.cpu()
+    assert_all_written(o_c, lse_c, "stream window")
+    rep = H // Hk
+    f = lambda t: t.double().numpy()
+    qd, kd, vd = f(inp["q"]), f(inp["k"]), f(inp["v"])
+
+    def oracle_rows(part):
+        out_o, out_l = [], []
+        for b, h, i in part:
+            oo, ll = oracle.attention_rows(qd[b:b + 1, h:h + 1], kd[b:b + 1, h // rep:h // rep + 1],
+                                           vd[b:b + 1, h // rep:h // rep + 1], [(0, 0, i)],
+                                           scale=inp["scale"], causal=causal, window=window)
+            out_o.append(oo[0])
+            out_l.append(ll[0])
+        return np.stack(out_o), np.array(out_l)
+
+    rows = (tile_rows(B, H, Nq, w.seed) + head_rows(0, 0, Nq) + head_rows(B - 1, H // 2, Nq)
+            + head_rows(B - 1, H - 1, Nq))
+    compare_rows(o_c, lse_c, rows, oracle_rows, "bf16", f"stream window {window}")
+
+
 def test_stream_strided_views_and_determinism():
     # [B, N, H, d] storage seen as [B, H, N, d] for q, k, v and the output;
     # two calls are bitwise equal
