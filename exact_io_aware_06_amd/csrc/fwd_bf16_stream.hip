@@ -1,6 +1,6 @@
 // bf16 forward, persistent ("stream") form for problems with no bias, key
-// lengths, key split or window, every key tile full (Nk a multiple of 128):
-// dense, or causal with the diagonal on key-tile boundaries.
+// lengths or key split, every key tile full (Nk a multiple of 128): dense,
+// causal with the diagonal on key-tile pairs, or a sliding window.
 //
 // Same arithmetic as fwd_bf16_kernel.h (transposed scores S^T = K Q^T with
 // v_mfma_f32_32x32x16_bf16, base-2 exponentials against an overflow-checked
@@ -81,10 +81,11 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  // Tiles of this workgroup (workgroup w runs on XCD w % 8). Dense: the
-  // logical tiles slot, slot + wpx, ... of its XCD's range. Causal: round r
-  // gives it the tile at position slot (r even) or wpx - 1 - slot (r odd)
-  // of the r-th group of wpx in its XCD's tiles sorted longest first.
+  // Tiles of this workgroup (workgroup w runs on XCD w % 8). Dense and
+  // window: the logical tiles slot, slot + wpx, ... of its XCD's range.
+  // Causal: round r gives it the tile at position slot (r even) or
+  // wpx - 1 - slot (r odd) of the r-th group of wpx in its XCD's tiles
+  // sorted longest first.
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, wpx = gridDim.x >> 3;
   const int base_logical = xcd * tm.per_xcd + slot;
   const int hpx = (p.B * p.H) >> 3;   // causal: heads per XCD
@@ -100,7 +101,7 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
   if (n_items == 0) return;
 
   const int Nq = p.Nq, Nk = p.Nk;
-  const int off = Nk - Nq;   // causal: key j hidden from query i when j > i + off
+  const int off = Nk - Nq;   // the diagonal: key i + off for query i
   const int64_t ksn = p.k_sn * 2, vsn = p.v_sn * 2;  // row strides in bytes
   struct Item {
     const uint8_t* q;   // row q0 + 32 * wave (clamped to the last row) of Q
