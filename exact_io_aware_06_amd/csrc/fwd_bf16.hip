@@ -45,29 +45,38 @@ static int device_cus() {
 }
 
 // The persistent form (fwd_bf16_stream.hip), 256-row query tiles and one
-// workgroup per compute unit, applies with no bias, key lengths, key split
-// or packed sequences, when every key tile is full and they come in
-// pairs (Nk a multiple of 128), rows are in reach of 32-bit copy offsets and
-// there are at least two query tiles per compute unit. Dense query tiles
-// host the next one's Q copy during their first key tiles and need at least
-// 14 of them at d = 128 (8 at d = 64). Causal problems also need the
-// diagonal on key-tile pairs (Nk >= Nq, Nk - Nq a multiple of 128) and B*H a
-// multiple of 8 (whole heads per XCD); windows need Nk >= Nq; short causal
-// and window tiles copy at once.
-// Returns the grid, or 0.
-static int stream_grid(const FwdParams& p, int d) {
+// workgroup per compute unit, streams key tiles of kt keys (64, or 128 at
+// d = 64). It applies with no bias, key lengths, key split or packed
+// sequences, when every key tile is full and they come in pairs (Nk a
+// multiple of 2 kt), rows are in reach of 32-bit copy offsets and there are
+// at least two query tiles per compute unit. Dense query tiles host the next
+// one's Q copy during their first key tiles and need at least 14 of them at
+// d = 128 (8 at d = 64). Causal problems also need the diagonal on key-tile
+// pairs (Nk >= Nq, Nk - Nq a multiple of 2 kt) and B*H a multiple of 8
+// (whole heads per XCD); windows need Nk >= Nq; short causal and window
+// tiles copy at once. Returns the grid, or 0.
+static int stream_grid(const FwdParams& p, int d, int kt) {
   if (p.n_split > 1 || p.cu_q != nullptr || p.bias != nullptr || p.kv_len != nullptr) return 0;
-  if (p.Nk % 128 != 0 || 64 * p.q_sn * 2 >= ((int64_t)1 << 31)) return 0;
+  if (p.Nk % (2 * kt) != 0 || 64 * p.q_sn * 2 >= ((int64_t)1 << 31)) return 0;
   const int cus = device_cus();
   if (cus % 8 != 0) return 0;
   const int64_t n_qtiles = (p.Nq + 255) / 256;
   const int64_t total = (int64_t)p.B * p.H * n_qtiles;
   if (total < 2 * (int64_t)cus) return 0;
-  if (!p.causal) return p.Nk / 64 >= (d == 128 ? 14 : 8) ? cus : 0;
+  if (!p.causal) return p.Nk / kt >= (d == 128 ? 14 : 8) ? cus : 0;
   const int64_t off = p.Nk - p.Nq;
   if (p.local) return off >= 0 ? cus : 0;
-  if (off < 0 || off % 128 != 0 || ((int64_t)p.B * p.H) % 8 != 0) return 0;
+  if (off < 0 || off % (2 * kt) != 0 || ((int64_t)p.B * p.H) % 8 != 0) return 0;
   return cus;
+}
+
+// Key tile of the persistent form: 128 keys for dense problems at d = 64
+// (half the per-tile checks, waits and barriers per key; the K/V buffers
+// take the 64 KiB of a d = 128 tile; measured 1.2-1.3% faster at
+// N = 2048 and 4096), else 64 (with a causal diagonal or a window edge, a
+// 128-key tile masks twice as much work: 2-3% slower).
+static int stream_key_tile(const FwdParams& p, int d) {
+  return (d == 64 && !p.causal && stream_grid(p, d, 128) > 0) ? 128 : 64;
 }
 
 int launch_fwd_bf16(const FwdParams& p_in, int d, void* stream) {
@@ -119,12 +128,12 @@ int launch_fwd_bf16(const FwdParams& p_in, int d, void* stream) {
   p.bias_dma = (p.bias != nullptr && d == 64 && p.bias_vec && p.Nk >= 4 && p.Nk % 4 == 0 &&
                 !packed && 32 * p.bias_sn * 4 + 256 < ((int64_t)1 << 31)) ? 1 : 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (const int grid = stream_grid(p, d); grid > 0) {
+  if (const int kt = stream_key_tile(p, d), grid = stream_grid(p, d, kt); grid > 0) {
     TileMap ts{};
     ts.n_qtiles = (int)((p.Nq + 255) / 256);
     ts.total = (int)((int64_t)p.B * p.H * ts.n_qtiles);
     ts.per_xcd = (ts.total + 7) / 8;
-    return (int)launch_bf16_stream(p, ts, d, grid, s);
+    return (int)launch_bf16_stream(p, ts, d, kt, grid, s);
   }
   if (varlen) return (int)launch_bf16_varlen(p, tm, d, waves, s);
   if (p.local) return (int)launch_bf16_local(p, tm, d, waves, s);

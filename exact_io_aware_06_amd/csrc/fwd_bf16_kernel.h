@@ -1032,8 +1032,11 @@ hipError_t launch_bf16_plain(const FwdParams& p, const TileMap& tm, int d, int w
 hipError_t launch_bf16_split(const FwdParams& p, const TileMap& tm, int d, int waves, hipStream_t s);
 hipError_t launch_bf16_local(const FwdParams& p, const TileMap& tm, int d, int waves, hipStream_t s);
 hipError_t launch_bf16_varlen(const FwdParams& p, const TileMap& tm, int d, int waves, hipStream_t s);
-// Persistent form for dense and causal problems (fwd_bf16_stream.hip):
-// `grid` workgroups, one per compute unit, each walking several query tiles.
-hipError_t launch_bf16_stream(const FwdParams& p, const TileMap& tm, int d, int grid, hipStream_t s);
+// Persistent form for dense, causal and window problems
+// (fwd_bf16_stream.hip): `grid` workgroups, one per compute unit, each
+// walking several query tiles as one stream of key tiles of `key_tile` keys
+// (64, or 128 for dense problems at d = 64).
+hipError_t launch_bf16_stream(const FwdParams& p, const TileMap& tm, int d, int key_tile, int grid,
+                              hipStream_t s);
 
 }  // namespace attn

@@ -30,6 +30,11 @@
 // c ^ (r mod d/8), so that the 16 lanes of a transposing read or of a row
 // copy hit 16 different bank groups.
 //
+// Key tiles hold 64 keys (NB = 2 blocks of 32), or 128 (NB = 4) for dense
+// problems at d = 64, whose vector work per MFMA is twice that of d = 128:
+// the per-tile overflow check, copy waits and barrier then come half as
+// often per key.
+//
 // Causal (bottom-right aligned: key j hidden from query i when
 // j > i + Nk - Nq; "Understanding FlashAttention Pt 1", section 3.5): query
 // tile t sees the key tiles up to its diagonal, 4 (t + 1) + (Nk - Nq) / 64
@@ -60,11 +65,17 @@
 namespace attn {
 namespace {
 
-template <int D, bool CAUSAL, bool LOCAL>
+// NB: 32-key blocks per key tile (2: 64 keys, 4: 128 keys).
+template <int D, int NB, bool CAUSAL, bool LOCAL>
 __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, TileMap tm) {
   static_assert(CAUSAL || !LOCAL, "a window is a two-sided causal mask");
+  static_assert(NB == 2 || NB == 4, "64- or 128-key tiles");
   constexpr int W = 8;
   using G = Geo<D, W>;
+  constexpr int kKT = 32 * NB;                  // keys per key tile
+  constexpr int kKBytes = kKT * D * 2;          // one K (or V) tile in LDS
+  constexpr int kSmemKV = 4 * kKBytes;          // two K and two V buffers
+  constexpr int kDmaPerWave = kKBytes / 1024 / W;  // 1 KB copies per wave per tile
   constexpr int kBr = G::kBr;                   // 256 query rows per tile
   constexpr int kC = D / 8;                     // 16-byte chunks per row
   constexpr int kRowBytes = 2 * D;
@@ -129,17 +140,17 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
     const int hk = h / p.head_group;
     Item r;
     r.q0 = qt * kBr;
-    r.nt = (CAUSAL ? min(Nk, r.q0 + kBr + off) : Nk) / kBc;
+    r.nt = (CAUSAL ? min(Nk, r.q0 + kBr + off) : Nk) / kKT;
     r.kb = 0;
     r.rot = 0;
     if constexpr (LOCAL) {
       // key tiles from the left edge of its first row to the right edge of
       // its last, made even (one more whole tile, masked, on either side)
-      int lo = max(r.q0 + off - p.win_left, 0) / kBc;
-      int hi_t = min((r.q0 + kBr - 1 + off + p.win_right) / kBc + 1, Nk / kBc);
+      int lo = max(r.q0 + off - p.win_left, 0) / kKT;
+      int hi_t = min((r.q0 + kBr - 1 + off + p.win_right) / kKT + 1, Nk / kKT);
       if ((hi_t - lo) & 1) {
         if (lo > 0) --lo;
-        else ++hi_t;   // hi_t odd < Nk / 64, which is even
+        else ++hi_t;   // hi_t odd < Nk / kKT, which is even
       }
       r.kb = lo;
       r.nt = hi_t - lo;
@@ -170,13 +181,13 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
   };
 
   uint8_t* const kbuf = smem;                    // K tile t in buffer t % 2
-  uint8_t* const vbuf = smem + 2 * G::kKBytes;   // V tile t in buffer t % 2
-  uint8_t* const qw = smem + G::kSmem + wave * kQWave;  // this wavefront's Q / O rows
+  uint8_t* const vbuf = smem + 2 * kKBytes;      // V tile t in buffer t % 2
+  uint8_t* const qw = smem + kSmemKV + wave * kQWave;  // this wavefront's Q / O rows
 
   // ---- LDS DMA lane offsets of a full K / V tile (every tile is full here)
-  uint32_t koff[G::kDmaPerWave], voff[G::kDmaPerWave];
+  uint32_t koff[kDmaPerWave], voff[kDmaPerWave];
 #pragma unroll
-  for (int i = 0; i < G::kDmaPerWave; ++i) {
+  for (int i = 0; i < kDmaPerWave; ++i) {
     koff[i] = (uint32_t)(k_dma_key<D, W>(wave, lane, i) * (int)ksn + k_dma_col<D, W>(wave, lane, i));
     voff[i] = (uint32_t)(v_dma_key<D, W>(wave, lane, i) * (int)vsn + v_dma_col<D, W>(wave, lane, i));
   }
@@ -217,10 +228,11 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
   const int gi = l32 & 15;
   const uint8_t* const vlane = vbuf + 2 * hi * G::kVBlock + 128 * (l32 >> 4) +
                                64 * ((gi >> 1) & 1) + 16 * (gi >> 2) + 8 * (gi & 1);
-  constexpr int kNq = 2 * G::kNkk;
-  constexpr int kNv = 4 * G::kNcb;
+  // K fragment i of a tile: 32-key block i % NB, k-step i / NB
+  constexpr int kNq = NB * G::kNkk;
+  constexpr int kNv = 2 * NB * G::kNcb;
   auto kfrag = [&](const uint8_t* kb, int i) {
-    return *reinterpret_cast<const bf16x8*>(kb + (i & 1) * 2 * G::kKBlock + (i >> 1) * 512);
+    return *reinterpret_cast<const bf16x8*>(kb + (i % NB) * 2 * G::kKBlock + (i / NB) * 512);
   };
   auto vfrag = [&](const uint8_t* vb, int i) {
     const uint8_t* p0 = vb + 4 * (i / G::kNcb) * G::kVBlock + 256 * (i % G::kNcb);
@@ -232,15 +244,15 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
   float l_run = 0.f;
   const float c2 = p.scale_log2;
 
-  auto tile_max = [&](const f32x16 (&s)[2]) {
+  auto tile_max = [&](const f32x16 (&s)[NB]) {
     float m = -INFINITY;
 #pragma unroll
-    for (int bb = 0; bb < 2; ++bb)
+    for (int bb = 0; bb < NB; ++bb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) m = fmaxf(m, s[bb][r]);
     return lane_pair_max(m) * c2;
   };
-  auto exp_slice = [&](const f32x16 (&s)[2], u32x4 (&pw)[2][2], float m_use, float& rs, int i) {
+  auto exp_slice = [&](const f32x16 (&s)[NB], u32x4 (&pw)[NB][2], float m_use, float& rs, int i) {
     const int bb = i >> 3, r = 2 * (i & 7);
     float x[2];
 #pragma unroll
@@ -258,24 +270,24 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
   // on the matrix pipe beside the second half of tile j's exponentials and
   // the tile copies; the overflow check; phase B = O += V_j P_j beside the
   // first half of tile j+1's exponentials.
-  constexpr int kSlices = 16;
+  constexpr int kSlices = 8 * NB;
   constexpr int kPre = kSlices / 2;
   constexpr int kSlicesA = kSlices - kPre;
-  constexpr int kNdma = 2 * G::kDmaPerWave;
-  auto phase_a = [&](auto with_qk, const uint8_t* kb, const f32x16 (&sc)[2], f32x16 (&sn)[2],
-                     u32x4 (&pb)[2][2], float m_use, auto&& dma) {
+  constexpr int kNdma = 2 * kDmaPerWave;
+  auto phase_a = [&](auto with_qk, const uint8_t* kb, const f32x16 (&sc)[NB], f32x16 (&sn)[NB],
+                     u32x4 (&pb)[NB][2], float m_use, auto&& dma) {
     float rs = 0.f;
     __builtin_amdgcn_s_setprio(1);
     if constexpr (decltype(with_qk)::value) {
-      sn[0] = f32x16{};
-      sn[1] = f32x16{};
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb) sn[bb] = f32x16{};
       bf16x8 kf[kPf];
 #pragma unroll
       for (int i = 0; i < kPf; ++i) kf[i] = kfrag(kb, i);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < kNq; ++i) {
-        sn[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % kPf], qf[i >> 1], sn[i & 1], 0, 0, 0);
+        sn[i % NB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % kPf], qf[i / NB], sn[i % NB], 0, 0, 0);
         if (i + kPf < kNq) kf[i % kPf] = kfrag(kb, i + kPf);
         dma(i);
 #pragma unroll
@@ -289,16 +301,18 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
     }
     return rs;
   };
-  auto phase_b = [&](auto with_next, const uint8_t* vb, u32x4 (&pb)[2][2], const f32x16 (&sn)[2],
+  auto phase_b = [&](auto with_next, const uint8_t* vb, u32x4 (&pb)[NB][2], const f32x16 (&sn)[NB],
                      float m_use, float& rs_next) {
     __builtin_amdgcn_s_setprio(0);
     bf16x8 vf[kPf];
 #pragma unroll
     for (int i = 0; i < kPf; ++i) vf[i] = vfrag(vb, i);
     __builtin_amdgcn_sched_barrier(0);
+    // the slices computed ahead write the P registers of key blocks
+    // 0 .. NB/2 - 1 (16-key groups u < NB), read by MFMAs i < NB * kNcb
     constexpr int kPer = kSlices / kNv;
     constexpr int kB0 = kNv - kPre / kPer;
-    static_assert(kPre % kPer == 0 && kPre <= 12, "slices must follow the MFMAs that read their P");
+    static_assert(kPre % kPer == 0 && kB0 >= NB * G::kNcb, "slices must follow the MFMAs that read their P");
 #pragma unroll
     for (int i = 0; i < kNv; ++i) {
       const int u = i / G::kNcb;
@@ -316,16 +330,16 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  auto qk_plain = [&](const uint8_t* kb, f32x16 (&s)[2]) {
-    s[0] = f32x16{};
-    s[1] = f32x16{};
+  auto qk_plain = [&](const uint8_t* kb, f32x16 (&s)[NB]) {
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) s[bb] = f32x16{};
     bf16x8 kf[kPf];
 #pragma unroll
     for (int i = 0; i < kPf; ++i) kf[i] = kfrag(kb, i);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < kNq; ++i) {
-      s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % kPf], qf[i >> 1], s[i & 1], 0, 0, 0);
+      s[i % NB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % kPf], qf[i / NB], s[i % NB], 0, 0, 0);
       if (i + kPf < kNq) kf[i % kPf] = kfrag(kb, i + kPf);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -336,16 +350,16 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
   // window, key < row + Nk - Nq - left); only tiles crossing an edge of this
   // wavefront's rows (register r of block bb holds key kv0 + 32 bb +
   // 16 (r / 8) + 8 hi + r % 8)
-  auto mask_causal = [&](f32x16 (&s)[2], int q0, int kv0) {
+  auto mask_causal = [&](f32x16 (&s)[NB], int q0, int kv0) {
     const int qmin = q0 + 32 * wave;
     const int offr = LOCAL ? off + p.win_right : off;
     const int offl = LOCAL ? off - p.win_left : 0;
-    const bool right = kv0 + kBc - 1 > qmin + offr;
+    const bool right = kv0 + kKT - 1 > qmin + offr;
     const bool left = LOCAL && kv0 < qmin + 31 + offl;
     if (right || left) {
       const int row = qmin + l32;
 #pragma unroll
-      for (int bb = 0; bb < 2; ++bb)
+      for (int bb = 0; bb < NB; ++bb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kv0 + 32 * bb + 16 * (r >> 3) + 8 * hi + (r & 7);
@@ -367,7 +381,7 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
     }
   };
 
-  u32x4 pb[2][2];
+  u32x4 pb[NB][2];
   float rs_half = 0.f;
 
   // Two kinds of iteration: ordinary (tile j+1 of the same query tile
@@ -380,7 +394,7 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
   using Yes = std::integral_constant<bool, true>;
   using No = std::integral_constant<bool, false>;
   auto iteration = [&](auto last, int j, const Item& cur, const Item& prv, const Item& nxt,
-                       bool has_next, bool has_prev, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+                       bool has_next, bool has_prev, f32x16 (&sc)[NB], f32x16 (&sn)[NB]) {
     constexpr bool kLast = decltype(last)::value;
     const int par = j & 1;
     if constexpr (!kLast) {
@@ -400,24 +414,24 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
     // past this query tile's keys they are nxt's first ones
     const int nt = cur.nt;
     auto ktile = [&](int t) {
-      return t < nt ? cur.k + tix(cur, t) * kBc * ksn : nxt.k + tix(nxt, t - nt) * kBc * ksn;
+      return t < nt ? cur.k + tix(cur, t) * kKT * ksn : nxt.k + tix(nxt, t - nt) * kKT * ksn;
     };
     auto vtile = [&](int t) {
-      return t < nt ? cur.v + tix(cur, t) * kBc * vsn : nxt.v + tix(nxt, t - nt) * kBc * vsn;
+      return t < nt ? cur.v + tix(cur, t) * kKT * vsn : nxt.v + tix(nxt, t - nt) * kKT * vsn;
     };
     const uint8_t* const kt = uniform_ptr(ktile(j + 2));
     const uint8_t* const vt = uniform_ptr(vtile(j + 1));
-    uint8_t* const kd = kbuf + par * G::kKBytes;
-    uint8_t* const vd = vbuf + (par ^ 1) * G::kVBytes;
+    uint8_t* const kd = kbuf + par * kKBytes;
+    uint8_t* const vd = vbuf + (par ^ 1) * kKBytes;
     auto dma = [&](int s) {
 #pragma unroll
       for (int n = 0; n < kNdma; ++n) {
         if ((n * kNq) / kNdma != s) continue;
-        if (n < G::kDmaPerWave) dma_k(kt, kd, n);
-        else dma_v(vt, vd, n - G::kDmaPerWave);
+        if (n < kDmaPerWave) dma_k(kt, kd, n);
+        else dma_v(vt, vd, n - kDmaPerWave);
       }
     };
-    float rs = rs_half + phase_a(Yes{}, klane + (par ^ 1) * G::kKBytes, sc, sn, pb,
+    float rs = rs_half + phase_a(Yes{}, klane + (par ^ 1) * kKBytes, sc, sn, pb,
                                  m_run == -INFINITY ? 0.f : m_run, dma);
     if (__builtin_amdgcn_ballot_w64(!(rs <= kBig) || m_run == -INFINITY) != 0) {
       // rare: move the reference to the tile maximum and redo the tile
@@ -438,9 +452,9 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
     rs_half = 0.f;
     // S_{j+1}: key tile j + 1 of this query tile, or nxt's first
     if constexpr (CAUSAL)
-      mask_causal(sn, kLast ? nxt.q0 : cur.q0, (kLast ? tix(nxt, 0) : tix(cur, j + 1)) * kBc);
+      mask_causal(sn, kLast ? nxt.q0 : cur.q0, (kLast ? tix(nxt, 0) : tix(cur, j + 1)) * kKT);
     using Next = std::integral_constant<bool, !kLast>;
-    phase_b(Next{}, vlane + par * G::kVBytes, pb, sn, m_run == -INFINITY ? 0.f : m_run, rs_half);
+    phase_b(Next{}, vlane + par * kKBytes, pb, sn, m_run == -INFINITY ? 0.f : m_run, rs_half);
     wait_tiles();
     __syncthreads();
   };
@@ -468,7 +482,7 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
   };
   // the new query tile's first score tile: its reference and the
   // exponentials computed ahead of iteration 0
-  auto start_tile = [&](const f32x16 (&s)[2]) {
+  auto start_tile = [&](const f32x16 (&s)[NB]) {
 #pragma unroll
     for (int cb = 0; cb < G::kNcb; ++cb) oacc[cb] = f32x16{};
     l_run = 0.f;
@@ -479,29 +493,29 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
     for (int k = 0; k < kPre; ++k) exp_slice(s, pb, m_use, rs_half, k);
   };
 
-  f32x16 sa[2], sb[2];
+  f32x16 sa[NB], sb[NB];
 
   // ---- prologue of the first query tile
   {
     const Item c0 = item(0);
 #pragma unroll
     for (int i = 0; i < kQCopies; ++i) q_copy(c0, i);
-    const uint8_t* k0 = uniform_ptr(c0.k + tix(c0, 0) * kBc * ksn);
-    const uint8_t* v0 = uniform_ptr(c0.v + tix(c0, 0) * kBc * vsn);
+    const uint8_t* k0 = uniform_ptr(c0.k + tix(c0, 0) * kKT * ksn);
+    const uint8_t* v0 = uniform_ptr(c0.v + tix(c0, 0) * kKT * vsn);
 #pragma unroll
-    for (int i = 0; i < G::kDmaPerWave; ++i) dma_k(k0, kbuf, i);
+    for (int i = 0; i < kDmaPerWave; ++i) dma_k(k0, kbuf, i);
 #pragma unroll
-    for (int i = 0; i < G::kDmaPerWave; ++i) dma_v(v0, vbuf, i);
-    const uint8_t* k1 = uniform_ptr(c0.k + tix(c0, 1) * kBc * ksn);
+    for (int i = 0; i < kDmaPerWave; ++i) dma_v(v0, vbuf, i);
+    const uint8_t* k1 = uniform_ptr(c0.k + tix(c0, 1) * kKT * ksn);
 #pragma unroll
-    for (int i = 0; i < G::kDmaPerWave; ++i) dma_k(k1, kbuf + G::kKBytes, i);
+    for (int i = 0; i < kDmaPerWave; ++i) dma_k(k1, kbuf + kKBytes, i);
     // the Q rows and K_0 (the oldest copies; they complete in issue order):
     // V_0 and K_1 may land while S_0 is computed
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * G::kDmaPerWave) : "memory");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kDmaPerWave) : "memory");
     __syncthreads();
     q_from_lds();
     qk_plain(klane, sa);
-    if constexpr (CAUSAL) mask_causal(sa, c0.q0, tix(c0, 0) * kBc);
+    if constexpr (CAUSAL) mask_causal(sa, c0.q0, tix(c0, 0) * kKT);
     // iteration 0 reads V_0 and K_1 and overwrites K buffer 0: every
     // wavefront's copies have landed and every one is done with K_0
     wait_tiles();
@@ -554,12 +568,11 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
   }
 }
 
-template <int D, bool CAUSAL, bool LOCAL>
+template <int D, int NB, bool CAUSAL, bool LOCAL>
 hipError_t launch_stream_d(const FwdParams& p, const TileMap& tm, int grid, hipStream_t stream) {
-  using G = Geo<D, 8>;
-  constexpr int kSmemAll = G::kSmem + 8 * 32 * 2 * D;  // K/V double buffers + Q/O rows
+  constexpr int kSmemAll = 4 * (32 * NB) * D * 2 + 8 * 32 * 2 * D;  // K/V double buffers + Q/O rows
   static bool attr_set = false;  // benign race: every caller sets the same value
-  auto kern = fwd_bf16_stream_kernel<D, CAUSAL, LOCAL>;
+  auto kern = fwd_bf16_stream_kernel<D, NB, CAUSAL, LOCAL>;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kSmemAll);
@@ -570,17 +583,20 @@ hipError_t launch_stream_d(const FwdParams& p, const TileMap& tm, int grid, hipS
   return hipGetLastError();
 }
 
+template <int D, int NB>
+hipError_t launch_stream_mask(const FwdParams& p, const TileMap& tm, int grid, hipStream_t s) {
+  return p.local ? launch_stream_d<D, NB, true, true>(p, tm, grid, s)
+                 : p.causal ? launch_stream_d<D, NB, true, false>(p, tm, grid, s)
+                            : launch_stream_d<D, NB, false, false>(p, tm, grid, s);
+}
+
 }  // namespace
 
-hipError_t launch_bf16_stream(const FwdParams& p, const TileMap& tm, int d, int grid, hipStream_t s) {
-  if (d == 128)
-    return p.local ? launch_stream_d<128, true, true>(p, tm, grid, s)
-                   : p.causal ? launch_stream_d<128, true, false>(p, tm, grid, s)
-                              : launch_stream_d<128, false, false>(p, tm, grid, s);
-  if (d == 64)
-    return p.local ? launch_stream_d<64, true, true>(p, tm, grid, s)
-                   : p.causal ? launch_stream_d<64, true, false>(p, tm, grid, s)
-                              : launch_stream_d<64, false, false>(p, tm, grid, s);
+hipError_t launch_bf16_stream(const FwdParams& p, const TileMap& tm, int d, int key_tile, int grid,
+                              hipStream_t s) {
+  if (d == 128 && key_tile == 64) return launch_stream_mask<128, 2>(p, tm, grid, s);
+  if (d == 64 && key_tile == 64) return launch_stream_mask<64, 2>(p, tm, grid, s);
+  if (d == 64 && key_tile == 128 && !p.causal) return launch_stream_d<64, 4, false, false>(p, tm, grid, s);
   return hipErrorInvalidValue;
 }
 

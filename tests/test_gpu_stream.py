@@ -44,7 +44,7 @@ CASES = [
     (2, 96, 96, 1000, 1024, 128),    # 768 tiles: 3 per workgroup, ragged last tile
     (3, 68, 17, 700, 512, 64),       # grouped heads (4 per K/V head), 612 tiles
     (2, 101, 101, 1024, 896, 128),   # 808 tiles: 3 or 4 per workgroup, Nk = 14 tiles
-    (1, 128, 128, 1300, 2048, 64),   # Nq > multiple of 256, long keys
+    (1, 128, 128, 1300, 2048, 64),   # Nq > multiple of 256, long keys (128-key tiles)
 ]
 
 
