@@ -118,9 +118,11 @@ int launch_fwd_bf16(const FwdParams& p_in, int d, void* stream) {
     tm.batch_inner = 0;
   }
   if (varlen) {
-    // groups of query tiles dealt round-robin over the XCDs (decode_tile)
+    // groups of query tiles dealt round-robin over the XCDs (decode_tile),
+    // longest sequences first when they can be ranked in one wavefront
     const int64_t groups = (int64_t)p.B * p.H;
     tm.per_xcd = (int)((groups + 7) / 8 * tm.n_qtiles);
+    tm.rank_seq = p.B <= 64 ? 1 : 0;
   }
   // d = 64 biased kernels stage each wave's 32 bias rows in LDS by DMA when
   // every row start is 16-byte aligned, whole 4-key chunks cover the keys,

@@ -314,6 +314,26 @@ __global__ __launch_bounds__(64 * W, 2) void fwd_bf16_kernel(FwdParams p, TileMa
   } else if (!decode_tile<SPLIT, VARLEN>(tm, p.B, packed ? p.Hk : p.H, b, h, qt, split)) {
     return;
   }
+  if (VARLEN && tm.rank_seq) {
+    // packed sequences: decode_tile's sequence index is a rank; the
+    // sequences are ranked by query x key length (ties by index), so the
+    // longest ones start first and the shorter ones fill in behind them
+    // (a list-scheduling model of the packed workload: 1.12x the ideal
+    // time in sequence order, 1.03x longest first)
+    const int ln = threadIdx.x & 63;
+    float wl = -1.f;
+    if (ln < p.B) {
+      const int a0 = min(max(p.cu_q[ln], 0), p.Nq), a1 = min(max(p.cu_q[ln + 1], a0), p.Nq);
+      const int c0 = min(max(p.cu_k[ln], 0), p.Nk), c1 = min(max(p.cu_k[ln + 1], c0), p.Nk);
+      wl = (float)(a1 - a0) * (float)(c1 - c0);
+    }
+    int rank = 0;
+    for (int j = 0; j < p.B; ++j) {
+      const float wj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), j));
+      rank += (wj > wl || (wj == wl && j < ln)) ? 1 : 0;
+    }
+    b = (int)__builtin_ctzll(__builtin_amdgcn_ballot_w64(ln < p.B && rank == b));
+  }
 
   for (int item = 0; item < (kPairable ? 2 : 1); ++item) {
   if (item == 1) {

@@ -133,6 +133,8 @@ struct TileMap {
                          // lengths): pairs per (head, query tile), the
                          // workgroup of pair r runs the batches of key-length
                          // rank r and B-1-r; total = H * n_qtiles * pairs
+  int32_t rank_seq;      // 1: packed sequences (B <= 64) dealt in decreasing
+                         // order of query x key length
 };
 
 // Number of flat heads to deal together so that one XCD's resident
