@@ -239,7 +239,8 @@ def bench_varlen(args, w):
                    "padded_ms_per_step": round(ms_padded, 4),
                    "speedup_vs_padded": round(ms_padded / ms, 3), "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": None},
+                     "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
+                     "traffic": _traffic(w.name, w.dtype)},
         "cpu_baseline": cpu, "clock_settle": args.clock_settle,
     }
     print(json.dumps(out), flush=True)
