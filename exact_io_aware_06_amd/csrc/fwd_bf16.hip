@@ -44,10 +44,25 @@ static int device_cus() {
   return cached[dev];
 }
 
+// Packed sequences take the persistent form (64-key tiles) with no window,
+// at most 64 sequences, H a multiple of 8 (H/8 heads of every sequence per
+// XCD), at most 2048 query tiles per head (B * ceil(max_q / 256)), at least
+// 64 keys in all (a sequence's last key tile is read shifted inside the
+// packed keys) and rows in reach of 32-bit copy offsets.
+static int stream_grid_varlen(const FwdParams& p, int kt) {
+  if (kt != 64 || p.local || p.bias != nullptr || p.kv_len != nullptr || p.n_split > 1) return 0;
+  if (p.B < 1 || p.B > 64 || p.H < 8 || p.H % 8 != 0 || p.Nk < 64 || p.max_q < 1) return 0;
+  if ((int64_t)p.B * ((p.max_q + 255) / 256) > 2048) return 0;
+  for (int64_t sn : {p.q_sn, p.k_sn, p.v_sn})
+    if (64 * sn * 2 >= ((int64_t)1 << 31)) return 0;
+  const int cus = device_cus();
+  return cus % 8 == 0 ? cus : 0;
+}
+
 // The persistent form (fwd_bf16_stream.hip), 256-row query tiles and one
 // workgroup per compute unit, streams key tiles of kt keys (64, or 128 at
-// d = 64). It applies with no bias, key lengths, key split or packed
-// sequences, when every key tile is full and they come in pairs (Nk a
+// d = 64). Unpacked, it applies with no bias, key lengths or key split,
+// when every key tile is full and they come in pairs (Nk a
 // multiple of 2 kt), rows are in reach of 32-bit copy offsets and there are
 // at least two query tiles per compute unit. Dense query tiles host the next
 // one's Q copy during their first key tiles and need at least 14 of them at
@@ -56,7 +71,8 @@ static int device_cus() {
 // (whole heads per XCD); windows need Nk >= Nq; short causal and window
 // tiles copy at once. Returns the grid, or 0.
 static int stream_grid(const FwdParams& p, int d, int kt) {
-  if (p.n_split > 1 || p.cu_q != nullptr || p.bias != nullptr || p.kv_len != nullptr) return 0;
+  if (p.cu_q != nullptr) return stream_grid_varlen(p, kt);
+  if (p.n_split > 1 || p.bias != nullptr || p.kv_len != nullptr) return 0;
   if (p.Nk % (2 * kt) != 0 || 64 * p.q_sn * 2 >= ((int64_t)1 << 31)) return 0;
   const int cus = device_cus();
   if (cus % 8 != 0) return 0;
@@ -132,7 +148,7 @@ int launch_fwd_bf16(const FwdParams& p_in, int d, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (const int kt = stream_key_tile(p, d), grid = stream_grid(p, d, kt); grid > 0) {
     TileMap ts{};
-    ts.n_qtiles = (int)((p.Nq + 255) / 256);
+    ts.n_qtiles = (int)(((varlen ? p.max_q : p.Nq) + 255) / 256);
     ts.total = (int)((int64_t)p.B * p.H * ts.n_qtiles);
     ts.per_xcd = (ts.total + 7) / 8;
     return (int)launch_bf16_stream(p, ts, d, kt, grid, s);

@@ -1,6 +1,7 @@
 // bf16 forward, persistent ("stream") form for problems with no bias, key
 // lengths or key split, every key tile full (Nk a multiple of 128): dense,
-// causal with the diagonal on key-tile pairs, or a sliding window.
+// causal with the diagonal on key-tile pairs, or a sliding window; and for
+// packed variable-length sequences (dense or causal, per sequence).
 //
 // Same arithmetic as fwd_bf16_kernel.h (transposed scores S^T = K Q^T with
 // v_mfma_f32_32x32x16_bf16, base-2 exponentials against an overflow-checked
@@ -60,16 +61,35 @@
 // (-inf) and the overflow check's rare path sets it at the first tile it
 // sees.
 
+//
+// Packed sequences ("flash-attention", Part II, variable-length batches):
+// the work list of (sequence, head, query tile) is built in LDS by every
+// workgroup at its start (longest tiles first, ranked in closed form), XCD
+// x takes heads x H/8 .. (x + 1) H/8 - 1 of every sequence, and its
+// workgroups deal the list greedily by the work they already hold. Key
+// tiles are a sequence's own keys in 64-key steps; the last one, read
+// shifted to end inside the packed keys, is masked to the keys it owns.
+
 #include "fwd_bf16_kernel.h"
 
 namespace attn {
 namespace {
 
 // NB: 32-key blocks per key tile (2: 64 keys, 4: 128 keys).
-template <int D, int NB, bool CAUSAL, bool LOCAL>
+// Packed sequences (VARLEN): at most kMaxSeqs sequences and kMaxEntries
+// query tiles of one head in all, listed in LDS behind the K/V and Q/O rows.
+constexpr int kMaxSeqs = 64;
+constexpr int kMaxEntries = 2048;
+constexpr int kGreedyRounds = 16;                 // greedy deal up to this many items per workgroup
+constexpr int kGreedyItems = kGreedyRounds * 64;  // (at most 64 workgroups per XCD)
+constexpr int kSeqTableBytes =
+    24 * kMaxSeqs + 4 * kMaxEntries + 4 * kGreedyItems + 4 * 64 + 4 * (kGreedyRounds + 1) + 16;
+
+template <int D, int NB, bool CAUSAL, bool LOCAL, bool VARLEN>
 __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, TileMap tm) {
   static_assert(CAUSAL || !LOCAL, "a window is a two-sided causal mask");
   static_assert(NB == 2 || NB == 4, "64- or 128-key tiles");
+  static_assert(!VARLEN || (NB == 2 && !LOCAL), "packed sequences: 64-key tiles, no window");
   constexpr int W = 8;
   using G = Geo<D, W>;
   constexpr int kKT = 32 * NB;                  // keys per key tile
@@ -84,6 +104,7 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
   constexpr int kRowsPerKB = 1024 / kRowBytes;  // rows per 1 KB (4 or 8)
   constexpr int kDrainIters = (kQCopies + 1) / 2;  // O copied out, 2 per iteration
   constexpr int kQ0 = kDrainIters;              // first iteration copying the next Q
+  constexpr int kSmemRows = kSmemKV + W * kQWave;  // K/V buffers and Q/O rows
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
   const int tid = threadIdx.x;
@@ -99,10 +120,92 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
   // sorted longest first.
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, wpx = gridDim.x >> 3;
   const int base_logical = xcd * tm.per_xcd + slot;
-  const int hpx = (p.B * p.H) >> 3;   // causal: heads per XCD
+  // heads per XCD: causal, of the B*H (batch, head) pairs; packed sequences,
+  // of the H heads (XCD x takes heads x H/8 .. (x + 1) H/8 - 1 of every
+  // sequence, so every XCD gets the same work)
+  const int hpx = VARLEN ? (p.H >> 3) : ((p.B * p.H) >> 3);
+
+  // Packed sequences: every workgroup lists the query tiles (b, t) of one
+  // head, t < min(ceil(rows_b / 256), tm.n_qtiles), longest first, in LDS:
+  // seq[b] = (rows, keys, tiles) and sbase[b] = (first row, first key) of
+  // sequence b, ent[r] = t * 64 + b for the tile of rank r, icost[i] the
+  // work of item i of the XCD's (tile, head) list in half key tiles. A
+  // tile's length is the number of 64-key tiles its rows see; it is
+  // non-decreasing in t within a sequence, so the tiles of sequence b'
+  // longer than v are a closed-form count (cnt_gt), and a tile's rank (by
+  // length descending, then sequence ascending, then t descending) is a sum
+  // of such counts over the sequences.
+  int4* const seq = reinterpret_cast<int4*>(smem + kSmemRows);
+  int2* const sbase = reinterpret_cast<int2*>(smem + kSmemRows + 16 * kMaxSeqs);
+  int* const ent = reinterpret_cast<int*>(smem + kSmemRows + 24 * kMaxSeqs);
+  int* const icost = ent + kMaxEntries;
+  int* const gkey = icost + kGreedyItems;   // greedy deal: the workgroups' keys (16-byte aligned)
+  int* const mine = gkey + 64;              // greedy deal: this workgroup's items, then their count
+  int* const nent = mine + kGreedyRounds + 1;
+  int n_ent = 0;
+  if constexpr (VARLEN) {
+    const int tid0 = threadIdx.x;
+    const int nqt = tm.n_qtiles;
+    if (tid0 < 64) {
+      // one wavefront (B <= 64): the sequences, and their tiles in all
+      int nq = 0;
+      if (tid0 < p.B) {
+        const int a0 = min(max(p.cu_q[tid0], 0), p.Nq), a1 = min(max(p.cu_q[tid0 + 1], a0), p.Nq);
+        const int c0 = min(max(p.cu_k[tid0], 0), p.Nk), c1 = min(max(p.cu_k[tid0 + 1], c0), p.Nk);
+        const int lq = a1 - a0;
+        nq = min((lq >> 8) + ((lq & 255) != 0 ? 1 : 0), nqt);
+        seq[tid0] = make_int4(lq, c1 - c0, nq, 0);
+        sbase[tid0] = make_int2(a0, c0);
+      }
+      int tot = nq;
+#pragma unroll
+      for (int dd = 32; dd >= 1; dd >>= 1) tot += __shfl_xor(tot, dd, 64);
+      if (tid0 == 0) nent[0] = tot;
+    }
+    __syncthreads();
+    n_ent = __builtin_amdgcn_readfirstlane(nent[0]);
+    // 64-key tiles seen by the rows of tile t (all keys without a mask)
+    auto length = [&](int lq, int lk, int t) {
+      int kv = lk;
+      if (CAUSAL) kv = min(lk, min(kBr * (t + 1), lq) + (lk - lq));
+      return (max(kv, 0) + kKT - 1) / kKT;
+    };
+    // tiles of a sequence longer than v (v >= -1)
+    auto cnt_gt = [&](const int4& sq, int v) {
+      if (v < 0) return sq.z;
+      if (sq.y <= kKT * v) return 0;
+      if (!CAUSAL) return sq.z;
+      return max(0, sq.z - max(0, (kKT * v - (sq.y - sq.x)) >> 8));
+    };
+    for (int e = tid0; e < p.B * nqt; e += 512) {
+      const int b = e / nqt, t = e - b * nqt;
+      const int4 sb = seq[b];
+      if (t >= sb.z) continue;
+      const int v = length(sb.x, sb.y, t);
+      int rank = sb.z - 1 - t - cnt_gt(sb, v);
+#pragma unroll 8
+      for (int b2 = 0; b2 < p.B; ++b2) {
+        const int4 s2 = seq[b2];
+        const int g = cnt_gt(s2, v);
+        rank += g + (b2 < b ? cnt_gt(s2, v - 1) - g : 0);
+      }
+      ent[rank] = (t << 6) | b;
+      // its work: the key tiles it runs (even, at least 2) plus about 2.5
+      // tiles of start and diagonal (measured), in half tiles
+      const int cost = 2 * max(2, v + (v & 1)) + 5;
+      for (int h = 0; h < hpx; ++h)
+        if (rank * hpx + h < kGreedyItems) icost[rank * hpx + h] = cost;
+    }
+    __syncthreads();
+  }
+
   int n_items;
-  if constexpr (CAUSAL && !LOCAL) {
-    const int n_x = hpx * tm.n_qtiles;
+  // packed sequences with at most kGreedyRounds items per workgroup: a
+  // greedy deal (below), else the alternating one
+  const int n_xv = hpx * n_ent;
+  const bool greedy = VARLEN && wpx <= 64 && n_xv <= kGreedyRounds * wpx;
+  if constexpr (VARLEN || (CAUSAL && !LOCAL)) {
+    const int n_x = hpx * (VARLEN ? n_ent : tm.n_qtiles);
     const int rounds = n_x / wpx, rem = n_x % wpx;
     n_items = rounds + (((rounds & 1) ? wpx - 1 - slot : slot) < rem ? 1 : 0);
   } else {
@@ -114,7 +217,7 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
   const int Nq = p.Nq, Nk = p.Nk;
   const int off = Nk - Nq;   // the diagonal: key i + off for query i
   const int64_t ksn = p.k_sn * 2, vsn = p.v_sn * 2;  // row strides in bytes
-  struct Item {
+  struct ItemBase {
     const uint8_t* q;   // row q0 + 32 * wave (clamped to the last row) of Q
     const uint8_t* k;   // key 0 of K
     const uint8_t* v;   // key 0 of V
@@ -125,7 +228,46 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
     int kb;             // window: its first key tile
     int rot;            // window: step 0 visits key tile kb + rot
   };
+  struct ItemSeq : ItemBase {
+    int lq, lk;         // packed: the sequence's query rows and keys
+    int kmin;           // packed: minus the sequence's first key
+  };
+  using Item = std::conditional_t<VARLEN, ItemSeq, ItemBase>;
   auto item = [&](int it) {
+    if constexpr (VARLEN) {
+      Item r;
+      // rank i of this XCD's (tile, head) list: the tile of rank i / hpx,
+      // head xcd * hpx + i % hpx (the first item is rank `slot` in both deals)
+      const int i = greedy ? (it == 0 ? slot : __builtin_amdgcn_readfirstlane(mine[it]))
+                           : it * wpx + ((it & 1) ? wpx - 1 - slot : slot);
+      const int e = __builtin_amdgcn_readfirstlane(ent[i / hpx]);
+      const int b = e & 63, h = xcd * hpx + i % hpx;
+      const int hk = h / p.head_group;
+      const int4 sq = seq[b];
+      const int2 sbb = sbase[b];
+      const int q_lo = __builtin_amdgcn_readfirstlane(sbb.x), k_lo = __builtin_amdgcn_readfirstlane(sbb.y);
+      r.lq = __builtin_amdgcn_readfirstlane(sq.x);
+      r.lk = __builtin_amdgcn_readfirstlane(sq.y);
+      r.kmin = -k_lo;
+      r.q0 = (e >> 6) * kBr;
+      r.kb = 0;
+      r.rot = 0;
+      // key tiles its rows see, made even and at least 2 (the extra tile,
+      // placed inside the sequence's keys, is masked whole)
+      const int kv = CAUSAL ? min(r.lk, min(r.q0 + kBr, r.lq) + (r.lk - r.lq)) : r.lk;
+      const int nraw = (max(kv, 0) + kKT - 1) / kKT;
+      r.nt = max(2, nraw + (nraw & 1));
+      const int wrow = min(r.q0 + 32 * wave, r.lq - 1);
+      r.q = uniform_ptr(reinterpret_cast<const uint8_t*>(static_cast<const __bf16*>(p.q) + h * p.q_sh +
+                                                         (int64_t)(q_lo + wrow) * p.q_sn));
+      r.k = uniform_ptr(reinterpret_cast<const uint8_t*>(static_cast<const __bf16*>(p.k) + hk * p.k_sh +
+                                                         (int64_t)k_lo * p.k_sn));
+      r.v = uniform_ptr(reinterpret_cast<const uint8_t*>(static_cast<const __bf16*>(p.v) + hk * p.v_sh +
+                                                         (int64_t)k_lo * p.v_sn));
+      r.o = static_cast<__bf16*>(p.o) + (int64_t)q_lo * p.o_sn + h * p.o_sh;
+      r.lse = p.lse + q_lo + h * p.l_sh;
+      return r;
+    }
     int qt, hb;
     if constexpr (CAUSAL && !LOCAL) {
       const int i = it * wpx + ((it & 1) ? wpx - 1 - slot : slot);
@@ -179,6 +321,20 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
       return t;
     }
   };
+  // first key of the tile read at step t. Packed sequences: tile t holds
+  // the sequence's keys [64 t, 64 t + 64) that exist; a tile reaching past
+  // the last key is read shifted to end there (or, for a sequence of fewer
+  // than 64 keys, to start at key 0 of the packed tensor), and the keys it
+  // reads outside its own range are masked, so no copy leaves the tensors.
+  // query rows of the tile's (batch, head) or sequence
+  auto rows = [&](const Item& it) {
+    if constexpr (VARLEN) return it.lq;
+    else return Nq;
+  };
+  auto kpos = [&](const Item& it, int t) {
+    if constexpr (VARLEN) return max(min(kKT * t, it.lk - kKT), it.kmin);
+    else return tix(it, t) * kKT;
+  };
 
   uint8_t* const kbuf = smem;                    // K tile t in buffer t % 2
   uint8_t* const vbuf = smem + 2 * kKBytes;      // V tile t in buffer t % 2
@@ -206,7 +362,8 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
     const int ln = fresh(lane);
     const int r = i * kRowsPerKB + ln / kC;
     const int wrow0 = it.q0 + 32 * wave;
-    const int rel = max(min(wrow0 + r, Nq - 1) - min(wrow0, Nq - 1), 0);
+    const int lq = rows(it);
+    const int rel = max(min(wrow0 + r, lq - 1) - min(wrow0, lq - 1), 0);
     const int chunk = (ln % kC) ^ (r % kC);
     dma16(it.q, (uint32_t)(rel * (int)(p.q_sn * 2) + 16 * chunk), qw + 1024 * i);
   };
@@ -368,6 +525,29 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
     }
   };
 
+  // packed sequences: the scores of tile t of `it` outside its own keys
+  // [64 t, min(64 t + 64, keys)), or (causal) of keys past the row's
+  // diagonal (key > row + keys - rows), become -inf
+  auto mask_seq = [&](f32x16 (&s)[NB], const Item& it, int t) {
+    if constexpr (VARLEN) {
+      const int pos = kpos(it, t);
+      const int klo = kKT * t, khi = min(klo + kKT, it.lk);
+      const int qmin = it.q0 + 32 * wave;
+      const int offr = it.lk - it.lq;
+      const bool right = CAUSAL && pos + kKT - 1 > qmin + offr;
+      if (pos < klo || pos + kKT > khi || right) {
+        const int row = qmin + l32;
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = pos + 32 * bb + 16 * (r >> 3) + 8 * hi + (r & 7);
+            if (key < klo || key >= khi || (CAUSAL && key > row + offr)) s[bb][r] = -INFINITY;
+          }
+      }
+    }
+  };
+
   // 1 KB piece i of the previous query tile's O, from this wavefront's LDS
   // rows to HBM (rows i * kRowsPerKB + lane / kC, whole 16-byte chunks)
   auto drain = [&](const Item& prv, int i) {
@@ -375,7 +555,7 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
     const int r = i * kRowsPerKB + ln / kC;
     const u32x4 x = *reinterpret_cast<const u32x4*>(qw + 1024 * i + 16 * ln);
     const int row = prv.q0 + 32 * wave + r;
-    if (row < Nq) {
+    if (row < rows(prv)) {
       const int chunk = (ln % kC) ^ (r % kC);
       *reinterpret_cast<u32x4*>(reinterpret_cast<uint8_t*>(prv.o + (int64_t)row * p.o_sn) + 16 * chunk) = x;
     }
@@ -414,10 +594,10 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
     // past this query tile's keys they are nxt's first ones
     const int nt = cur.nt;
     auto ktile = [&](int t) {
-      return t < nt ? cur.k + tix(cur, t) * kKT * ksn : nxt.k + tix(nxt, t - nt) * kKT * ksn;
+      return t < nt ? cur.k + kpos(cur, t) * ksn : nxt.k + kpos(nxt, t - nt) * ksn;
     };
     auto vtile = [&](int t) {
-      return t < nt ? cur.v + tix(cur, t) * kKT * vsn : nxt.v + tix(nxt, t - nt) * kKT * vsn;
+      return t < nt ? cur.v + kpos(cur, t) * vsn : nxt.v + kpos(nxt, t - nt) * vsn;
     };
     const uint8_t* const kt = uniform_ptr(ktile(j + 2));
     const uint8_t* const vt = uniform_ptr(vtile(j + 1));
@@ -451,8 +631,12 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
     l_run += rs;
     rs_half = 0.f;
     // S_{j+1}: key tile j + 1 of this query tile, or nxt's first
-    if constexpr (CAUSAL)
+    if constexpr (VARLEN) {
+      if constexpr (kLast) mask_seq(sn, nxt, 0);
+      else mask_seq(sn, cur, j + 1);
+    } else if constexpr (CAUSAL) {
       mask_causal(sn, kLast ? nxt.q0 : cur.q0, (kLast ? tix(nxt, 0) : tix(cur, j + 1)) * kKT);
+    }
     using Next = std::integral_constant<bool, !kLast>;
     phase_b(Next{}, vlane + par * kKBytes, pb, sn, m_run == -INFINITY ? 0.f : m_run, rs_half);
     wait_tiles();
@@ -477,7 +661,7 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
         *reinterpret_cast<bf16x4*>(row + 16 * ((4 * cb + g) ^ sw)) = w;
       }
     const int my_q = it.q0 + 32 * wave + (ln & 31);
-    if ((ln >> 5) == 0 && my_q < Nq)
+    if ((ln >> 5) == 0 && my_q < rows(it))
       it.lse[my_q] = (l_tot > 0.f) ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
   };
   // the new query tile's first score tile: its reference and the
@@ -500,22 +684,59 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
     const Item c0 = item(0);
 #pragma unroll
     for (int i = 0; i < kQCopies; ++i) q_copy(c0, i);
-    const uint8_t* k0 = uniform_ptr(c0.k + tix(c0, 0) * kKT * ksn);
-    const uint8_t* v0 = uniform_ptr(c0.v + tix(c0, 0) * kKT * vsn);
+    const uint8_t* k0 = uniform_ptr(c0.k + kpos(c0, 0) * ksn);
+    const uint8_t* v0 = uniform_ptr(c0.v + kpos(c0, 0) * vsn);
 #pragma unroll
     for (int i = 0; i < kDmaPerWave; ++i) dma_k(k0, kbuf, i);
 #pragma unroll
     for (int i = 0; i < kDmaPerWave; ++i) dma_v(v0, vbuf, i);
-    const uint8_t* k1 = uniform_ptr(c0.k + tix(c0, 1) * kKT * ksn);
+    const uint8_t* k1 = uniform_ptr(c0.k + kpos(c0, 1) * ksn);
 #pragma unroll
     for (int i = 0; i < kDmaPerWave; ++i) dma_k(k1, kbuf + kKBytes, i);
+    if constexpr (VARLEN) {
+      if (greedy && wave == 0) {
+        // Greedy deal of this XCD's items (sorted longest first) while the
+        // copies land: round r hands its wpx items, longest first, to the
+        // workgroups in order of the work they hold (least first, ties by
+        // slot). Lane s is workgroup slot s; every workgroup of the XCD
+        // computes the same deal and keeps its own items.
+        int load = 0, n_mine = 0;
+        const int rounds = (n_xv + wpx - 1) / wpx;
+        const int nk4 = (wpx + 3) >> 2;
+        for (int r = 0; r < rounds; ++r) {
+          const int ir = r * wpx + lane;   // the item of rank `lane` in this round
+          const int c = (lane < wpx && ir < n_xv) ? icost[ir] : 0;
+          const int key = lane < wpx ? (load << 6) | lane : 0x7fffffff;
+          // every lane's key to LDS, then each lane counts the smaller ones
+          // (one wavefront: its LDS accesses complete in order)
+          gkey[lane] = key;
+          int rank = 0;
+#pragma unroll 4
+          for (int q4 = 0; q4 < nk4; ++q4) {
+            const int4 kk = reinterpret_cast<const int4*>(gkey)[q4];
+            rank += (kk.x < key ? 1 : 0) + (kk.y < key ? 1 : 0) + (kk.z < key ? 1 : 0) + (kk.w < key ? 1 : 0);
+          }
+          const int ci = __builtin_amdgcn_ds_bpermute(rank << 2, c);
+          const int ii = r * wpx + rank;
+          if (lane < wpx && ii < n_xv) {
+            load += ci;
+            if (lane == slot) mine[n_mine] = ii;
+            ++n_mine;
+          }
+        }
+        if (lane == slot) mine[kGreedyRounds] = n_mine;
+      }
+    }
     // the Q rows and K_0 (the oldest copies; they complete in issue order):
     // V_0 and K_1 may land while S_0 is computed
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kDmaPerWave) : "memory");
     __syncthreads();
+    if constexpr (VARLEN)
+      if (greedy) n_items = __builtin_amdgcn_readfirstlane(mine[kGreedyRounds]);
     q_from_lds();
     qk_plain(klane, sa);
-    if constexpr (CAUSAL) mask_causal(sa, c0.q0, tix(c0, 0) * kKT);
+    if constexpr (VARLEN) mask_seq(sa, c0, 0);
+    else if constexpr (CAUSAL) mask_causal(sa, c0.q0, tix(c0, 0) * kKT);
     // iteration 0 reads V_0 and K_1 and overwrites K buffer 0: every
     // wavefront's copies have landed and every one is done with K_0
     wait_tiles();
@@ -535,7 +756,7 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
     // its start (each drain's LDS read is complete before the copy that
     // overwrites its rows is issued: the store that uses it waits for it).
     bool spread_prev = has_prev, spread_next = has_next;
-    if constexpr (CAUSAL) {
+    if constexpr (CAUSAL || VARLEN) {
       if (nt < kQ0 + kQCopies + 1) {
         if (has_prev) {
 #pragma unroll
@@ -568,11 +789,12 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
   }
 }
 
-template <int D, int NB, bool CAUSAL, bool LOCAL>
+template <int D, int NB, bool CAUSAL, bool LOCAL, bool VARLEN = false>
 hipError_t launch_stream_d(const FwdParams& p, const TileMap& tm, int grid, hipStream_t stream) {
-  constexpr int kSmemAll = 4 * (32 * NB) * D * 2 + 8 * 32 * 2 * D;  // K/V double buffers + Q/O rows
+  // K/V double buffers + Q/O rows (+ the packed sequences' tile list)
+  constexpr int kSmemAll = 4 * (32 * NB) * D * 2 + 8 * 32 * 2 * D + (VARLEN ? kSeqTableBytes : 0);
   static bool attr_set = false;  // benign race: every caller sets the same value
-  auto kern = fwd_bf16_stream_kernel<D, NB, CAUSAL, LOCAL>;
+  auto kern = fwd_bf16_stream_kernel<D, NB, CAUSAL, LOCAL, VARLEN>;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kSmemAll);
@@ -590,10 +812,26 @@ hipError_t launch_stream_mask(const FwdParams& p, const TileMap& tm, int grid, h
                             : launch_stream_d<D, NB, false, false>(p, tm, grid, s);
 }
 
+template <int D>
+hipError_t launch_stream_varlen(const FwdParams& p, const TileMap& tm, int grid, hipStream_t s) {
+  return p.causal ? launch_stream_d<D, 2, true, false, true>(p, tm, grid, s)
+                  : launch_stream_d<D, 2, false, false, true>(p, tm, grid, s);
+}
+
 }  // namespace
 
 hipError_t launch_bf16_stream(const FwdParams& p, const TileMap& tm, int d, int key_tile, int grid,
                               hipStream_t s) {
+  if (p.cu_q != nullptr) {
+    // packed sequences: 64-key tiles, no window, B <= 64, B * n_qtiles
+    // query tiles per head at most kMaxEntries
+    if (key_tile != 64 || p.local || p.B < 1 || p.B > kMaxSeqs ||
+        (int64_t)p.B * tm.n_qtiles > kMaxEntries || p.H < 8 || p.H % 8 != 0 || p.Nk < 64)
+      return hipErrorInvalidValue;
+    if (d == 128) return launch_stream_varlen<128>(p, tm, grid, s);
+    if (d == 64) return launch_stream_varlen<64>(p, tm, grid, s);
+    return hipErrorInvalidValue;
+  }
   if (d == 128 && key_tile == 64) return launch_stream_mask<128, 2>(p, tm, grid, s);
   if (d == 64 && key_tile == 64) return launch_stream_mask<64, 2>(p, tm, grid, s);
   if (d == 64 && key_tile == 128 && !p.causal) return launch_stream_d<64, 4, false, false>(p, tm, grid, s);

@@ -76,6 +76,63 @@ def test_varlen_matches_oracle(lens_q, lens_k, H, Hk, d, dtype, causal):
             f"varlen {lens_q}")
 
 
+# Packed sequences with H a multiple of 8, at most 64 sequences and at least
+# 64 keys in all take the persistent kernel (one workgroup per compute unit
+# walking a longest-first list of (sequence, head, query tile) built on the
+# device, 64-key tiles read shifted at a sequence's end and masked to the
+# sequence's own keys). Cases: empty, one-row and sub-64-key sequences, a
+# sequence without keys, more queries than keys (rows that see no key),
+# grouped K/V heads, many short sequences, long ones of several query tiles.
+PERSISTENT_CASES = [
+    # (lens_q, lens_k, H, Hk, d, causal)
+    ([300, 1, 0, 513, 64, 1000], None, 8, 8, 128, True),
+    ([300, 1, 0, 513, 64, 1000], None, 8, 8, 64, False),
+    ([257, 700, 5], None, 16, 2, 128, True),
+    ([17, 200], [90, 650], 8, 8, 64, True),
+    ([40, 3, 100], [10, 0, 80], 8, 8, 128, False),
+    ([40, 3, 100], [10, 0, 80], 8, 4, 64, True),
+    ([300, 200, 129], [100, 250, 129], 8, 8, 128, True),
+    ([2100, 1300, 64, 65, 777], None, 8, 2, 128, True),
+    ([2100, 1300, 64, 65, 777], None, 8, 8, 64, False),
+    ([5, 61, 130, 255, 256, 257, 1, 90, 300, 12, 44, 199, 63, 64, 65, 511, 512, 513, 7, 100,
+      20, 380, 3, 33, 250], None, 8, 8, 64, True),
+    ([5, 61, 130, 255, 256, 257, 1, 90, 300, 12, 44, 199, 63, 64, 65, 511, 512, 513, 7, 100,
+      20, 380, 3, 33, 250], [64, 10, 130, 700, 0, 257, 1, 90, 300, 500, 44, 199, 63, 64, 65,
+                             511, 100, 513, 7, 100, 20, 380, 3, 33, 250], 8, 8, 128, False),
+]
+
+
+@pytest.mark.parametrize("lens_q,lens_k,H,Hk,d,causal", PERSISTENT_CASES)
+def test_varlen_persistent_matches_oracle(lens_q, lens_k, H, Hk, d, causal):
+    lens_k = lens_q if lens_k is None else lens_k
+    _banner(f"varlen persistent q={lens_q} k={lens_k} H={H} Hk={Hk} d={d} causal={causal}")
+    q, k, v, cu_q, cu_k = _packed(lens_q, lens_k, H, Hk, d, "bf16", seed=3 * sum(lens_q) + d)
+    T = q.shape[0]
+    out = torch.full((T, H, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((H, T), float("nan"), dtype=torch.float32, device="cuda")
+    o, lse = _run(q, k, v, cu_q, cu_k, max(lens_q), causal, out=out, lse=lse)
+    ro, rl = oracle.attention_varlen(q.double().numpy(), k.double().numpy(), v.double().numpy(),
+                                     cu_q.numpy(), cu_k.numpy(), scale=d ** -0.5, causal=causal)
+    compare(o.double().cpu().numpy(), lse.double().cpu().numpy().T, ro, rl.T, "bf16",
+            f"varlen persistent {lens_q}")
+
+
+def test_varlen_persistent_offsets_outside_tensors_are_clamped():
+    # the clamped-offsets case of the per-tile kernel, with 8 heads (the
+    # persistent kernel): [0, 120), an empty sequence and [80, 200)
+    q, k, v, _, _ = _packed([200], [200], 8, 8, 128, "bf16", seed=64)
+    cu = torch.tensor([-7, 120, 80, 1 << 30], dtype=torch.int32)
+    o, l = _run(q, k, v, cu, cu, 256, True)
+    oc, lc = o.cpu().double().numpy(), l.cpu().double().numpy().T
+    assert not np.isnan(oc).any()
+    f = lambda t: t.double().numpy()
+    for lo, hi, keep in ((0, 120, np.r_[0:80]), (80, 200, np.r_[120:200])):
+        ro, rl = oracle.attention_varlen(f(q), f(k), f(v), np.array([lo, hi]), np.array([lo, hi]),
+                                         scale=128 ** -0.5, causal=True)
+        compare(oc[keep], lc[keep], ro[keep], rl.T[keep], "bf16",
+                f"varlen persistent clamped offsets [{lo}, {hi})")
+
+
 def test_varlen_window():
     lens = [900, 77, 600]
     q, k, v, cu_q, cu_k = _packed(lens, lens, 2, 2, 128, "bf16", seed=61)
