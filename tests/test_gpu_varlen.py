@@ -117,6 +117,37 @@ def test_varlen_persistent_matches_oracle(lens_q, lens_k, H, Hk, d, causal):
             f"varlen persistent {lens_q}")
 
 
+@pytest.mark.parametrize("case", ["max_seqs", "alternating_deal", "table_limit", "per_tile_65"])
+def test_varlen_persistent_limits(case):
+    # the persistent form's limits: 64 sequences (the most it takes), more
+    # than 16 items per workgroup (the alternating deal instead of the
+    # greedy one: 64 sequences x 5 query tiles x 2 heads per XCD), the
+    # largest tile list (64 sequences x ceil(8192 / 256) = 2048 entries), and
+    # 65 sequences (the per-tile launch); compared in full
+    r = np.random.default_rng({"max_seqs": 1, "alternating_deal": 2, "table_limit": 3,
+                               "per_tile_65": 4}[case])
+    if case == "max_seqs":
+        lens, H, Hk, d, causal, max_q = list(r.integers(1, 400, 64)), 8, 8, 64, True, None
+    elif case == "alternating_deal":
+        lens, H, Hk, d, causal, max_q = list(r.integers(1030, 1100, 64)), 16, 8, 64, True, None
+    elif case == "table_limit":
+        lens, H, Hk, d, causal, max_q = list(r.integers(1, 90, 64)), 8, 2, 128, False, 8192
+        lens[17] = 1500
+    else:
+        lens, H, Hk, d, causal, max_q = list(r.integers(1, 300, 65)), 8, 8, 128, True, None
+    lens = [int(x) for x in lens]
+    _banner(f"varlen persistent limits {case}: {len(lens)} sequences, {sum(lens)} rows, H={H}")
+    q, k, v, cu_q, cu_k = _packed(lens, lens, H, Hk, d, "bf16", seed=sum(lens))
+    T = q.shape[0]
+    out = torch.full((T, H, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((H, T), float("nan"), dtype=torch.float32, device="cuda")
+    o, lse = _run(q, k, v, cu_q, cu_k, max_q or max(lens), causal, out=out, lse=lse)
+    ro, rl = oracle.attention_varlen(q.double().numpy(), k.double().numpy(), v.double().numpy(),
+                                     cu_q.numpy(), cu_k.numpy(), scale=d ** -0.5, causal=causal)
+    compare(o.double().cpu().numpy(), lse.double().cpu().numpy().T, ro, rl.T, "bf16",
+            f"varlen persistent limits {case}")
+
+
 def test_varlen_persistent_offsets_outside_tensors_are_clamped():
     # the clamped-offsets case of the per-tile kernel, with 8 heads (the
     # persistent kernel): [0, 120), an empty sequence and [80, 200)
