@@ -207,7 +207,10 @@ def bench_varlen(args, w):
         kp[b, :, :n] = k[c[b]:c[b + 1]].transpose(0, 1)
         vp[b, :, :n] = v[c[b]:c[b + 1]].transpose(0, 1)
     kv_len = lens.to(torch.int32).to(dev)
-    step_p, _, _ = ea.prepare_call(qp, kp, vp, kv_len=kv_len, causal=w.causal, scale=inp["scale"])
+    step_p = None
+    if not args.no_padded:
+        step_p, _, _ = ea.prepare_call(qp, kp, vp, kv_len=kv_len, causal=w.causal,
+                                       scale=inp["scale"])
 
     def timed(fn):
         warm_up(fn, args)
@@ -220,7 +223,7 @@ def bench_varlen(args, w):
         return start.elapsed_time(stop) / args.steps
 
     ms = timed(step)
-    ms_padded = timed(step_p)
+    ms_padded = timed(step_p) if step_p is not None else None
     flops = varlen_flops(w, lens)
     tflops = flops / (ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
@@ -236,8 +239,9 @@ def bench_varlen(args, w):
         "dtype": w.dtype, "data": "synthetic",
         "config": {**w.describe(), "total_tokens": int(lens.sum()),
                    "lens": [int(x) for x in lens], "flops_per_step": flops,
-                   "padded_ms_per_step": round(ms_padded, 4),
-                   "speedup_vs_padded": round(ms_padded / ms, 3), "parallelism": "single GPU"},
+                   "padded_ms_per_step": round(ms_padded, 4) if ms_padded else None,
+                   "speedup_vs_padded": round(ms_padded / ms, 3) if ms_padded else None,
+                   "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
                      "traffic": _traffic(w.name, w.dtype)},
@@ -387,6 +391,9 @@ def main(argv=None):
                     help="cold caches: write a 512 MiB buffer before every timed call and "
                          "report the median call (each call timed on its own)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-padded", action="store_true",
+                    help="packed-sequence workloads: skip the padded-batch comparison (so "
+                         "that a profile of the run holds the packed call only)")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a device-to-device copy of MIB mebibytes (the "

@@ -2,7 +2,7 @@
 
     python -m exact_io_aware_06_amd.profsum stats  <kernel_stats.csv> <out.txt> <command...>
     python -m exact_io_aware_06_amd.profsum counters [--kernel SUBSTR] [--last N] <workload> <out.txt> <pmc_dir>... -- <command...>
-    python -m exact_io_aware_06_amd.profsum traffic <workload> <fetch_dir> <write_dir> \
+    python -m exact_io_aware_06_amd.profsum traffic [--kernel SUBSTR] <workload> <fetch_dir> <write_dir> \
         <copy_fetch_dir> <copy_write_dir> <copy_mib> <kernel_src[,src...]> <out.txt> <command...>
 
 `stats` copies the per-kernel duration table. `counters` averages the SQ/GRBM
@@ -143,10 +143,10 @@ def source_sha256(paths):
     return h.hexdigest()
 
 
-def traffic(workload, fdir, wdir, cfdir, cwdir, copy_mib, src, out, cmd):
+def traffic(workload, fdir, wdir, cfdir, cwdir, copy_mib, src, out, cmd, kernel="fwd_"):
     # the forward kernel only (a split launch also runs the merge kernel)
-    fetch, nf = _counter(fdir, "FETCH_SIZE", "fwd_")
-    write, nw = _counter(wdir, "WRITE_SIZE", "fwd_")
+    fetch, nf = _counter(fdir, "FETCH_SIZE", kernel)
+    write, nw = _counter(wdir, "WRITE_SIZE", kernel)
     cfetch, _ = _counter(cfdir, "FETCH_SIZE", "copyBuffer")
     cwrite, _ = _counter(cwdir, "WRITE_SIZE", "copyBuffer")
     copy_kib = float(copy_mib) * 1024.0
@@ -186,6 +186,10 @@ if __name__ == "__main__":
         cut = args.index("--")
         counters(args[0], args[1], args[2:cut], " ".join(args[cut + 1:]), kernel, last)
     elif mode == "traffic":
-        traffic(*sys.argv[2:10], " ".join(sys.argv[10:]))
+        args = sys.argv[2:]
+        kernel = "fwd_"
+        if args[0] == "--kernel":
+            kernel, args = args[1], args[2:]
+        traffic(*args[:8], " ".join(args[8:]), kernel=kernel)
     else:
         raise SystemExit(__doc__)
