@@ -131,8 +131,8 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
   // sequence b, ent[r] = t * 64 + b for the tile of rank r, icost[i] the
   // work of item i of the XCD's (tile, head) list in half key tiles. A
   // tile's length is the number of 64-key tiles its rows see; it is
-  // non-decreasing in t within a sequence, so the tiles of sequence b'
-  // longer than v are a closed-form count (cnt_gt), and a tile's rank (by
+  // non-decreasing in t within a sequence, so the number of tiles of
+  // sequence b' longer than v has a closed form (cnt_gt), and a tile's rank (by
   // length descending, then sequence ascending, then t descending) is a sum
   // of such counts over the sequences.
   int4* const seq = reinterpret_cast<int4*>(smem + kSmemRows);
@@ -144,23 +144,22 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
   int* const nent = mine + kGreedyRounds + 1;
   int n_ent = 0;
   if constexpr (VARLEN) {
-    const int tid0 = threadIdx.x;
     const int nqt = tm.n_qtiles;
-    if (tid0 < 64) {
+    if (tid < 64) {
       // one wavefront (B <= 64): the sequences, and their tiles in all
       int nq = 0;
-      if (tid0 < p.B) {
-        const int a0 = min(max(p.cu_q[tid0], 0), p.Nq), a1 = min(max(p.cu_q[tid0 + 1], a0), p.Nq);
-        const int c0 = min(max(p.cu_k[tid0], 0), p.Nk), c1 = min(max(p.cu_k[tid0 + 1], c0), p.Nk);
+      if (tid < p.B) {
+        const int a0 = min(max(p.cu_q[tid], 0), p.Nq), a1 = min(max(p.cu_q[tid + 1], a0), p.Nq);
+        const int c0 = min(max(p.cu_k[tid], 0), p.Nk), c1 = min(max(p.cu_k[tid + 1], c0), p.Nk);
         const int lq = a1 - a0;
         nq = min((lq >> 8) + ((lq & 255) != 0 ? 1 : 0), nqt);
-        seq[tid0] = make_int4(lq, c1 - c0, nq, 0);
-        sbase[tid0] = make_int2(a0, c0);
+        seq[tid] = make_int4(lq, c1 - c0, nq, 0);
+        sbase[tid] = make_int2(a0, c0);
       }
       int tot = nq;
 #pragma unroll
       for (int dd = 32; dd >= 1; dd >>= 1) tot += __shfl_xor(tot, dd, 64);
-      if (tid0 == 0) nent[0] = tot;
+      if (tid == 0) nent[0] = tot;
     }
     __syncthreads();
     n_ent = __builtin_amdgcn_readfirstlane(nent[0]);
@@ -177,7 +176,7 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
       if (!CAUSAL) return sq.z;
       return max(0, sq.z - max(0, (kKT * v - (sq.y - sq.x)) >> 8));
     };
-    for (int e = tid0; e < p.B * nqt; e += 512) {
+    for (int e = tid; e < p.B * nqt; e += 512) {
       const int b = e / nqt, t = e - b * nqt;
       const int4 sb = seq[b];
       if (t >= sb.z) continue;
