@@ -5,7 +5,9 @@
     python -m exact_io_aware_06_amd.profsum traffic [--kernel SUBSTR] <workload> <fetch_dir> <write_dir> \
         <copy_fetch_dir> <copy_write_dir> <copy_mib> <kernel_src[,src...]> <out.txt> <command...>
 
-`stats` copies the per-kernel duration table. `counters` averages the SQ/GRBM
+`stats` copies the per-kernel duration table and, from the kernel trace
+beside it, adds the busiest kernel's mean over its last 150 dispatches
+(bench.py's timed calls, after the clock-settling ones). `counters` averages the SQ/GRBM
 counters of one kernel (the kernels whose name contains SUBSTR, default
 "fwd_bf16") over its dispatches and derives MFMA busy
 fraction (per SIMD, from SQ_VALU_MFMA_BUSY_CYCLES over 1024 SIMDs and the
@@ -39,7 +41,7 @@ def _counter(d, name, kernel_substr):
     return sum(vals) / len(vals), len(vals)
 
 
-def stats(src, out, cmd):
+def stats(src, out, cmd, last=150):
     rows = list(csv.DictReader(open(src)))
     with open(out, "w") as f:
         f.write(f"# rocprofv3 --kernel-trace --stats summary\n# command: {cmd}\n")
@@ -48,6 +50,20 @@ def stats(src, out, cmd):
             f.write(f"{r['Name']} | {r['Calls']} | {float(r['AverageNs'])/1e3:.1f} | "
                     f"{float(r['MinNs'])/1e3:.1f} | {float(r['MaxNs'])/1e3:.1f} | "
                     f"{float(r['Percentage']):.2f}\n")
+        # the kernel trace beside the stats: the busiest kernel over its last
+        # `last` dispatches (bench.py's 100 timed and 50 single-timed calls,
+        # after the clock-settling and warm-up calls, whose clocks still ramp)
+        trace = os.path.join(os.path.dirname(src), os.path.basename(src).replace(
+            "kernel_stats.csv", "kernel_trace.csv"))
+        if rows and os.path.exists(trace):
+            name = rows[0]["Name"]
+            d = [(int(t["End_Timestamp"]) - int(t["Start_Timestamp"])) / 1e3
+                 for t in csv.DictReader(open(trace)) if t["Kernel_Name"] == name]
+            if len(d) > last:
+                tail = sorted(d[-last:])
+                f.write(f"# {name}: mean of the last {last} dispatches {sum(tail) / last:.1f} us, "
+                        f"median {tail[last // 2]:.1f} us ({len(d) - last} earlier dispatches "
+                        f"excluded; all {len(d)}: mean {sum(d) / len(d):.1f} us)\n")
 
 
 def _durations_ns(d, kernel):
