@@ -99,6 +99,8 @@ PERSISTENT_CASES = [
     ([5, 61, 130, 255, 256, 257, 1, 90, 300, 12, 44, 199, 63, 64, 65, 511, 512, 513, 7, 100,
       20, 380, 3, 33, 250], [64, 10, 130, 700, 0, 257, 1, 90, 300, 500, 44, 199, 63, 64, 65,
                              511, 100, 513, 7, 100, 20, 380, 3, 33, 250], 8, 8, 128, False),
+    ([700, 33, 1200], [900, 33, 1000], 8, 1, 128, True),    # one K/V head for all
+    ([700, 33, 1200], None, 16, 1, 64, False),
 ]
 
 
