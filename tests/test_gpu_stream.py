@@ -198,3 +198,84 @@ def test_stream_strided_views_and_determinism():
 
     rows = tile_rows(B, H, N, 72) + head_rows(1, 77, N)
     compare_rows(o_c, lse_c, rows, oracle_rows, "bf16", "stream strided")
+
+
+def _random_stream_cases(n, seed):
+    """Seeded shapes that meet the persistent form's conditions: at least
+    two 256-row query tiles per compute unit (512 on MI355X's 256 CUs), key
+    counts a multiple of 128; causal: Nk - Nq a multiple of 128 and B*H a
+    multiple of 8; windows: Nk >= Nq. Tile counts per workgroup, ragged
+    query tiles, diagonal offsets and band widths vary from case to case."""
+    r = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        d = int(r.choice([64, 128]))
+        mode = ("dense", "causal", "window")[len(cases) % 3]
+        rep = int(r.choice([1, 2, 4]))
+        if mode == "causal":
+            Nq = 128 * int(r.integers(4, 17))
+            Nk = Nq + 128 * int(r.integers(0, 4))
+        else:
+            Nq = int(r.integers(200, 1700))
+            Nk = 128 * int(r.integers(14 if d == 128 else 8, 21))
+            if mode == "window":
+                Nk = max(Nk, 128 * ((Nq + 127) // 128))
+        tiles = (Nq + 255) // 256
+        bh = int(r.integers(512, 1400)) // tiles + 1
+        bh = max(8, ((bh + 8 * rep - 1) // (8 * rep)) * 8 * rep)   # B*H, a multiple of 8 * rep
+        B = int(r.choice([b for b in (1, 2, 3, 4) if bh % (b * rep) == 0 and (bh // b) % 8 == 0] or [1]))
+        H = bh // B
+        if B * H * Nk * d > 80_000_000:
+            continue
+        causal, window = mode == "causal", None
+        if mode == "window":
+            causal = bool(r.integers(2))
+            left = int(r.integers(1, 1500))
+            right = 0 if causal else int(r.choice([-1, int(r.integers(0, 400))]))
+            window = (left, right)
+        cases.append((B, H, H // rep, Nq, Nk, d, causal, window))
+    return cases
+
+
+RANDOM_CASES = _random_stream_cases(12, 20260)
+
+
+@pytest.mark.parametrize("B,H,Hk,Nq,Nk,d,causal,window", RANDOM_CASES)
+def test_stream_random_shapes(B, H, Hk, Nq, Nk, d, causal, window):
+    # Seeded shapes across the persistent form's three deals (dense every
+    # wpx-th tile, causal longest-first rounds, window rotated bands), with
+    # grouped heads; one row of every 128-row tile and the first and last
+    # heads in full. [Understanding FlashAttention Pt 1, sections 2.4, 3.1
+    # and 3.5.]
+    _banner(f"stream random B={B} H={H} Hk={Hk} Nq={Nq} Nk={Nk} d={d} causal={causal} window={window}")
+    w = workloads.Workload("stream_random", B, H, Nq, Nk, d, causal=causal, window=window,
+                           seed=7 * B * H + 3 * Nq + Nk + d, Hk=Hk)
+    inp = workloads.make_inputs(w)
+    o, lse = nan_outputs(B, H, Nq, d, "bf16")
+    ea.attn_fwd(inp["q"].cuda(), inp["k"].cuda(), inp["v"].cuda(), scale=inp["scale"],
+                causal=causal, window=window, out=o, lse=lse)
+    torch.cuda.synchronize()
+    o_c, lse_c = o.cpu(), lse.cpu()
+    assert_all_written(o_c, lse_c, "stream random")
+    rep = H // Hk
+    f = lambda t: t.double().numpy()
+    qd, kd, vd = f(inp["q"]), f(inp["k"]), f(inp["v"])
+
+    def oracle_rows(part):
+        by_head = {}
+        for n, (b, h, i) in enumerate(part):
+            by_head.setdefault((b, h), []).append((n, i))
+        out_o = np.zeros((len(part), d))
+        out_l = np.zeros(len(part))
+        for (b, h), items in by_head.items():
+            oo, ll = oracle.attention_rows(qd[b:b + 1, h:h + 1], kd[b:b + 1, h // rep:h // rep + 1],
+                                           vd[b:b + 1, h // rep:h // rep + 1],
+                                           [(0, 0, i) for _, i in items], scale=inp["scale"],
+                                           causal=causal, window=window)
+            for r_, (n, _) in enumerate(items):
+                out_o[n] = oo[r_]
+                out_l[n] = ll[r_]
+        return out_o, out_l
+
+    rows = tile_rows(B, H, Nq, w.seed) + head_rows(0, 0, Nq) + head_rows(B - 1, H - 1, Nq)
+    compare_rows(o_c, lse_c, rows, oracle_rows, "bf16", f"stream random d={d} Nq={Nq} Nk={Nk}")
