@@ -260,3 +260,43 @@ def test_varlen_full_size_every_tile(name):
         rl.append(ll)
     compare(np.concatenate(go), np.concatenate(gl), np.concatenate(ro), np.concatenate(rl),
             w.dtype, f"varlen full {name} every tile")
+
+
+def _random_varlen_cases(n, seed):
+    """Seeded packed batches: 1-64 sequences whose lengths mix lognormal
+    draws with empty, single-row and tile-edge lengths, key lengths equal to
+    the query lengths or drawn separately, H a multiple of 8 (the persistent
+    form) with one to all query heads per K/V head."""
+    r = np.random.default_rng(seed)
+    edge = [0, 1, 63, 64, 65, 255, 256, 257]
+    cases = []
+    for c in range(n):
+        ns = int(r.integers(1, 65))
+        lq = [int(min(3000, round(float(np.exp(np.log(300) + 1.0 * r.normal())))))
+              if r.random() < 0.8 else int(r.choice(edge)) for _ in range(ns)]
+        lk = None
+        if c % 3 == 2:
+            lk = [int(min(3000, max(0, x + int(r.integers(-100, 300))))) for x in lq]
+        H = int(r.choice([8, 16, 24]))
+        Hk = int(r.choice([h for h in (1, 2, 4, 8, H) if H % h == 0]))
+        d = int(r.choice([64, 128]))
+        cases.append((lq, lk, H, Hk, d, bool(c % 2)))
+    return cases
+
+
+@pytest.mark.parametrize("lens_q,lens_k,H,Hk,d,causal", _random_varlen_cases(10, 9090))
+def test_varlen_random_batches(lens_q, lens_k, H, Hk, d, causal):
+    # seeded packed batches against the oracle, compared in full into
+    # NaN-filled outputs [flash-attention, Part II, variable-length batches]
+    lens_k = lens_q if lens_k is None else lens_k
+    _banner(f"varlen random {len(lens_q)} sequences rows={sum(lens_q)} keys={sum(lens_k)} "
+            f"H={H} Hk={Hk} d={d} causal={causal}")
+    q, k, v, cu_q, cu_k = _packed(lens_q, lens_k, H, Hk, d, "bf16", seed=5 * sum(lens_q) + d + H)
+    T = q.shape[0]
+    out = torch.full((T, H, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((H, T), float("nan"), dtype=torch.float32, device="cuda")
+    o, lse = _run(q, k, v, cu_q, cu_k, max(max(lens_q), 1), causal, out=out, lse=lse)
+    ro, rl = oracle.attention_varlen(q.double().numpy(), k.double().numpy(), v.double().numpy(),
+                                     cu_q.numpy(), cu_k.numpy(), scale=d ** -0.5, causal=causal)
+    compare(o.double().cpu().numpy(), lse.double().cpu().numpy().T, ro, rl.T, "bf16",
+            f"varlen random {len(lens_q)} sequences")
