@@ -59,9 +59,28 @@ static int stream_grid_varlen(const FwdParams& p, int kt) {
   return cus % 8 == 0 ? cus : 0;
 }
 
+// Padded batches with a bias take the persistent form's work list with batch
+// b as sequence b (64-key tiles, keys kv_len[b] or Nk) at d = 64 without a
+// causal mask or window, when the bias blocks can be copied by LDS DMA
+// (bias_dma: rows 16-byte aligned, Nk a multiple of 4), at most 64 batches,
+// H a multiple of 8, at least 64 keys, at most 2048 query tiles per head
+// (B * ceil(Nq / 256)), rows in reach of 32-bit copy offsets and at least
+// two query tiles per compute unit.
+static int stream_grid_bias(const FwdParams& p, int d, int kt) {
+  if (d != 64 || kt != 64 || p.causal || p.local || p.n_split > 1 || !p.bias_dma) return 0;
+  if (p.B < 1 || p.B > 64 || p.H < 8 || p.H % 8 != 0 || p.Nk < 64) return 0;
+  const int64_t nqt = (p.Nq + 255) / 256;
+  if ((int64_t)p.B * nqt > 2048) return 0;
+  for (int64_t sn : {p.q_sn, p.k_sn, p.v_sn})
+    if (64 * sn * 2 >= ((int64_t)1 << 31)) return 0;
+  const int cus = device_cus();
+  if (cus % 8 != 0 || (int64_t)p.B * p.H * nqt < 2 * (int64_t)cus) return 0;
+  return cus;
+}
+
 // The persistent form (fwd_bf16_stream.hip), 256-row query tiles and one
 // workgroup per compute unit, streams key tiles of kt keys (64, or 128 at
-// d = 64). Unpacked, it applies with no bias, key lengths or key split,
+// d = 64). Unpacked and unbiased, it applies with no key lengths or key split,
 // when every key tile is full and they come in pairs (Nk a
 // multiple of 2 kt), rows are in reach of 32-bit copy offsets and there are
 // at least two query tiles per compute unit. Dense query tiles host the next
@@ -72,7 +91,8 @@ static int stream_grid_varlen(const FwdParams& p, int kt) {
 // tiles copy at once. Returns the grid, or 0.
 static int stream_grid(const FwdParams& p, int d, int kt) {
   if (p.cu_q != nullptr) return stream_grid_varlen(p, kt);
-  if (p.n_split > 1 || p.bias != nullptr || p.kv_len != nullptr) return 0;
+  if (p.bias != nullptr) return stream_grid_bias(p, d, kt);
+  if (p.n_split > 1 || p.kv_len != nullptr) return 0;
   if (p.Nk % (2 * kt) != 0 || 64 * p.q_sn * 2 >= ((int64_t)1 << 31)) return 0;
   const int cus = device_cus();
   if (cus % 8 != 0) return 0;

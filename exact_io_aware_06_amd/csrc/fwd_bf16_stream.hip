@@ -69,6 +69,17 @@
 // workgroups deal the list greedily by the work they already hold. Key
 // tiles are a sequence's own keys in 64-key steps; the last one, read
 // shifted to end inside the packed keys, is masked to the keys it owns.
+//
+// Padded batches with a bias (d = 64, not causal; BIAS): the same work list
+// with batch b as sequence b (all Nq query rows, key count kv_len[b] or Nk)
+// and the batch strides of the tensors; key tiles are read in place (the
+// last 64 keys of the tensor for a tile reaching past them). Each wavefront
+// copies the fp32 bias block of its 32 rows for the next key tile into its
+// own 8 KB of LDS by DMA (no other wavefront reads it) right after reading
+// the current one, which it adds to the raw scores as scale * qk + bias
+// (natural units, one FMA; the exponentials then take log2(e)). The copy is
+// the iteration's last vector memory operation and may stay in flight
+// across the barrier: it is waited for where the next block is read.
 
 #include "fwd_bf16_kernel.h"
 
@@ -85,11 +96,20 @@ constexpr int kGreedyItems = kGreedyRounds * 64;  // (at most 64 workgroups per 
 constexpr int kSeqTableBytes =
     24 * kMaxSeqs + 4 * kMaxEntries + 4 * kGreedyItems + 4 * 64 + 4 * (kGreedyRounds + 1) + 16;
 
-template <int D, int NB, bool CAUSAL, bool LOCAL, bool VARLEN>
+// LDS of the bias blocks (BIAS): one 8 KB block of 32 rows x 64 keys (fp32)
+// per wavefront, behind the K/V buffers, Q/O rows and the work list.
+constexpr int kBiasWave = 32 * 64 * 4;
+template <int D, int NB>
+constexpr int bias_lds_offset() {
+  return (4 * (32 * NB) * D * 2 + 8 * 32 * 2 * D + kSeqTableBytes + 255) / 256 * 256;
+}
+
+template <int D, int NB, bool CAUSAL, bool LOCAL, bool VARLEN, bool BIAS>
 __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, TileMap tm) {
   static_assert(CAUSAL || !LOCAL, "a window is a two-sided causal mask");
   static_assert(NB == 2 || NB == 4, "64- or 128-key tiles");
   static_assert(!VARLEN || (NB == 2 && !LOCAL), "packed sequences: 64-key tiles, no window");
+  static_assert(!BIAS || (VARLEN && D == 64 && !CAUSAL), "bias: padded batches at d = 64, not causal");
   constexpr int W = 8;
   using G = Geo<D, W>;
   constexpr int kKT = 32 * NB;                  // keys per key tile
@@ -149,11 +169,20 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
       // one wavefront (B <= 64): the sequences, and their tiles in all
       int nq = 0;
       if (tid < p.B) {
-        const int a0 = min(max(p.cu_q[tid], 0), p.Nq), a1 = min(max(p.cu_q[tid + 1], a0), p.Nq);
-        const int c0 = min(max(p.cu_k[tid], 0), p.Nk), c1 = min(max(p.cu_k[tid + 1], c0), p.Nk);
-        const int lq = a1 - a0;
+        int a0 = 0, c0 = 0, lq = p.Nq, lk = p.Nk;
+        if constexpr (BIAS) {
+          // batch tid: every query row, kv_len[tid] keys (clamped) or all
+          if (p.kv_len != nullptr) lk = min(max(p.kv_len[tid], 0), p.Nk);
+        } else {
+          a0 = min(max(p.cu_q[tid], 0), p.Nq);
+          const int a1 = min(max(p.cu_q[tid + 1], a0), p.Nq);
+          c0 = min(max(p.cu_k[tid], 0), p.Nk);
+          const int c1 = min(max(p.cu_k[tid + 1], c0), p.Nk);
+          lq = a1 - a0;
+          lk = c1 - c0;
+        }
         nq = min((lq >> 8) + ((lq & 255) != 0 ? 1 : 0), nqt);
-        seq[tid] = make_int4(lq, c1 - c0, nq, 0);
+        seq[tid] = make_int4(lq, lk, nq, 0);
         sbase[tid] = make_int2(a0, c0);
       }
       int tot = nq;
@@ -231,7 +260,11 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
     int lq, lk;         // packed: the sequence's query rows and keys
     int kmin;           // packed: minus the sequence's first key
   };
-  using Item = std::conditional_t<VARLEN, ItemSeq, ItemBase>;
+  struct ItemBias : ItemSeq {
+    const uint8_t* bias;  // bias: row min(q0 + 32 * wave, Nq - 1), key 0 of (batch, head)
+    int brmax;            // bias: rows of this wavefront's block that exist, minus 1
+  };
+  using Item = std::conditional_t<BIAS, ItemBias, std::conditional_t<VARLEN, ItemSeq, ItemBase>>;
   auto item = [&](int it) {
     if constexpr (VARLEN) {
       Item r;
@@ -257,14 +290,21 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
       const int nraw = (max(kv, 0) + kKT - 1) / kKT;
       r.nt = max(2, nraw + (nraw & 1));
       const int wrow = min(r.q0 + 32 * wave, r.lq - 1);
-      r.q = uniform_ptr(reinterpret_cast<const uint8_t*>(static_cast<const __bf16*>(p.q) + h * p.q_sh +
-                                                         (int64_t)(q_lo + wrow) * p.q_sn));
-      r.k = uniform_ptr(reinterpret_cast<const uint8_t*>(static_cast<const __bf16*>(p.k) + hk * p.k_sh +
-                                                         (int64_t)k_lo * p.k_sn));
-      r.v = uniform_ptr(reinterpret_cast<const uint8_t*>(static_cast<const __bf16*>(p.v) + hk * p.v_sh +
-                                                         (int64_t)k_lo * p.v_sn));
-      r.o = static_cast<__bf16*>(p.o) + (int64_t)q_lo * p.o_sn + h * p.o_sh;
-      r.lse = p.lse + q_lo + h * p.l_sh;
+      // padded batches (BIAS): batch b at its batch strides (q_lo = k_lo = 0)
+      const int64_t bb = BIAS ? (int64_t)b : (int64_t)0;
+      r.q = uniform_ptr(reinterpret_cast<const uint8_t*>(static_cast<const __bf16*>(p.q) + bb * p.q_sb +
+                                                         h * p.q_sh + (int64_t)(q_lo + wrow) * p.q_sn));
+      r.k = uniform_ptr(reinterpret_cast<const uint8_t*>(static_cast<const __bf16*>(p.k) + bb * p.k_sb +
+                                                         hk * p.k_sh + (int64_t)k_lo * p.k_sn));
+      r.v = uniform_ptr(reinterpret_cast<const uint8_t*>(static_cast<const __bf16*>(p.v) + bb * p.v_sb +
+                                                         hk * p.v_sh + (int64_t)k_lo * p.v_sn));
+      r.o = static_cast<__bf16*>(p.o) + bb * p.o_sb + (int64_t)q_lo * p.o_sn + h * p.o_sh;
+      r.lse = p.lse + bb * p.l_sb + q_lo + h * p.l_sh;
+      if constexpr (BIAS) {
+        r.bias = uniform_ptr(reinterpret_cast<const uint8_t*>(p.bias + bb * p.bias_sb + h * p.bias_sh +
+                                                              (int64_t)wrow * p.bias_sn));
+        r.brmax = r.lq - 1 - wrow;
+      }
       return r;
     }
     int qt, hb;
@@ -330,8 +370,12 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
     if constexpr (VARLEN) return it.lq;
     else return Nq;
   };
+  // Padded batches (BIAS) read tile t in place, or the last 64 keys of the
+  // tensor when it reaches past them (a multiple of 4 keys: the bias
+  // blocks' 16-byte chunks stay aligned).
   auto kpos = [&](const Item& it, int t) {
-    if constexpr (VARLEN) return max(min(kKT * t, it.lk - kKT), it.kmin);
+    if constexpr (BIAS) return min(kKT * t, Nk - kKT);
+    else if constexpr (VARLEN) return max(min(kKT * t, it.lk - kKT), it.kmin);
     else return tix(it, t) * kKT;
   };
 
@@ -398,7 +442,9 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
   f32x16 oacc[G::kNcb];
   float m_run = -INFINITY;  // reference R of this lane's row (base 2)
   float l_run = 0.f;
-  const float c2 = p.scale_log2;
+  // base-2 factor of the scores: scale * log2(e) on raw dot products, log2(e)
+  // on biased scores (already scale * qk + bias)
+  const float c2 = BIAS ? kLog2e : p.scale_log2;
 
   auto tile_max = [&](const f32x16 (&s)[NB]) {
     float m = -INFINITY;
@@ -560,6 +606,53 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
     }
   };
 
+  // Bias blocks (BIAS): this wavefront's 32 rows x 64 keys of key tile t of
+  // `it`, copied into its own 8 KB of LDS (chunk kc, keys 4 kc .. 4 kc + 3,
+  // of row r at 16-byte slot 16 r + (kc ^ (r mod 16)): one row's 16 lanes
+  // copy 256 contiguous bytes, and the reads below of 16 rows hit 16
+  // different bank groups); rows past the last query re-read the last one.
+  uint8_t* const bias_lds = smem + bias_lds_offset<D, NB>() + wave * kBiasWave;
+  auto dma_bias = [&](const Item& it, int t) {
+    if constexpr (BIAS) {
+      const uint8_t* src = uniform_ptr(it.bias + 4 * kpos(it, t));
+      const int ln = fresh(lane);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int r = 4 * i + (ln >> 4);
+        const int kc = (ln & 15) ^ (r & 15);
+        dma16(src, (uint32_t)(min(r, it.brmax) * (int)(p.bias_sn * 4) + 16 * kc), bias_lds + 1024 * i);
+      }
+    }
+  };
+  // The block in LDS as 16-byte chunks of the lane's row: read g holds
+  // chunk 8 (g / 4) + 4 ((g / 2) % 2) + 2 hi + g % 2, i.e. the keys of
+  // registers 4 (g % 4) .. 4 (g % 4) + 3 of score block g / 4 (register r
+  // of block bb holds key 32 bb + 16 (r / 8) + 8 hi + r % 8).
+  auto bias_read = [&](int g) {
+    const int kc = 8 * (g >> 2) + 4 * ((g >> 1) & 1) + 2 * hi + (g & 1);
+    return *reinterpret_cast<const f32x4*>(bias_lds + 256 * l32 + 16 * (kc ^ (l32 & 15)));
+  };
+  // scores -> scale * qk + bias (natural units, one FMA); then, once this
+  // wavefront's reads are done, the block of key tile t of `it` is copied
+  // over the one just read
+  auto add_bias = [&](f32x16 (&s)[NB], const Item& it, int t) {
+    if constexpr (BIAS) {
+      // the block's copies were issued before this iteration's K/V copies
+      // (kNdma of them, the only vector memory operations that may still be
+      // in flight once it has landed)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kNdma) : "memory");
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        const f32x4 x = bias_read(g);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          s[g >> 2][4 * (g & 3) + e] = __builtin_fmaf(s[g >> 2][4 * (g & 3) + e], p.scale, x[e]);
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      dma_bias(it, t);
+    }
+  };
+
   u32x4 pb[NB][2];
   float rs_half = 0.f;
 
@@ -629,7 +722,15 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
     }
     l_run += rs;
     rs_half = 0.f;
-    // S_{j+1}: key tile j + 1 of this query tile, or nxt's first
+    // S_{j+1}: key tile j + 1 of this query tile, or nxt's first. Bias: its
+    // block (copied during the previous iteration) is added, then the block
+    // of the tile after it (tile j + 2 of this query tile, else nxt's tile
+    // j + 2 - nt) is copied over it once this wavefront's reads are done.
+    if constexpr (BIAS) {
+      if constexpr (kLast) add_bias(sn, nxt, 1);
+      else if (j + 2 < nt) add_bias(sn, cur, j + 2);
+      else add_bias(sn, nxt, 0);
+    }
     if constexpr (VARLEN) {
       if constexpr (kLast) mask_seq(sn, nxt, 0);
       else mask_seq(sn, cur, j + 1);
@@ -638,7 +739,13 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
     }
     using Next = std::integral_constant<bool, !kLast>;
     phase_b(Next{}, vlane + par * kKBytes, pb, sn, m_run == -INFINITY ? 0.f : m_run, rs_half);
-    wait_tiles();
+    if constexpr (BIAS) {
+      // the bias copies (issued after this iteration's K/V copies) may stay
+      // in flight into the next iteration
+      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    } else {
+      wait_tiles();
+    }
     __syncthreads();
   };
 
@@ -683,6 +790,7 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
     const Item c0 = item(0);
 #pragma unroll
     for (int i = 0; i < kQCopies; ++i) q_copy(c0, i);
+    dma_bias(c0, 0);
     const uint8_t* k0 = uniform_ptr(c0.k + kpos(c0, 0) * ksn);
     const uint8_t* v0 = uniform_ptr(c0.v + kpos(c0, 0) * vsn);
 #pragma unroll
@@ -734,6 +842,7 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
       if (greedy) n_items = __builtin_amdgcn_readfirstlane(mine[kGreedyRounds]);
     q_from_lds();
     qk_plain(klane, sa);
+    add_bias(sa, c0, 1);
     if constexpr (VARLEN) mask_seq(sa, c0, 0);
     else if constexpr (CAUSAL) mask_causal(sa, c0.q0, tix(c0, 0) * kKT);
     // iteration 0 reads V_0 and K_1 and overwrites K buffer 0: every
@@ -786,14 +895,19 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
       for (int i = 0; i < kQCopies; ++i) drain(cur, i);
     }
   }
+  // the last bias copies must land in this workgroup's LDS before it ends
+  if constexpr (BIAS) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-template <int D, int NB, bool CAUSAL, bool LOCAL, bool VARLEN = false>
+template <int D, int NB, bool CAUSAL, bool LOCAL, bool VARLEN = false, bool BIAS = false>
 hipError_t launch_stream_d(const FwdParams& p, const TileMap& tm, int grid, hipStream_t stream) {
-  // K/V double buffers + Q/O rows (+ the packed sequences' tile list)
-  constexpr int kSmemAll = 4 * (32 * NB) * D * 2 + 8 * 32 * 2 * D + (VARLEN ? kSeqTableBytes : 0);
+  // K/V double buffers + Q/O rows (+ the packed sequences' tile list) (+ the
+  // eight wavefronts' bias blocks)
+  constexpr int kSmemAll = BIAS ? bias_lds_offset<D, NB>() + 8 * kBiasWave
+                                : 4 * (32 * NB) * D * 2 + 8 * 32 * 2 * D + (VARLEN ? kSeqTableBytes : 0);
+  static_assert(kSmemAll <= 160 * 1024, "LDS of one workgroup");
   static bool attr_set = false;  // benign race: every caller sets the same value
-  auto kern = fwd_bf16_stream_kernel<D, NB, CAUSAL, LOCAL, VARLEN>;
+  auto kern = fwd_bf16_stream_kernel<D, NB, CAUSAL, LOCAL, VARLEN, BIAS>;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kSmemAll);
@@ -821,6 +935,16 @@ hipError_t launch_stream_varlen(const FwdParams& p, const TileMap& tm, int grid,
 
 hipError_t launch_bf16_stream(const FwdParams& p, const TileMap& tm, int d, int key_tile, int grid,
                               hipStream_t s) {
+  if (p.bias != nullptr) {
+    // padded batches with a bias: d = 64, 64-key tiles, not causal, bias
+    // blocks by LDS DMA, B <= 64, B * n_qtiles query tiles per head at most
+    // kMaxEntries
+    if (d != 64 || key_tile != 64 || p.causal || p.local || p.cu_q != nullptr || p.n_split > 1 ||
+        !p.bias_dma || p.B < 1 || p.B > kMaxSeqs || (int64_t)p.B * tm.n_qtiles > kMaxEntries ||
+        p.H < 8 || p.H % 8 != 0 || p.Nk < 64)
+      return hipErrorInvalidValue;
+    return launch_stream_d<64, 2, false, false, true, true>(p, tm, grid, s);
+  }
   if (p.cu_q != nullptr) {
     // packed sequences: 64-key tiles, no window, B <= 64, B * n_qtiles
     // query tiles per head at most kMaxEntries

@@ -279,3 +279,67 @@ def test_stream_random_shapes(B, H, Hk, Nq, Nk, d, causal, window):
 
     rows = tile_rows(B, H, Nq, w.seed) + head_rows(0, 0, Nq) + head_rows(B - 1, H - 1, Nq)
     compare_rows(o_c, lse_c, rows, oracle_rows, "bf16", f"stream random d={d} Nq={Nq} Nk={Nk}")
+
+
+BIAS_CASES = [
+    # (B, H, Hk, Nq, Nk, bias batches, bias heads, kv_len, -inf fraction):
+    # d = 64, not causal, H a multiple of 8, at least 512 query tiles of 256
+    # rows: padded batches with a bias on the persistent form
+    (8, 16, 16, 1024, 1024, 1, 16, [614, 397, 242, 762, 429, 625, 464, 860], 0.0),
+    (2, 64, 16, 1000, 700, 2, 64, [0, 700], 0.0),          # full bias, ragged rows, no keys
+    (4, 32, 32, 1024, 516, 4, 1, None, 0.02),              # head-broadcast bias, -inf entries
+    (2, 80, 20, 777, 1028, 1, 1, [1028, 3], 0.0),          # one bias for all; shifted last tile
+    (4, 32, 8, 1024, 64, 1, 32, [1, 64, 63, 9999], 0.0),   # 64 keys (one tile), kv_len > Nk
+]
+
+
+@pytest.mark.parametrize("B,H,Hk,Nq,Nk,bb,bh,kv,ninf", BIAS_CASES)
+def test_stream_bias_matches_oracle(B, H, Hk, Nq, Nk, bb, bh, kv, ninf):
+    # Additive fp32 bias (broadcast over batches and/or heads) and per-batch
+    # key lengths on the persistent form (each wavefront's bias block copied
+    # into LDS one key tile ahead): one row of every 128-row tile and the
+    # first and last heads in full, NaN-filled outputs. [Understanding
+    # FlashAttention Pt 1, section 0.2 (additive bias) and 3.5 (padding
+    # masks); flash-attention, Part II (padded batches).]
+    _banner(f"stream bias B={B} H={H} Hk={Hk} Nq={Nq} Nk={Nk} bias=[{bb},{bh}] kv={kv} ninf={ninf}")
+    d = 64
+    g = torch.Generator().manual_seed(B * H + Nq + Nk + bb + bh)
+    q = torch.randn(B, H, Nq, d, generator=g).to(torch.bfloat16)
+    k = torch.randn(B, Hk, Nk, d, generator=g).to(torch.bfloat16)
+    v = torch.randn(B, Hk, Nk, d, generator=g).to(torch.bfloat16)
+    bias = 0.5 * torch.randn(bb, bh, Nq, Nk, generator=g)
+    if ninf > 0:
+        bias[torch.rand(bias.shape, generator=g) < ninf] = float("-inf")
+        bias[0, 0, 5, :] = float("-inf")   # a row that sees no key at all
+    kv_len = None if kv is None else torch.tensor(kv, dtype=torch.int32)
+    scale = float(torch.tensor(d ** -0.5, dtype=torch.float32))
+    o, lse = nan_outputs(B, H, Nq, d, "bf16")
+    ea.attn_fwd(q.cuda(), k.cuda(), v.cuda(), bias=bias.cuda(),
+                kv_len=None if kv_len is None else kv_len.cuda(), scale=scale, out=o, lse=lse)
+    torch.cuda.synchronize()
+    o_c, lse_c = o.cpu(), lse.cpu()
+    assert_all_written(o_c, lse_c, "stream bias")
+    rep = H // Hk
+    f = lambda t: t.double().numpy()
+    qd, kd, vd, bd = f(q), f(k), f(v), f(bias)
+    kvn = None if kv_len is None else kv_len.numpy()
+
+    def oracle_rows(part):
+        by_head = {}
+        for n, (b, h, i) in enumerate(part):
+            by_head.setdefault((b, h), []).append((n, i))
+        out_o = np.zeros((len(part), d))
+        out_l = np.zeros(len(part))
+        for (b, h), items in by_head.items():
+            bsel = bd[(b if bb > 1 else 0):(b if bb > 1 else 0) + 1, (h if bh > 1 else 0):(h if bh > 1 else 0) + 1]
+            oo, ll = oracle.attention_rows(qd[b:b + 1, h:h + 1], kd[b:b + 1, h // rep:h // rep + 1],
+                                           vd[b:b + 1, h // rep:h // rep + 1],
+                                           [(0, 0, i) for _, i in items], scale=scale, bias=bsel,
+                                           kv_len=None if kvn is None else kvn[b:b + 1])
+            for r_, (n, _) in enumerate(items):
+                out_o[n] = oo[r_]
+                out_l[n] = ll[r_]
+        return out_o, out_l
+
+    rows = tile_rows(B, H, Nq, B + H + Nq) + head_rows(0, 0, Nq) + head_rows(B - 1, H - 1, Nq)
+    compare_rows(o_c, lse_c, rows, oracle_rows, "bf16", f"stream bias Nq={Nq} Nk={Nk}")
