@@ -11,31 +11,56 @@ namespace attn {
 namespace {
 
 // ------------------------------------------------------------- preprocess
-// LPR lanes per query row, 8 elements (16 bytes) of O and dO per lane.
-template <int LPR>
+// LPR lanes per query row, 8 elements (16 bytes) of O and dO per lane, kRep
+// rows per lane (their loads issued together).
+// GRID3: workgroup (x, h, b) takes kRep * kRows rows of head h of batch b
+// from row x * kRep * kRows on (no per-lane division); else a flat grid over
+// all B * H * Nq rows (for H or B beyond a grid dimension's 65535).
+constexpr int kPreRep = 4;
+template <int LPR, bool GRID3>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
-  constexpr int kRows = 256 / LPR;  // rows per workgroup
+  constexpr int kRows = 256 / LPR;  // rows per workgroup and repetition
   const int sub = threadIdx.x % LPR;
-  const int64_t rows = (int64_t)p.B * p.H * p.Nq;
-  const int64_t row = (int64_t)blockIdx.x * kRows + threadIdx.x / LPR;
-  const bool ok = row < rows;
-  const int64_t rr = ok ? row : rows - 1;
-  const int i = (int)(rr % p.Nq);
-  const int h = (int)((rr / p.Nq) % p.H);
-  const int b = (int)(rr / ((int64_t)p.Nq * p.H));
-  const __bf16* orow = static_cast<const __bf16*>(p.o) + b * p.o_sb + h * p.o_sh + (int64_t)i * p.o_sn;
-  const __bf16* drow = static_cast<const __bf16*>(p.do_) + b * p.do_sb + h * p.do_sh + (int64_t)i * p.do_sn;
-  const bf16x8 ov = *reinterpret_cast<const bf16x8*>(orow + 8 * sub);
-  const bf16x8 dv = *reinterpret_cast<const bf16x8*>(drow + 8 * sub);
-  float acc = 0.f;
+  int i[kPreRep], h[kPreRep], b[kPreRep];
+  bool ok[kPreRep];
+  int64_t row[kPreRep];
+  bf16x8 ov[kPreRep], dv[kPreRep];
+  float lv[kPreRep];
 #pragma unroll
-  for (int c = 0; c < 8; ++c) acc = __builtin_fmaf((float)ov[c], (float)dv[c], acc);
+  for (int r = 0; r < kPreRep; ++r) {
+    if constexpr (GRID3) {
+      h[r] = blockIdx.y;
+      b[r] = blockIdx.z;
+      const int i0 = (blockIdx.x * kPreRep + r) * kRows + threadIdx.x / LPR;
+      ok[r] = i0 < p.Nq;
+      i[r] = ok[r] ? i0 : p.Nq - 1;
+      row[r] = ((int64_t)b[r] * p.H + h[r]) * p.Nq + i[r];
+    } else {
+      const int64_t rows = (int64_t)p.B * p.H * p.Nq;
+      row[r] = ((int64_t)blockIdx.x * kPreRep + r) * kRows + threadIdx.x / LPR;
+      ok[r] = row[r] < rows;
+      const int64_t rr = ok[r] ? row[r] : rows - 1;
+      i[r] = (int)(rr % p.Nq);
+      h[r] = (int)((rr / p.Nq) % p.H);
+      b[r] = (int)(rr / ((int64_t)p.Nq * p.H));
+    }
+    const __bf16* orow = static_cast<const __bf16*>(p.o) + b[r] * p.o_sb + h[r] * p.o_sh + (int64_t)i[r] * p.o_sn;
+    const __bf16* drow = static_cast<const __bf16*>(p.do_) + b[r] * p.do_sb + h[r] * p.do_sh + (int64_t)i[r] * p.do_sn;
+    ov[r] = *reinterpret_cast<const bf16x8*>(orow + 8 * sub);
+    dv[r] = *reinterpret_cast<const bf16x8*>(drow + 8 * sub);
+    lv[r] = p.lse[b[r] * p.l_sb + h[r] * p.l_sh + i[r]];
+  }
 #pragma unroll
-  for (int o = LPR / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
-  if (ok && sub == 0) {
-    p.dsum[row] = acc;
-    const float l = p.lse[b * p.l_sb + h * p.l_sh + i];
-    p.lse2[row] = (l == -INFINITY) ? -INFINITY : -l * kLog2e;
+  for (int r = 0; r < kPreRep; ++r) {
+    float acc = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc = __builtin_fmaf((float)ov[r][c], (float)dv[r][c], acc);
+#pragma unroll
+    for (int o = LPR / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+    if (ok[r] && sub == 0) {
+      p.dsum[row[r]] = acc;
+      p.lse2[row[r]] = (lv[r] == -INFINITY) ? -INFINITY : -lv[r] * kLog2e;
+    }
   }
 }
 
@@ -81,8 +106,16 @@ int launch_bwd_bf16(const BwdParams& p, int d, void* stream) {
   if (d != 64 && d != 128) return (int)hipErrorInvalidValue;
   const int64_t rows = (int64_t)p.B * p.H * p.Nq;
   if (rows > 0) {
-    if (d == 128) hipLaunchKernelGGL(bwd_pre_kernel<16>, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, s, p);
-    else hipLaunchKernelGGL(bwd_pre_kernel<8>, dim3((unsigned)((rows + 31) / 32)), dim3(256), 0, s, p);
+    const int kr = (d == 128 ? 16 : 32) * kPreRep;   // rows per workgroup
+    if (p.H <= 65535 && p.B <= 65535) {
+      const dim3 grid((unsigned)((p.Nq + kr - 1) / kr), (unsigned)p.H, (unsigned)p.B);
+      if (d == 128) hipLaunchKernelGGL((bwd_pre_kernel<16, true>), grid, dim3(256), 0, s, p);
+      else hipLaunchKernelGGL((bwd_pre_kernel<8, true>), grid, dim3(256), 0, s, p);
+    } else {
+      const dim3 grid((unsigned)((rows + kr - 1) / kr));
+      if (d == 128) hipLaunchKernelGGL((bwd_pre_kernel<16, false>), grid, dim3(256), 0, s, p);
+      else hipLaunchKernelGGL((bwd_pre_kernel<8, false>), grid, dim3(256), 0, s, p);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return (int)e;
   }
