@@ -290,6 +290,8 @@ BIAS_CASES = [
     (4, 32, 32, 1024, 516, 4, 1, None, 0.02),              # head-broadcast bias, -inf entries
     (2, 80, 20, 777, 1028, 1, 1, [1028, 3], 0.0),          # one bias for all; shifted last tile
     (4, 32, 8, 1024, 64, 1, 32, [1, 64, 63, 9999], 0.0),   # 64 keys (one tile), kv_len > Nk
+    # 20 query rows: every wavefront's bias block re-reads the last row
+    (8, 64, 64, 20, 300, 1, 64, [300, 1, 77, 0, 128, 129, 64, 299], 0.0),
 ]
 
 
