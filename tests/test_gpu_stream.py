@@ -345,3 +345,35 @@ def test_stream_bias_matches_oracle(B, H, Hk, Nq, Nk, bb, bh, kv, ninf):
 
     rows = tile_rows(B, H, Nq, B + H + Nq) + head_rows(0, 0, Nq) + head_rows(B - 1, H - 1, Nq)
     compare_rows(o_c, lse_c, rows, oracle_rows, "bf16", f"stream bias Nq={Nq} Nk={Nk}")
+
+
+def test_stream_bias_strided_views_and_determinism():
+    # [B, N, H, d] storage seen as [B, H, N, d] for q, k, v and the output, a
+    # bias whose rows are padded to a larger stride, key lengths; the biased
+    # persistent form (d = 64) against the oracle, and two calls bitwise equal
+    g = torch.Generator().manual_seed(97)
+    B, H, N, Nk, d = 4, 32, 1024, 640, 64
+    qs = torch.randn(B, N, H, d, generator=g).to(torch.bfloat16).cuda()
+    ks = torch.randn(B, Nk, H, d, generator=g).to(torch.bfloat16).cuda()
+    vs = torch.randn(B, Nk, H, d, generator=g).to(torch.bfloat16).cuda()
+    q, k, v = qs.transpose(1, 2), ks.transpose(1, 2), vs.transpose(1, 2)
+    bias_store = 0.5 * torch.randn(1, H, N, Nk + 12, generator=g)
+    bias = bias_store[..., :Nk].cuda()          # row stride Nk + 12 floats (16-byte multiple)
+    kv_len = torch.tensor([640, 100, 513, 0], dtype=torch.int32)
+    out_store = torch.full((B, N, H, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    out = out_store.transpose(1, 2)
+    lse = torch.full((B, H, N), float("nan"), dtype=torch.float32, device="cuda")
+    ea.attn_fwd(q, k, v, bias=bias, kv_len=kv_len.cuda(), out=out, lse=lse)
+    o2, l2 = ea.attn_fwd(q, k, v, bias=bias, kv_len=kv_len.cuda())
+    torch.cuda.synchronize()
+    assert torch.equal(out, o2) and torch.equal(lse, l2)
+    o_c, lse_c = out.cpu(), lse.cpu()
+    assert_all_written(o_c, lse_c, "stream bias strided")
+    qd, kd, vd = (t.double().cpu().numpy() for t in (q, k, v))
+    bd = bias.double().cpu().numpy()
+
+    def oracle_rows(part):
+        return oracle.attention_rows(qd, kd, vd, part, scale=d ** -0.5, bias=bd, kv_len=kv_len.numpy())
+
+    rows = tile_rows(B, H, N, 98) + head_rows(1, 17, N) + head_rows(3, 0, N)
+    compare_rows(o_c, lse_c, rows, oracle_rows, "bf16", "stream bias strided")
