@@ -511,6 +511,13 @@ hipError_t set_lds(Kern kern, int bytes, bool& done) {
 // wavefronts per workgroup of the dK/dV and dQ kernels (32 keys or rows each)
 constexpr int kWkv = 4;
 constexpr int kWq = 4;
+// LDS requested per workgroup at d = 64 to hold two workgroups per CU
+// instead of the three that registers and LDS would allow (the request is
+// raised until only two fit in the CU's 160 KB): for dQ always, for dK/dV
+// with a causal or window edge, whose deal groups heads for two per CU
+// (dispatch_group). Measured A/B, c2 causal backward 172 -> 159 us, dense
+// c2 263 -> 261 us (dK/dV capped on dense problems too: 264).
+constexpr int kLdsTwoPerCu = 56 * 1024;
 
 template <int D, bool CAUSAL, bool HAS_BIAS, bool LOCAL>
 hipError_t launch_bwd_d(const BwdParams& p, hipStream_t s) {
@@ -522,7 +529,8 @@ hipError_t launch_bwd_d(const BwdParams& p, hipStream_t s) {
   tk.group = CAUSAL ? dispatch_group(tk.n_qtiles, 2) : 1;  // two workgroups per CU
   if (tk.total > 0) {
     auto kern = bwd_dkdv_kernel<D, kWkv, CAUSAL, HAS_BIAS, LOCAL>;
-    constexpr int lds = 2 * (2 * Geo<D, kWkv>::kKBytes + 2 * kBt * 4);
+    constexpr int lds0 = 2 * (2 * Geo<D, kWkv>::kKBytes + 2 * kBt * 4);
+    constexpr int lds = (D == 64 && CAUSAL && lds0 < kLdsTwoPerCu) ? kLdsTwoPerCu : lds0;
     static bool done = false;
     hipError_t e = set_lds(kern, lds, done);
     if (e != hipSuccess) return e;
@@ -539,7 +547,8 @@ hipError_t launch_bwd_d(const BwdParams& p, hipStream_t s) {
   tq.group = CAUSAL ? dispatch_group(tq.n_qtiles, 2) : 1;
   if (tq.total > 0) {
     auto kern = bwd_dq_kernel<D, kWq, CAUSAL, HAS_BIAS, LOCAL>;
-    constexpr int lds = 2 * 2 * Geo<D, kWq>::kKBytes;
+    constexpr int lds0 = 2 * 2 * Geo<D, kWq>::kKBytes;
+    constexpr int lds = (D == 64 && lds0 < kLdsTwoPerCu) ? kLdsTwoPerCu : lds0;
     static bool done = false;
     hipError_t e = set_lds(kern, lds, done);
     if (e != hipSuccess) return e;
