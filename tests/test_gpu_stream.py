@@ -377,3 +377,35 @@ def test_stream_bias_strided_views_and_determinism():
 
     rows = tile_rows(B, H, N, 98) + head_rows(1, 17, N) + head_rows(3, 0, N)
     compare_rows(o_c, lse_c, rows, oracle_rows, "bf16", "stream bias strided")
+
+
+def _random_bias_cases(n, seed):
+    """Seeded padded batches with a bias that take the biased persistent
+    form: d = 64, H a multiple of 8, at most 64 batches, Nk a multiple of 4
+    and at least 64, at least 512 query tiles of 256 rows; bias broadcast
+    over batches and/or heads or not, key lengths drawn per batch (some
+    zero, some beyond Nk) or absent."""
+    r = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        Nq = int(r.integers(100, 1300))
+        Nk = 4 * int(r.integers(16, 400))
+        tiles = (Nq + 255) // 256
+        B = int(r.integers(1, 9))
+        H = 8 * max(1, -(-512 // (8 * B * tiles)) + int(r.integers(0, 3)))
+        if B * H * Nk * 64 > 60_000_000 or B * H * Nq * Nk > 4_000_000_000:
+            continue
+        Hk = H // int(r.choice([h for h in (1, 2, 4, 8) if H % h == 0]))
+        bb = B if r.random() < 0.5 else 1
+        bh = H if r.random() < 0.7 else 1
+        kv = None
+        if r.random() < 0.8:
+            kv = [int(x) for x in r.integers(0, Nk + 100, B)]
+        cases.append((B, H, Hk, Nq, Nk, bb, bh, kv, 0.0))
+    return cases
+
+
+@pytest.mark.parametrize("B,H,Hk,Nq,Nk,bb,bh,kv,ninf", _random_bias_cases(6, 4242))
+def test_stream_bias_random_shapes(B, H, Hk, Nq, Nk, bb, bh, kv, ninf):
+    # seeded shapes through the same checks as the fixed biased cases
+    test_stream_bias_matches_oracle(B, H, Hk, Nq, Nk, bb, bh, kv, ninf)
