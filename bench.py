@@ -375,6 +375,24 @@ def warm_up(fn, args):
     torch.cuda.synchronize()
 
 
+def gemm_ms(torch, n, warmup, steps):
+    """Milliseconds per plain bf16 n x n x n product through torch (the
+    vendor GEMM library): the matrix throughput this board sustains."""
+    a = torch.randn(n, n, dtype=torch.bfloat16, device="cuda")
+    b = torch.randn(n, n, dtype=torch.bfloat16, device="cuda")
+    c = torch.empty(n, n, dtype=torch.bfloat16, device="cuda")
+    for _ in range(warmup):
+        torch.matmul(a, b, out=c)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        torch.matmul(a, b, out=c)
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -433,18 +451,7 @@ def main(argv=None):
 
     if args.gemm_calibration:
         n = args.gemm_calibration
-        a = torch.randn(n, n, dtype=torch.bfloat16, device="cuda")
-        b = torch.randn(n, n, dtype=torch.bfloat16, device="cuda")
-        for _ in range(max(args.warmup or 30, 1)):
-            c = a @ b
-        torch.cuda.synchronize()
-        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        start.record()
-        for _ in range(max(args.steps, 1)):
-            c = a @ b
-        stop.record()
-        torch.cuda.synchronize()
-        ms = start.elapsed_time(stop) / max(args.steps, 1)
+        ms = gemm_ms(torch, n, max(args.warmup or 30, 1), max(args.steps, 1))
         print(json.dumps({"gemm_bf16_n": n, "ms": round(ms, 4),
                           "tflops": round(2.0 * n ** 3 / (ms * 1e-3) / 1e12, 1)}), flush=True)
         return 0
@@ -547,6 +554,16 @@ def main(argv=None):
                     "bytes_per_step": algo, "timed": "split forward + merge (whole step)"}
         extra = {"num_splits": n_split}
 
+    gemm = None
+    if roofline["bound"] == "mfma" and w.dtype == "bf16" and not args.cold:
+        # context, after the timed region: what the vendor GEMM reaches on
+        # this board (a dense contraction with none of attention's softmax)
+        gms = gemm_ms(torch, 8192, 10, 20)
+        gt = 2.0 * 8192 ** 3 / (gms * 1e-3) / 1e12
+        gemm = {"vendor_gemm_bf16_8192_tflops": round(gt, 1),
+                "vendor_gemm_frac_of_peak": round(gt / peak, 4),
+                "attention_over_gemm": round(tflops / gt, 4)}
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(inp, w, args.cpu_budget)
@@ -563,6 +580,7 @@ def main(argv=None):
                    if args.cold else "warm (inputs resident)"},
         "roofline": roofline, "cpu_baseline": cpu,
         "per_call_ms": calls, "clock_settle": args.clock_settle,
+        "gemm_context": gemm,
     }
     print(json.dumps(out), flush=True)
     return 0
