@@ -1,7 +1,8 @@
 // bf16 forward, persistent ("stream") form for problems with no bias, key
 // lengths or key split, every key tile full (Nk a multiple of 128): dense,
-// causal with the diagonal on key-tile pairs, or a sliding window; and for
-// packed variable-length sequences (dense or causal, per sequence).
+// causal with the diagonal on key-tile pairs, or a sliding window; for
+// packed variable-length sequences (dense or causal, per sequence); and for
+// padded batches with an additive bias and key lengths at d = 64.
 //
 // Same arithmetic as fwd_bf16_kernel.h (transposed scores S^T = K Q^T with
 // v_mfma_f32_32x32x16_bf16, base-2 exponentials against an overflow-checked
