@@ -122,3 +122,31 @@ def test_split_forward_beyond_2_31_key_elements(spike_inputs, num_splits):
     rl = s_star + math.log(e_rel)
     compare(o[0, 0].double().cpu().numpy(), lse[0, 0].double().cpu().numpy(),
             ro[None], np.array([rl]), "bf16", f"large split Nk={nk} s*={s_star:.2f}")
+
+
+def test_many_heads_biased_forward_d64():
+    # the biased persistent form (d = 64, padded batches with a bias and key
+    # lengths) on q, k, v, o of 2.18e9 elements each: rows of the last heads
+    # lie past element 2^31; a bias shared by every batch and head
+    B, H, N, d = 2, 8320, 2048, 64
+    assert B * H * N * d > 2 ** 31
+    _banner(f"large: B={B} H={H} N={N} d={d} biased forward with key lengths")
+    q, k, v = (_randn((B, H, N, d), 950 + i) for i in range(3))
+    g = torch.Generator(device="cuda")
+    g.manual_seed(960)
+    bias = 0.5 * torch.randn((1, 1, N, N), generator=g, device="cuda", dtype=torch.float32)
+    kv_len = torch.tensor([1500, 2048], dtype=torch.int32, device="cuda")
+    o = torch.full((B, H, N, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((B, H, N), float("nan"), dtype=torch.float32, device="cuda")
+    ea.attn_fwd(q, k, v, bias=bias, kv_len=kv_len, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert not torch.isnan(lse).any()
+    scale = 1 / math.sqrt(d)
+    bd = bias.double().cpu().numpy()
+    kl = kv_len.cpu().numpy()
+    for b, h in ((0, 0), (1, 4100), (B - 1, H - 1)):
+        sl = lambda t: t[b:b + 1, h:h + 1].double().cpu().numpy()
+        ro, rl = oracle.attention_forward(sl(q), sl(k), sl(v), scale=scale, bias=bd,
+                                          kv_len=kl[b:b + 1])
+        compare(sl(o), sl(lse), ro, rl, "bf16", f"large biased fwd head ({b}, {h})")
+    del q, k, v, o, lse
