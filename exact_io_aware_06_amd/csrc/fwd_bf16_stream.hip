@@ -638,9 +638,10 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
   // over the one just read
   auto add_bias = [&](f32x16 (&s)[NB], const Item& it, int t) {
     if constexpr (BIAS) {
-      // the block's copies were issued before this iteration's K/V copies
-      // (kNdma of them, the only vector memory operations that may still be
-      // in flight once it has landed)
+      // vector memory operations complete in issue order: once at most the
+      // kNdma K/V copies of this iteration's phase A are outstanding, the
+      // block's copies (issued in the previous iteration, or the prologue)
+      // and this iteration's O and Q copies have landed
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kNdma) : "memory");
 #pragma unroll
       for (int g = 0; g < 8; ++g) {
@@ -741,8 +742,9 @@ __global__ __launch_bounds__(512, 2) void fwd_bf16_stream_kernel(FwdParams p, Ti
     using Next = std::integral_constant<bool, !kLast>;
     phase_b(Next{}, vlane + par * kKBytes, pb, sn, m_run == -INFINITY ? 0.f : m_run, rs_half);
     if constexpr (BIAS) {
-      // the bias copies (issued after this iteration's K/V copies) may stay
-      // in flight into the next iteration
+      // the eight bias copies, this iteration's last vector memory
+      // operations, may stay in flight into the next iteration; every K/V,
+      // Q and O copy before them has landed
       asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
     } else {
       wait_tiles();
