@@ -220,3 +220,38 @@ def test_decode_full_size_every_row(name):
             gl.append(lse_c[b, h].double().numpy())
     compare(np.concatenate(go), np.concatenate(gl), np.concatenate(ro), np.concatenate(rl),
             "bf16", f"decode {name} every row")
+
+
+def _random_split_cases(n, seed):
+    """Seeded split-key problems: decoding-sized and larger query counts,
+    grouped K/V heads (packed row spaces where Nq <= 64), causal or not, a
+    bias and/or per-batch key lengths, split counts from 1 to 40."""
+    r = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        B = int(r.integers(1, 4))
+        Hk = int(r.choice([1, 2, 3]))
+        H = Hk * int(r.choice([1, 2, 4, 8]))
+        Nq = int(r.choice([1, 2, 5, 17, 64, 65, 130]))
+        Nk = int(r.integers(1, 3000))
+        d = int(r.choice([64, 128]))
+        causal = bool(r.integers(2))
+        bias = bool(r.random() < 0.4)
+        kv = [int(x) for x in r.integers(0, Nk + 50, B)] if r.random() < 0.5 else None
+        ns = int(r.integers(1, 41))
+        cases.append((B, H, Hk, Nq, Nk, d, causal, bias, kv, ns))
+    return cases
+
+
+@pytest.mark.parametrize("B,H,Hk,Nq,Nk,d,causal,bias,kv,ns", _random_split_cases(10, 5151))
+def test_split_random_problems(B, H, Hk, Nq, Nk, d, causal, bias, kv, ns):
+    # seeded problems through the split-key forward and merge, compared in
+    # full with the oracle [flash-attention, Part III; FlashAttention:
+    # Mathematical Foundations..., section 7 (decoding)]
+    _banner(f"split random B={B} H={H} Hk={Hk} Nq={Nq} Nk={Nk} d={d} causal={causal} "
+            f"bias={bias} kv={kv} splits={ns}")
+    inp = _inputs(B, H, Nq, Nk, d, causal=causal, Hk=Hk, bias=bias, kv_len=kv,
+                  seed=31 * B + 7 * Nk + ns)
+    o, lse = run_split(inp, ns)
+    ro, rl = _oracle(inp)
+    compare(o, lse, ro, rl, "bf16", f"split random Nq={Nq} Nk={Nk} splits={ns}")
