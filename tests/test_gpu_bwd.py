@@ -160,3 +160,32 @@ def test_bwd_full_size_heads():
         ref = oracle.attention_backward(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(do),
                                         scale=inp["scale"])
         _compare([x[b:b + 1, h:h + 1] for x in got], ref, f"bwd full c3 head ({b}, {h})")
+
+
+def _random_bwd_cases(n, seed):
+    """Seeded backward problems: ragged query and key counts, grouped K/V
+    heads, causal, a window or neither, a bias and/or per-batch key lengths."""
+    r = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        B = int(r.integers(1, 3))
+        Hk = int(r.choice([1, 2]))
+        H = Hk * int(r.choice([1, 2, 3]))
+        Nq = int(r.integers(1, 400))
+        Nk = int(r.integers(1, 400))
+        d = int(r.choice([64, 128]))
+        mode = int(r.integers(3))
+        causal = mode == 1
+        window = (int(r.integers(0, 200)), int(r.integers(-1, 100))) if mode == 2 else None
+        bias = bool(r.random() < 0.3)
+        kv = [int(x) for x in r.integers(0, Nk + 20, B)] if r.random() < 0.4 else None
+        cases.append((B, H, Hk, Nq, Nk, d, causal, window, bias, kv))
+    return cases
+
+
+@pytest.mark.parametrize("B,H,Hk,Nq,Nk,d,causal,window,bias,kv", _random_bwd_cases(10, 6161))
+def test_bwd_random_problems(B, H, Hk, Nq, Nk, d, causal, window, bias, kv):
+    # seeded problems, dQ, dK, dV against the oracle at the gradient bar
+    # [FlashAttention, Explained, section 17; flash-attention, Part VII]
+    _check(B, H, Hk, Nq, Nk, d, seed=13 * Nq + Nk + d, causal=causal, window=window, bias=bias,
+           kv_len=kv)
