@@ -523,3 +523,51 @@ def test_causal_grouped_dispatch_ragged_last_group(d, B, H):
     ro, rl = run_oracle(inp)
     compare(o.double().cpu().numpy(), lse.double().cpu().numpy(), ro, rl, "bf16",
             f"causal grouped d={d} B={B} H={H}")
+
+
+def _random_forward_cases(n, seed):
+    """Seeded small problems through the per-tile kernels (too few query tiles
+    for the persistent form): both dtypes and head dimensions, grouped K/V
+    heads, causal or not, a bias broadcast over batches and/or heads, per-batch
+    key lengths (zero and past Nk included), ragged counts."""
+    r = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        dtype = "f32" if r.random() < 0.25 else "bf16"
+        d = int(r.choice([64, 128]))
+        B = int(r.integers(1, 4))
+        Hk = int(r.choice([1, 2]))
+        H = Hk * int(r.choice([1, 2, 3]))
+        Nq = int(r.integers(1, 700))
+        Nk = int(r.integers(1, 700))
+        causal = bool(r.integers(2))
+        bias = None
+        if r.random() < 0.5:
+            bias = (int(r.choice([1, B])), int(r.choice([1, H])))
+        kv = [int(x) for x in r.integers(0, Nk + 30, B)] if r.random() < 0.5 else None
+        cases.append((dtype, d, B, H, Hk, Nq, Nk, causal, bias, kv))
+    return cases
+
+
+@pytest.mark.parametrize("dtype,d,B,H,Hk,Nq,Nk,causal,bias,kv", _random_forward_cases(12, 7373))
+def test_random_small_problems(dtype, d, B, H, Hk, Nq, Nk, causal, bias, kv):
+    # seeded problems, every row compared with the oracle [Understanding
+    # FlashAttention Pt 1, sections 0.2, 2.4 and 3.5]
+    _banner(f"random dtype={dtype} d={d} B={B} H={H} Hk={Hk} Nq={Nq} Nk={Nk} causal={causal} "
+            f"bias={bias} kv={kv}")
+    g = torch.Generator().manual_seed(17 * Nq + Nk + d + B)
+    st = torch.bfloat16 if dtype == "bf16" else torch.float32
+    q = torch.randn(B, H, Nq, d, generator=g).to(st)
+    k = torch.randn(B, Hk, Nk, d, generator=g).to(st)
+    v = torch.randn(B, Hk, Nk, d, generator=g).to(st)
+    bb = None if bias is None else 0.5 * torch.randn(bias[0], bias[1], Nq, Nk, generator=g)
+    kl = None if kv is None else torch.tensor(kv, dtype=torch.int32)
+    scale = float(torch.tensor(d ** -0.5, dtype=torch.float32))
+    inp = {"q": q, "k": k, "v": v, "bias": bb, "kv_len": kl, "causal": causal, "scale": scale}
+    o, lse = run_gpu(inp)
+    rep = H // Hk
+    ref = dict(inp)
+    ref["k"] = k.repeat_interleave(rep, dim=1)
+    ref["v"] = v.repeat_interleave(rep, dim=1)
+    ro, rl = run_oracle(ref)
+    compare(o, lse, ro, rl, dtype, f"random Nq={Nq} Nk={Nk}")
