@@ -162,3 +162,42 @@ def test_window_full_size_every_tile(name):
                                      window=w.window)
 
     compare_rows(o_c, lse_c, full_size_rows(w), oracle_rows, w.dtype, f"window full {name}")
+
+
+def _random_window_cases(n, seed):
+    """Seeded windowed problems through the per-tile and split kernels: both
+    dtypes and head dimensions, grouped heads, one- and two-sided bands of
+    every width (0 to past the keys), causal or not, a bias and key lengths."""
+    r = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        dtype = "f32" if r.random() < 0.25 else "bf16"
+        d = int(r.choice([64, 128]))
+        B = int(r.integers(1, 3))
+        Hk = int(r.choice([1, 2]))
+        H = Hk * int(r.choice([1, 2]))
+        Nq = int(r.integers(1, 900))
+        Nk = int(r.integers(1, 900))
+        causal = bool(r.integers(2))
+        window = (int(r.integers(-1, 700)), int(r.integers(-1, 300)))
+        bias = bool(r.random() < 0.3)
+        kv = [int(x) for x in r.integers(0, Nk + 30, B)] if r.random() < 0.4 else None
+        split = dtype == "bf16" and r.random() < 0.3
+        cases.append((dtype, d, B, H, Hk, Nq, Nk, causal, window, bias, kv, split))
+    return cases
+
+
+@pytest.mark.parametrize("dtype,d,B,H,Hk,Nq,Nk,causal,window,bias,kv,split",
+                         _random_window_cases(10, 8484))
+def test_window_random_problems(dtype, d, B, H, Hk, Nq, Nk, causal, window, bias, kv, split):
+    # seeded windowed problems, every row compared with the oracle (reading
+    # of the band: around the bottom-right diagonal, a negative bound open)
+    # [flash-attention, Part III, window_size; FlashAttention, Explained,
+    # section 14]
+    _banner(f"window random {dtype} d={d} B={B} H={H} Hk={Hk} Nq={Nq} Nk={Nk} causal={causal} "
+            f"window={window} bias={bias} kv={kv} split={split}")
+    inp = _inputs(B, H, Nq, Nk, d, dtype=dtype, seed=11 * Nq + Nk + d, Hk=Hk, bias=bias,
+                  kv_len=kv)
+    o, lse = _gpu_run(inp, causal, window, split=split, num_splits=3 if split else None)
+    ro, rl = _oracle(inp, causal, window)
+    compare(o, lse, ro, rl, dtype, f"window random {window}")
