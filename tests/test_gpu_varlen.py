@@ -300,3 +300,41 @@ def test_varlen_random_batches(lens_q, lens_k, H, Hk, d, causal):
                                      cu_q.numpy(), cu_k.numpy(), scale=d ** -0.5, causal=causal)
     compare(o.double().cpu().numpy(), lse.double().cpu().numpy().T, ro, rl.T, "bf16",
             f"varlen random {len(lens_q)} sequences")
+
+
+def _random_varlen_tile_cases(n, seed):
+    """Seeded packed batches for the per-tile launch (H not a multiple of 8,
+    or fp32): both dtypes and head dimensions, a window on some."""
+    r = np.random.default_rng(seed)
+    cases = []
+    for c in range(n):
+        ns = int(r.integers(1, 20))
+        lq = [int(min(1500, round(float(np.exp(np.log(200) + 1.0 * r.normal())))))
+              if r.random() < 0.8 else int(r.choice([0, 1, 63, 64, 65, 256, 257])) for _ in range(ns)]
+        lk = None
+        if c % 3 == 1:
+            lk = [int(min(1500, max(0, x + int(r.integers(-60, 200))))) for x in lq]
+        Hk = int(r.choice([1, 2, 3]))
+        H = Hk * int(r.choice([1, 2]))
+        d = int(r.choice([64, 128]))
+        dtype = "f32" if r.random() < 0.3 else "bf16"
+        window = (int(r.integers(0, 300)), int(r.integers(-1, 100))) if r.random() < 0.3 else None
+        cases.append((lq, lk, H, Hk, d, dtype, bool(c % 2), window))
+    return cases
+
+
+@pytest.mark.parametrize("lens_q,lens_k,H,Hk,d,dtype,causal,window", _random_varlen_tile_cases(8, 7171))
+def test_varlen_random_tile_batches(lens_q, lens_k, H, Hk, d, dtype, causal, window):
+    # seeded packed batches through the per-tile launch, compared in full
+    # [flash-attention, Part II, variable-length batches]
+    lens_k = lens_q if lens_k is None else lens_k
+    _banner(f"varlen random tile {len(lens_q)} sequences rows={sum(lens_q)} keys={sum(lens_k)} "
+            f"H={H} Hk={Hk} d={d} {dtype} causal={causal} window={window}")
+    q, k, v, cu_q, cu_k = _packed(lens_q, lens_k, H, Hk, d, dtype, seed=9 * sum(lens_q) + d + H)
+    o, lse = _run(q, k, v, cu_q, cu_k, max(max(lens_q), 1), causal, window=window)
+    ro, rl = oracle.attention_varlen(q.double().numpy(), k.double().numpy(), v.double().numpy(),
+                                     cu_q.numpy(), cu_k.numpy(), scale=d ** -0.5, causal=causal,
+                                     window=window)
+    T = q.shape[0]
+    compare(o.double().cpu().numpy()[:T], lse.double().cpu().numpy().T[:T], ro, rl.T, dtype,
+            f"varlen random tile {len(lens_q)} sequences")
